@@ -1,0 +1,171 @@
+/*
+ * seer.h -- C ABI of the MI355X (gfx950) SeerAttention hot path.
+ *
+ * Pages cited:
+ *   [E] "SeerAttention: Learning Intrinsic Sparse Attention in Your LLMs"
+ *       (paper-graph-ui explainer of arXiv 2410.13276)
+ *   [R] "SeerAttention: Self-distilled Attention Gating for Efficient
+ *       Long-context Prefilling" (OpenReview discussion, paperhub)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensors are row-major. Q is [B, Hq, S, D]; K and V are [B, Hkv, S, D]
+ *    (grouped-query attention: query head h reads KV head h / (Hq / Hkv)).
+ *    Q, K, V are bfloat16 (raw 16-bit patterns, `const void*`).
+ *  - Block maps (gate scores, block mask, ground truth) are [B, Hq, nb, nb]
+ *    with nb = ceil(S / 64); entry (i, j) is query block i against key block j.
+ *    The last block may be ragged (S not a multiple of 64).
+ *  - Attention is causal (prefill): key u is visible to query t iff u <= t.
+ *    The softmax scale is 1/sqrt(D).
+ *  - Every pointer argument except `topk_per_head` is DEVICE memory owned by
+ *    the caller. The library allocates nothing, keeps no state between calls
+ *    and never synchronizes the host: work is enqueued on `hip_stream`
+ *    (a hipStream_t; NULL means the default stream) and outputs are valid
+ *    once that stream has reached the end of the call.
+ *  - Arguments are validated on the host before anything is enqueued. On any
+ *    error the call returns a non-zero seer_status, enqueues nothing and
+ *    writes nothing; seer_last_error() then describes the problem.
+ *  - Results are bitwise deterministic from run to run.
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef SEER_H_
+#define SEER_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum seer_status {
+  SEER_OK = 0,
+  SEER_ERR_INVALID_ARG = 1, /* null pointer where one is required, bad enum,
+                               non-finite threshold, k < 1 */
+  SEER_ERR_SHAPE = 2,       /* negative size, heads_q % heads_kv != 0,
+                               block != 64, sizes whose tensors overflow */
+  SEER_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, gate_dim not a multiple
+                               of 16 in [16, 256], too many blocks per row */
+  SEER_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the query */
+  SEER_ERR_HIP = 5          /* the HIP runtime reported an error */
+} seer_status;
+
+/* Problem sizes. block must be 64 (the gate's pooling window, which is also
+ * the attention tile: [E] section 3.4, "Block-sparse FlashAttention kernel").
+ * Zero sizes are valid and make a call a no-op. */
+typedef struct seer_shape {
+  int32_t batch;
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t seq_len;
+  int32_t head_dim;
+  int32_t block;
+} seer_shape;
+
+typedef enum seer_mask_mode {
+  SEER_MASK_THRESHOLD = 0, /* b_ij = score_ij > T           ([E] 3.4 Method 2) */
+  SEER_MASK_TOPK = 1       /* k largest scores of row i      ([E] 3.4 Method 1) */
+} seer_mask_mode;
+
+typedef enum seer_dtype { SEER_F32 = 0, SEER_BF16 = 1 } seer_dtype;
+
+/* ------------------------------------------------------------------------
+ * AttnGate ([E] section 3.4, "AttnGate: The Learned Sparsity Predictor" and
+ * its score equation; "Pooling Method Selection"; "Inference Procedure",
+ * Methods 1 and 2; [R] response 3.3 on mask generation).
+ *
+ *   Qp[b,h,i]  = mean of Q[b,h,t] over the tokens t of block i        ([B,Hq,nb,D])
+ *   Kp[b,g,i]  = [max | min | mean] of K[b,g,t] over block i          ([B,Hkv,nb,3D])
+ *   Q'[b,h,i]  = Qp[b,h,i] . w_q[h]                                    (D -> gate_dim)
+ *   K'[b,h,j]  = Kp[b,g(h),j] . w_k[h]   (w_k per query head), or
+ *               Kp[b,g(h),j] . w_k[g(h)] (wk_per_kv_head != 0)        (3D -> gate_dim)
+ *   score[b,h,i,j] = softmax over j <= i of Q'_i . K'_j / sqrt(D); 0 for j > i
+ *   mask[b,h,i,j]  = 1 if the block is selected, else 0 (also 0 for j > i)
+ *     threshold: score > threshold (strict)
+ *     top-k    : the k largest causal scores of row i, ties to the lower j;
+ *                a row with i+1 <= k keeps all its causal blocks
+ *   Everything is computed in fp32; the mask is decided on the fp32 scores.
+ *
+ * q            device bf16 [B,Hq,S,D]
+ * k            device bf16 [B,Hkv,S,D]
+ * w_q          device fp32 [Hq,D,gate_dim]
+ * w_k          device fp32 [Hq,3D,gate_dim] or [Hkv,3D,gate_dim]
+ * threshold    used in SEER_MASK_THRESHOLD mode; must be finite
+ * topk_k       uniform k for SEER_MASK_TOPK (>= 1) when topk_per_head is NULL
+ * topk_per_head HOST array of Hq values of k (>= 1), or NULL; read during the call
+ * scores       device fp32 [B,Hq,nb,nb] output, or NULL if not wanted
+ * block_mask   device uint8 [B,Hq,nb,nb] output (required)
+ * workspace    device scratch of at least seer_gate_workspace_size() bytes
+ * ---------------------------------------------------------------------- */
+size_t seer_gate_workspace_size(const seer_shape* shape, int32_t gate_dim, int32_t wk_per_kv_head,
+                                int32_t want_scores);
+seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_per_kv_head,
+                          const void* q, const void* k, const float* w_q, const float* w_k,
+                          seer_mask_mode mode, float threshold, int32_t topk_k,
+                          const int32_t* topk_per_head, float* scores, uint8_t* block_mask,
+                          void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Causal GQA block-sparse attention forward ([E] section 3.4, "Block-sparse
+ * FlashAttention kernel": a tile whose mask entry is 0 is skipped whole -- no
+ * Q.K^T, no softmax, no P.V and no K/V loads -- and a tile whose entry is 1 is
+ * computed as in FlashAttention-2; [R] response 3.3: blocks marked True are
+ * activated in the kernel).
+ *
+ *   O[b,h,t]  = sum_u softmax_u(Q[b,h,t] . K[b,g,u] / sqrt(D)) V[b,g,u]
+ *               over keys u <= t whose block is active in mask[b,h,t/64,u/64]
+ *   lse[b,h,t] = natural-log sum of exp of those logits
+ *   A query with no active key gets O = 0 and lse = -inf.
+ *
+ * block_mask   device uint8 [B,Hq,nb,nb]; any non-zero byte means "compute";
+ *              entries above the diagonal are ignored. NULL = dense causal
+ *              attention over every block (the speedup denominator).
+ * out          device [B,Hq,S,D] in out_dtype (fp32 or bf16)
+ * lse          device fp32 [B,Hq,S] output, or NULL
+ * workspace    may be NULL: seer_attn_workspace_size() is 0 (the active-block
+ *              list of each row is compacted on chip)
+ * ---------------------------------------------------------------------- */
+size_t seer_attn_workspace_size(const seer_shape* shape);
+seer_status seer_block_sparse_attn_fwd(const seer_shape* shape, const void* q, const void* k,
+                                       const void* v, const uint8_t* block_mask, void* out,
+                                       seer_dtype out_dtype, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Dense causal attention that also emits the 2D-maxpooled attention map, the
+ * gate's distillation target ([E] section 3.4, "Training Procedure": gt
+ * equation and the customized training kernel that stores the per-tile row
+ * maxima r_ij, rescales them with the final row statistics and takes a
+ * column max).
+ *
+ *   gt[b,h,i,j] = max over t in block i, u in block j, u <= t of
+ *                 softmax_u(Q[b,h,t] . K[b,g,u] / sqrt(D));  0 for j > i
+ *   (raw max-pooled probabilities, not renormalized)
+ *
+ * out, lse     as for seer_block_sparse_attn_fwd with block_mask = NULL
+ * gt           device fp32 [B,Hq,nb,nb] output (required)
+ * workspace    device scratch of at least seer_gt_workspace_size() bytes
+ *              (the stored per-row, per-key-block maxima)
+ * ---------------------------------------------------------------------- */
+size_t seer_gt_workspace_size(const seer_shape* shape);
+seer_status seer_attn_maxpool_gt(const seer_shape* shape, const void* q, const void* k,
+                                 const void* v, void* out, seer_dtype out_dtype, float* lse,
+                                 float* gt, void* workspace, size_t workspace_bytes,
+                                 void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics.
+ * seer_status_string: static name of a status code.
+ * seer_last_error: message of the last failing call on this thread ("" if
+ *   none); valid until the next call on this thread.
+ * seer_version: library version string.
+ * ---------------------------------------------------------------------- */
+const char* seer_status_string(seer_status status);
+const char* seer_last_error(void);
+const char* seer_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEER_H_ */

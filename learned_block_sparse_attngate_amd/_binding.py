@@ -1,0 +1,251 @@
+"""ctypes binding of libseer.so (the C ABI in include/seer.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libseer.so. PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is missing or the GPU is not a gfx950,
+the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Union
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libseer.so")
+
+SEER_OK = 0
+SEER_ERR_INVALID_ARG = 1
+SEER_ERR_SHAPE = 2
+SEER_ERR_UNSUPPORTED = 3
+SEER_ERR_WORKSPACE = 4
+SEER_ERR_HIP = 5
+
+SEER_MASK_THRESHOLD = 0
+SEER_MASK_TOPK = 1
+SEER_F32 = 0
+SEER_BF16 = 1
+
+BLOCK = 64
+
+# Every symbol include/seer.h declares (checked by the CPU tests).
+EXPORTED = (
+    "seer_gate_workspace_size", "seer_gate_fwd",
+    "seer_attn_workspace_size", "seer_block_sparse_attn_fwd",
+    "seer_gt_workspace_size", "seer_attn_maxpool_gt",
+    "seer_status_string", "seer_last_error", "seer_version",
+)
+
+
+class SeerShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+                ("seq_len", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32)]
+
+
+class SeerError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+_LIB = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libseer.so once and declare its signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m learned_block_sparse_attngate_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
+    shp = ctypes.POINTER(SeerShape)
+    lib.seer_gate_workspace_size.argtypes = [shp, i32, i32, i32]
+    lib.seer_gate_workspace_size.restype = sz
+    lib.seer_gate_fwd.argtypes = [shp, i32, i32, vp, vp, vp, vp, ctypes.c_int, f32, i32,
+                                  ctypes.POINTER(i32), vp, vp, vp, sz, vp]
+    lib.seer_gate_fwd.restype = ctypes.c_int
+    lib.seer_attn_workspace_size.argtypes = [shp]
+    lib.seer_attn_workspace_size.restype = sz
+    lib.seer_block_sparse_attn_fwd.argtypes = [shp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, sz, vp]
+    lib.seer_block_sparse_attn_fwd.restype = ctypes.c_int
+    lib.seer_gt_workspace_size.argtypes = [shp]
+    lib.seer_gt_workspace_size.restype = sz
+    lib.seer_attn_maxpool_gt.argtypes = [shp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, sz, vp]
+    lib.seer_attn_maxpool_gt.restype = ctypes.c_int
+    lib.seer_status_string.argtypes = [ctypes.c_int]
+    lib.seer_status_string.restype = ctypes.c_char_p
+    lib.seer_last_error.argtypes = []
+    lib.seer_last_error.restype = ctypes.c_char_p
+    lib.seer_version.argtypes = []
+    lib.seer_version.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _status_name(status: int) -> str:
+    names = {0: "SEER_OK", 1: "SEER_ERR_INVALID_ARG", 2: "SEER_ERR_SHAPE", 3: "SEER_ERR_UNSUPPORTED",
+             4: "SEER_ERR_WORKSPACE", 5: "SEER_ERR_HIP"}
+    return names.get(status, f"status {status}")
+
+
+def _check(status: int):
+    if status != SEER_OK:
+        msg = load_library().seer_last_error().decode(errors="replace")
+        raise SeerError(status, msg)
+
+
+def make_shape(batch, heads_q, heads_kv, seq_len, head_dim, block=BLOCK) -> SeerShape:
+    return SeerShape(batch, heads_q, heads_kv, seq_len, head_dim, block)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return workspace
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def nblocks(seq_len: int) -> int:
+    return -(-seq_len // BLOCK)
+
+
+# ---------------------------------------------------------------------------
+def seer_gate_fwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor, *,
+                  mode: str = "threshold", threshold: float = 5e-4,
+                  topk: Union[int, Sequence[int], None] = None, wk_per_kv_head: bool = False,
+                  want_scores: bool = True, scores: Optional[torch.Tensor] = None,
+                  block_mask: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """AttnGate scores and block mask. Returns (block_mask uint8, scores fp32 or None)."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16)
+    _need(w_q, "w_q", torch.float32)
+    _need(w_k, "w_k", torch.float32)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    Dg = w_q.shape[-1]
+    nb = nblocks(S)
+    shape = make_shape(B, Hq, Hkv, S, D)
+    dev = q.device
+    if block_mask is None:
+        block_mask = torch.empty((B, Hq, nb, nb), dtype=torch.uint8, device=dev)
+    if want_scores and scores is None:
+        scores = torch.empty((B, Hq, nb, nb), dtype=torch.float32, device=dev)
+    if not want_scores:
+        scores = None
+    m = SEER_MASK_TOPK if mode == "topk" else SEER_MASK_THRESHOLD
+    if mode not in ("topk", "threshold"):
+        raise ValueError(f"mode must be 'threshold' or 'topk', got {mode!r}")
+    per_head = None
+    k_uniform = 0
+    if m == SEER_MASK_TOPK:
+        if topk is None:
+            raise ValueError("topk mode needs topk")
+        if isinstance(topk, int):
+            k_uniform = topk
+        else:
+            per_head = (ctypes.c_int32 * len(topk))(*[int(x) for x in topk])
+            if len(topk) != Hq:
+                raise ValueError(f"per-head topk needs {Hq} values")
+    nbytes = lib.seer_gate_workspace_size(ctypes.byref(shape), Dg, int(wk_per_kv_head), int(scores is not None))
+    workspace = _workspace(nbytes, dev, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.seer_gate_fwd(ctypes.byref(shape), Dg, int(wk_per_kv_head), _ptr(q), _ptr(k), _ptr(w_q), _ptr(w_k),
+                             m, float(threshold), int(k_uniform), per_head, _ptr(scores), _ptr(block_mask),
+                             _ptr(workspace), ws_bytes, _stream(dev)))
+    return block_mask, scores
+
+
+def seer_block_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               block_mask: Optional[torch.Tensor] = None, *,
+                               out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                               lse: Optional[torch.Tensor] = None, want_lse: bool = False):
+    """Causal GQA block-sparse attention (block_mask=None: dense causal). Returns (out, lse or None)."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16)
+    _need(v, "v", torch.bfloat16)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    shape = make_shape(B, Hq, Hkv, S, D)
+    dev = q.device
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8)
+        if tuple(block_mask.shape) != (B, Hq, nblocks(S), nblocks(S)):
+            raise ValueError(f"block_mask must be {(B, Hq, nblocks(S), nblocks(S))}, got {tuple(block_mask.shape)}")
+    if out is None:
+        out = torch.empty((B, Hq, S, D), dtype=out_dtype, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    dt = SEER_BF16 if out.dtype == torch.bfloat16 else SEER_F32
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    _check(lib.seer_block_sparse_attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_mask),
+                                          _ptr(out), dt, _ptr(lse), None, 0, _stream(dev)))
+    return out, lse
+
+
+def seer_attn_maxpool_gt(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                         out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                         lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                         gt: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Dense causal attention plus the 2D-maxpooled map. Returns (out, lse or None, gt)."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16)
+    _need(v, "v", torch.bfloat16)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    nb = nblocks(S)
+    shape = make_shape(B, Hq, Hkv, S, D)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, Hq, S, D), dtype=out_dtype, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    if gt is None:
+        gt = torch.empty((B, Hq, nb, nb), dtype=torch.float32, device=dev)
+    dt = SEER_BF16 if out.dtype == torch.bfloat16 else SEER_F32
+    nbytes = lib.seer_gt_workspace_size(ctypes.byref(shape))
+    workspace = _workspace(nbytes, dev, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.seer_attn_maxpool_gt(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(out), dt, _ptr(lse),
+                                    _ptr(gt), _ptr(workspace), ws_bytes, _stream(dev)))
+    return out, lse, gt
+
+
+def gt_workspace_bytes(batch, heads_q, heads_kv, seq_len, head_dim) -> int:
+    shape = make_shape(batch, heads_q, heads_kv, seq_len, head_dim)
+    return load_library().seer_gt_workspace_size(ctypes.byref(shape))
+
+
+def gate_workspace_bytes(batch, heads_q, heads_kv, seq_len, head_dim, gate_dim, wk_per_kv_head=False,
+                         want_scores=True) -> int:
+    shape = make_shape(batch, heads_q, heads_kv, seq_len, head_dim)
+    return load_library().seer_gate_workspace_size(ctypes.byref(shape), gate_dim, int(wk_per_kv_head),
+                                                   int(want_scores))
+
+
+def version() -> str:
+    return load_library().seer_version().decode()

@@ -1,0 +1,306 @@
+// Host side of the C ABI declared in include/seer.h: argument validation,
+// workspace layout and kernel launch. Nothing here allocates device memory or
+// synchronizes the host.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "../../include/seer.h"
+#include "seer_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+seer_status fail(seer_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+seer_status fail(seer_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+seer_status ok() {
+  g_last_error.clear();
+  return SEER_OK;
+}
+
+constexpr int kBlock = 64;
+constexpr long long kMaxSeqAttn = 1LL << 22;    // 65536 key blocks (16-bit on-chip list)
+constexpr int kMaxNbGate = 16384;               // one score row in LDS (64 KiB)
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+long long nblocks(const seer_shape* s) { return (static_cast<long long>(s->seq_len) + kBlock - 1) / kBlock; }
+
+// Shape checks shared by every call. Sets *empty when there is nothing to do.
+seer_status check_shape(const seer_shape* s, bool* empty) {
+  if (s == nullptr) return fail(SEER_ERR_INVALID_ARG, "shape is NULL");
+  if (s->batch < 0 || s->heads_q < 0 || s->heads_kv < 0 || s->seq_len < 0 || s->head_dim < 0)
+    return fail(SEER_ERR_SHAPE, "negative size (batch %d, heads_q %d, heads_kv %d, seq_len %d, head_dim %d)",
+                s->batch, s->heads_q, s->heads_kv, s->seq_len, s->head_dim);
+  if (s->block != kBlock) return fail(SEER_ERR_SHAPE, "block must be 64 (got %d)", s->block);
+  if (s->heads_q > 0 && (s->heads_kv == 0 || s->heads_q % s->heads_kv != 0))
+    return fail(SEER_ERR_SHAPE, "heads_q (%d) must be a positive multiple of heads_kv (%d)", s->heads_q,
+                s->heads_kv);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(SEER_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", s->head_dim);
+  if (s->seq_len > kMaxSeqAttn)
+    return fail(SEER_ERR_UNSUPPORTED, "seq_len %d exceeds the supported maximum %lld", s->seq_len, kMaxSeqAttn);
+  const long long rows = static_cast<long long>(s->batch) * s->heads_q * nblocks(s);
+  if (rows > 0x7fffffffLL)
+    return fail(SEER_ERR_SHAPE, "batch * heads_q * blocks = %lld exceeds the launch limit", rows);
+  *empty = (s->batch == 0 || s->heads_q == 0 || s->seq_len == 0);
+  return SEER_OK;
+}
+
+seer_status check_device() {
+  static std::once_flag once[64];
+  static bool good[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SEER_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(SEER_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+  std::call_once(once[dev], [dev]() {
+    hipDeviceProp_t prop;
+    good[dev] = hipGetDeviceProperties(&prop, dev) == hipSuccess && strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  });
+  if (!good[dev]) return fail(SEER_ERR_UNSUPPORTED, "device %d is not a gfx950 (MI355X) GPU", dev);
+  return SEER_OK;
+}
+
+int attn_sched(const seer_shape* s) {
+  static int env = [] {
+    const char* v = getenv("SEER_ATTN_SCHED");
+    return v ? atoi(v) : -1;
+  }();
+  const int bh = s->batch * s->heads_q;
+  if (env == 0) return 0;
+  return (bh % 8 == 0) ? 1 : 0;
+}
+
+seer::AttnArgs attn_args(const seer_shape* s, const void* q, const void* k, const void* v) {
+  seer::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.B = s->batch;
+  a.Hq = s->heads_q;
+  a.Hkv = s->heads_kv;
+  a.S = s->seq_len;
+  a.D = s->head_dim;
+  a.nb = static_cast<int>(nblocks(s));
+  a.group = s->heads_q / s->heads_kv;
+  a.ntri = static_cast<long long>(a.nb) * (a.nb + 1) / 2;
+  a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(s->head_dim)));
+  a.sched = attn_sched(s);
+  return a;
+}
+
+seer_status check_qkv(const void* q, const void* k, const void* v) {
+  if (q == nullptr || k == nullptr || (v == nullptr))
+    return fail(SEER_ERR_INVALID_ARG, "q, k and v must be non-NULL device pointers");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+    return fail(SEER_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
+  return SEER_OK;
+}
+
+seer_status check_out(void* out, seer_dtype dt, float* lse) {
+  if (out == nullptr) return fail(SEER_ERR_INVALID_ARG, "out must be a non-NULL device pointer");
+  if (dt != SEER_F32 && dt != SEER_BF16) return fail(SEER_ERR_INVALID_ARG, "out_dtype %d is not SEER_F32/SEER_BF16", dt);
+  if (!aligned(out, dt == SEER_F32 ? 16 : 8)) return fail(SEER_ERR_INVALID_ARG, "out is misaligned for its dtype");
+  if (lse != nullptr && !aligned(lse, 4)) return fail(SEER_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  return SEER_OK;
+}
+
+struct GateLayout {
+  size_t qp, kp, qg, kg, scores, total;
+};
+
+GateLayout gate_layout(const seer_shape* s, int dg, int wk_per_kv, bool want_scores) {
+  const size_t B = s->batch, Hq = s->heads_q, Hkv = s->heads_kv, D = s->head_dim, nb = nblocks(s);
+  const size_t hwk = wk_per_kv ? Hkv : Hq;
+  GateLayout L{};
+  size_t off = 0;
+  L.qp = off; off += align_up(B * Hq * nb * D * 4);
+  L.kp = off; off += align_up(B * Hkv * nb * 3 * D * 4);
+  L.qg = off; off += align_up(B * Hq * nb * dg * 4);
+  L.kg = off; off += align_up(B * hwk * nb * dg * 4);
+  L.scores = off; off += want_scores ? 0 : align_up(B * Hq * nb * nb * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* seer_status_string(seer_status s) {
+  switch (s) {
+    case SEER_OK: return "SEER_OK";
+    case SEER_ERR_INVALID_ARG: return "SEER_ERR_INVALID_ARG";
+    case SEER_ERR_SHAPE: return "SEER_ERR_SHAPE";
+    case SEER_ERR_UNSUPPORTED: return "SEER_ERR_UNSUPPORTED";
+    case SEER_ERR_WORKSPACE: return "SEER_ERR_WORKSPACE";
+    case SEER_ERR_HIP: return "SEER_ERR_HIP";
+  }
+  return "SEER_ERR_UNKNOWN";
+}
+
+const char* seer_last_error(void) { return g_last_error.c_str(); }
+
+const char* seer_version(void) { return "seer-mi355x 0.1.0 (gfx950)"; }
+
+// ---------------------------------------------------------------------------
+size_t seer_gate_workspace_size(const seer_shape* shape, int32_t gate_dim, int32_t wk_per_kv_head,
+                                int32_t want_scores) {
+  bool empty = false;
+  if (check_shape(shape, &empty) != SEER_OK || gate_dim <= 0) return 0;
+  return gate_layout(shape, gate_dim, wk_per_kv_head != 0, want_scores != 0).total;
+}
+
+seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_per_kv_head, const void* q,
+                          const void* k, const float* w_q, const float* w_k, seer_mask_mode mode,
+                          float threshold, int32_t topk_k, const int32_t* topk_per_head, float* scores,
+                          uint8_t* block_mask, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  bool empty = false;
+  seer_status st = check_shape(shape, &empty);
+  if (st != SEER_OK) return st;
+  if (gate_dim < 16 || gate_dim > 256 || gate_dim % 16 != 0)
+    return fail(SEER_ERR_UNSUPPORTED, "gate_dim must be a multiple of 16 in [16, 256] (got %d)", gate_dim);
+  if (mode != SEER_MASK_THRESHOLD && mode != SEER_MASK_TOPK)
+    return fail(SEER_ERR_INVALID_ARG, "mask mode %d is not SEER_MASK_THRESHOLD/SEER_MASK_TOPK", mode);
+  if (mode == SEER_MASK_THRESHOLD && !isfinite(threshold))
+    return fail(SEER_ERR_INVALID_ARG, "threshold must be finite");
+  seer::TopkTable tk{};
+  if (mode == SEER_MASK_TOPK) {
+    if (shape->heads_q > seer::kMaxTopkHeads)
+      return fail(SEER_ERR_UNSUPPORTED, "top-k supports at most %d query heads", seer::kMaxTopkHeads);
+    for (int h = 0; h < shape->heads_q; ++h) {
+      const int kv = topk_per_head ? topk_per_head[h] : topk_k;
+      if (kv < 1) return fail(SEER_ERR_INVALID_ARG, "top-k value %d (head %d) must be >= 1", kv, h);
+      tk.k[h] = kv;
+    }
+  }
+  if (nblocks(shape) > kMaxNbGate)
+    return fail(SEER_ERR_UNSUPPORTED, "the gate supports at most %d blocks per sequence", kMaxNbGate);
+  if (empty) return ok();
+  st = check_qkv(q, k, k);
+  if (st != SEER_OK) return st;
+  if (w_q == nullptr || w_k == nullptr) return fail(SEER_ERR_INVALID_ARG, "w_q and w_k must be non-NULL");
+  if (block_mask == nullptr) return fail(SEER_ERR_INVALID_ARG, "block_mask must be non-NULL");
+  if (scores != nullptr && !aligned(scores, 4)) return fail(SEER_ERR_INVALID_ARG, "scores must be 4-byte aligned");
+  const GateLayout L = gate_layout(shape, gate_dim, wk_per_kv_head != 0, scores != nullptr);
+  if (workspace == nullptr || workspace_bytes < L.total || !aligned(workspace, kAlign))
+    return fail(SEER_ERR_WORKSPACE, "workspace must be %zu bytes, 256-byte aligned (got %zu at %p)", L.total,
+                workspace_bytes, workspace);
+  st = check_device();
+  if (st != SEER_OK) return st;
+
+  char* ws = static_cast<char*>(workspace);
+  seer::GateArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.wq = w_q;
+  a.wk = w_k;
+  a.qp = reinterpret_cast<float*>(ws + L.qp);
+  a.kp = reinterpret_cast<float*>(ws + L.kp);
+  a.qg = reinterpret_cast<float*>(ws + L.qg);
+  a.kg = reinterpret_cast<float*>(ws + L.kg);
+  a.scores = scores ? scores : reinterpret_cast<float*>(ws + L.scores);
+  a.mask = block_mask;
+  a.B = shape->batch;
+  a.Hq = shape->heads_q;
+  a.Hkv = shape->heads_kv;
+  a.S = shape->seq_len;
+  a.D = shape->head_dim;
+  a.nb = static_cast<int>(nblocks(shape));
+  a.Dg = gate_dim;
+  a.group = shape->heads_q / shape->heads_kv;
+  a.wk_per_kv = wk_per_kv_head != 0;
+  a.scale = static_cast<float>(1.0 / sqrt(static_cast<double>(shape->head_dim)));
+  a.mode = mode == SEER_MASK_TOPK ? 1 : 0;
+  a.threshold = threshold;
+  hipError_t e = seer::launch_gate(a, tk, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SEER_ERR_HIP, "gate launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+size_t seer_attn_workspace_size(const seer_shape* shape) {
+  (void)shape;
+  return 0;
+}
+
+seer_status seer_block_sparse_attn_fwd(const seer_shape* shape, const void* q, const void* k, const void* v,
+                                       const uint8_t* block_mask, void* out, seer_dtype out_dtype, float* lse,
+                                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  bool empty = false;
+  seer_status st = check_shape(shape, &empty);
+  if (st != SEER_OK) return st;
+  if (out_dtype != SEER_F32 && out_dtype != SEER_BF16)
+    return fail(SEER_ERR_INVALID_ARG, "out_dtype %d is not SEER_F32/SEER_BF16", out_dtype);
+  if (empty) return ok();
+  if ((st = check_qkv(q, k, v)) != SEER_OK) return st;
+  if ((st = check_out(out, out_dtype, lse)) != SEER_OK) return st;
+  if ((st = check_device()) != SEER_OK) return st;
+  seer::AttnArgs a = attn_args(shape, q, k, v);
+  a.mask = block_mask;
+  a.out = out;
+  a.lse = lse;
+  a.out_bf16 = out_dtype == SEER_BF16;
+  hipError_t e = seer::launch_attn(a, block_mask ? 0 : 1, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SEER_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+size_t seer_gt_workspace_size(const seer_shape* shape) {
+  bool empty = false;
+  if (check_shape(shape, &empty) != SEER_OK) return 0;
+  const size_t nb = nblocks(shape);
+  return align_up(static_cast<size_t>(shape->batch) * shape->heads_q * (nb * (nb + 1) / 2) * kBlock * sizeof(float));
+}
+
+seer_status seer_attn_maxpool_gt(const seer_shape* shape, const void* q, const void* k, const void* v, void* out,
+                                 seer_dtype out_dtype, float* lse, float* gt, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream) {
+  bool empty = false;
+  seer_status st = check_shape(shape, &empty);
+  if (st != SEER_OK) return st;
+  if (out_dtype != SEER_F32 && out_dtype != SEER_BF16)
+    return fail(SEER_ERR_INVALID_ARG, "out_dtype %d is not SEER_F32/SEER_BF16", out_dtype);
+  if (empty) return ok();
+  if ((st = check_qkv(q, k, v)) != SEER_OK) return st;
+  if ((st = check_out(out, out_dtype, lse)) != SEER_OK) return st;
+  if (gt == nullptr || !aligned(gt, 4)) return fail(SEER_ERR_INVALID_ARG, "gt must be a non-NULL, 4-byte aligned device pointer");
+  const size_t need = seer_gt_workspace_size(shape);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
+    return fail(SEER_ERR_WORKSPACE, "workspace must be %zu bytes, 16-byte aligned (got %zu at %p)", need,
+                workspace_bytes, workspace);
+  if ((st = check_device()) != SEER_OK) return st;
+  seer::AttnArgs a = attn_args(shape, q, k, v);
+  a.out = out;
+  a.lse = lse;
+  a.out_bf16 = out_dtype == SEER_BF16;
+  a.rmax = static_cast<float*>(workspace);
+  a.gt = gt;
+  hipError_t e = seer::launch_attn(a, 2, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SEER_ERR_HIP, "ground-truth attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

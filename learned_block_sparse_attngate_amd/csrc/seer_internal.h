@@ -1,0 +1,55 @@
+// Kernel argument blocks and launchers shared between the host API and the
+// kernel translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace seer {
+
+struct AttnArgs {
+  const uint16_t* q;   // bf16 [B,Hq,S,D]
+  const uint16_t* k;   // bf16 [B,Hkv,S,D]
+  const uint16_t* v;   // bf16 [B,Hkv,S,D]
+  const uint8_t* mask; // u8 [B,Hq,nb,nb] (sparse mode only)
+  void* out;           // [B,Hq,S,D] fp32 or bf16
+  float* lse;          // fp32 [B,Hq,S] or null
+  float* rmax;         // ground-truth scratch [B*Hq][nb(nb+1)/2][64] fp32 (log2 units)
+  float* gt;           // fp32 [B,Hq,nb,nb]
+  int B, Hq, Hkv, S, D, nb, group;
+  long long ntri;      // nb(nb+1)/2
+  float scale_log2;    // log2(e) / sqrt(D)
+  int out_bf16;
+  int sched;           // 0: heads interleaved across XCDs, 1: a KV group's heads on one XCD
+};
+
+// mode: 0 block-sparse (mask), 1 dense causal, 2 dense causal + ground-truth maxima
+hipError_t launch_attn(const AttnArgs& a, int mode, hipStream_t st);
+
+struct GateArgs {
+  const uint16_t* q;   // bf16 [B,Hq,S,D]
+  const uint16_t* k;   // bf16 [B,Hkv,S,D]
+  const float* wq;     // [Hq,D,Dg]
+  const float* wk;     // [Hwk,3D,Dg]
+  float* qp;           // [B,Hq,nb,D]
+  float* kp;           // [B,Hkv,nb,3D]
+  float* qg;           // [B,Hq,nb,Dg]
+  float* kg;           // [B,Hwk,nb,Dg]
+  float* scores;       // [B,Hq,nb,nb] (caller's output or workspace)
+  uint8_t* mask;       // [B,Hq,nb,nb]
+  int B, Hq, Hkv, S, D, nb, Dg, group;
+  int wk_per_kv;       // 1: Hwk = Hkv, 0: Hwk = Hq
+  float scale;         // 1/sqrt(D)
+  int mode;            // 0 threshold, 1 top-k
+  float threshold;
+};
+
+constexpr int kMaxTopkHeads = 256;
+struct TopkTable {
+  int k[kMaxTopkHeads];
+};
+
+hipError_t launch_gate(const GateArgs& a, const TopkTable& tk, hipStream_t st);
+
+}  // namespace seer

@@ -1,0 +1,134 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/seer.h declares, sizes its workspaces as documented, and rejects bad
+arguments on the host before any HIP call (fake device pointers are passed;
+they are never dereferenced because validation fails first)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import learned_block_sparse_attngate_amd as seer
+from learned_block_sparse_attngate_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "seer.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libseer.so not built")
+
+FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x10002)
+
+
+def _lib():
+    return seer.load_library()
+
+
+def _shape(b=1, hq=4, hkv=2, s=256, d=128, blk=64):
+    return seer.make_shape(b, hq, hkv, s, d, blk)
+
+
+def _attn(shape, q=FAKE, k=FAKE, v=FAKE, mask=None, out=FAKE, dt=B.SEER_F32, lse=None):
+    return _lib().seer_block_sparse_attn_fwd(ctypes.byref(shape) if shape is not None else None, q, k, v, mask,
+                                             out, dt, lse, None, 0, None)
+
+
+def _gate(shape, dg=128, per_kv=0, mode=B.SEER_MASK_THRESHOLD, T=5e-4, k=4, per_head=None, scores=None,
+          mask=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return _lib().seer_gate_fwd(ctypes.byref(shape), dg, per_kv, FAKE, FAKE, FAKE, FAKE, mode, T, k, per_head,
+                                scores, mask, ws, ws_bytes, None)
+
+
+def test_exports_every_declared_symbol():
+    src = open(HEADER).read()
+    declared = set(re.findall(r"\b(seer_[a-z_]+)\s*\(", src))
+    assert declared == set(seer.EXPORTED)
+    lib = _lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    for name in declared:
+        assert re.search(rf"\bT {name}$", nm, re.M), f"{name} not exported as a text symbol"
+
+
+def test_status_strings_and_version():
+    lib = _lib()
+    for code, name in [(0, b"SEER_OK"), (1, b"SEER_ERR_INVALID_ARG"), (2, b"SEER_ERR_SHAPE"),
+                       (3, b"SEER_ERR_UNSUPPORTED"), (4, b"SEER_ERR_WORKSPACE"), (5, b"SEER_ERR_HIP")]:
+        assert lib.seer_status_string(code) == name
+    assert b"gfx950" in lib.seer_version()
+
+
+def test_shape_validation():
+    assert _attn(None) == B.SEER_ERR_INVALID_ARG
+    assert _attn(_shape(s=-1)) == B.SEER_ERR_SHAPE
+    assert b"negative" in _lib().seer_last_error()
+    assert _attn(_shape(blk=32)) == B.SEER_ERR_SHAPE
+    assert _attn(_shape(hq=6, hkv=4)) == B.SEER_ERR_SHAPE
+    assert _attn(_shape(hq=4, hkv=0)) == B.SEER_ERR_SHAPE
+    assert _attn(_shape(d=96)) == B.SEER_ERR_UNSUPPORTED
+    assert _attn(_shape(s=(1 << 22) + 1)) == B.SEER_ERR_UNSUPPORTED
+    assert _attn(_shape(b=4096, hq=4096, hkv=1, s=1 << 20)) == B.SEER_ERR_SHAPE
+
+
+def test_empty_problem_is_a_noop():
+    # nothing to do: OK even with NULL tensors, and no HIP call is made
+    assert _attn(_shape(s=0), q=None, k=None, v=None, out=None) == B.SEER_OK
+    assert _attn(_shape(b=0), q=None, k=None, v=None, out=None) == B.SEER_OK
+    assert _lib().seer_last_error() == b""
+
+
+def test_pointer_validation():
+    assert _attn(_shape(), q=None) == B.SEER_ERR_INVALID_ARG
+    assert _attn(_shape(), v=None) == B.SEER_ERR_INVALID_ARG
+    assert _attn(_shape(), k=FAKE_ODD) == B.SEER_ERR_INVALID_ARG
+    assert _attn(_shape(), out=None) == B.SEER_ERR_INVALID_ARG
+    assert _attn(_shape(), dt=7) == B.SEER_ERR_INVALID_ARG
+    assert _attn(_shape(), out=ctypes.c_void_p(0x10008), dt=B.SEER_F32) == B.SEER_ERR_INVALID_ARG
+
+
+def test_gate_validation():
+    s = _shape()
+    assert _gate(s, dg=100) == B.SEER_ERR_UNSUPPORTED
+    assert _gate(s, dg=512) == B.SEER_ERR_UNSUPPORTED
+    assert _gate(s, mode=5) == B.SEER_ERR_INVALID_ARG
+    assert _gate(s, T=math.nan) == B.SEER_ERR_INVALID_ARG
+    assert _gate(s, T=math.inf) == B.SEER_ERR_INVALID_ARG
+    assert _gate(s, mode=B.SEER_MASK_TOPK, k=0) == B.SEER_ERR_INVALID_ARG
+    ph = (ctypes.c_int32 * 4)(3, 3, 0, 3)
+    assert _gate(s, mode=B.SEER_MASK_TOPK, per_head=ph) == B.SEER_ERR_INVALID_ARG
+    assert b"head 2" in _lib().seer_last_error()
+    assert _gate(s, mask=None) == B.SEER_ERR_INVALID_ARG
+    assert _gate(s, ws=None) == B.SEER_ERR_WORKSPACE
+    need = _lib().seer_gate_workspace_size(ctypes.byref(s), 128, 0, 0)
+    assert _gate(s, ws_bytes=need - 1) == B.SEER_ERR_WORKSPACE
+    big = _shape(s=64 * 16385)
+    assert _gate(big) == B.SEER_ERR_UNSUPPORTED
+
+
+def test_gt_validation():
+    s = _shape()
+    lib = _lib()
+    need = lib.seer_gt_workspace_size(ctypes.byref(s))
+    assert lib.seer_attn_maxpool_gt(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, B.SEER_F32, None, None, FAKE, need,
+                                    None) == B.SEER_ERR_INVALID_ARG
+    assert lib.seer_attn_maxpool_gt(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, B.SEER_F32, None, FAKE, FAKE,
+                                    need - 1, None) == B.SEER_ERR_WORKSPACE
+
+
+def test_workspace_sizes():
+    lib = _lib()
+    s = _shape(b=2, hq=4, hkv=2, s=200, d=64)
+    nb = 4
+    align = lambda x: (x + 255) // 256 * 256
+    assert lib.seer_attn_workspace_size(ctypes.byref(s)) == 0
+    assert lib.seer_gt_workspace_size(ctypes.byref(s)) == align(2 * 4 * (nb * (nb + 1) // 2) * 64 * 4)
+    want = (align(2 * 4 * nb * 64 * 4) + align(2 * 2 * nb * 192 * 4) + align(2 * 4 * nb * 32 * 4)
+            + align(2 * 4 * nb * 32 * 4))
+    assert lib.seer_gate_workspace_size(ctypes.byref(s), 32, 0, 1) == want
+    assert lib.seer_gate_workspace_size(ctypes.byref(s), 32, 0, 0) == want + align(2 * 4 * nb * nb * 4)
+    want_kv = (align(2 * 4 * nb * 64 * 4) + align(2 * 2 * nb * 192 * 4) + align(2 * 4 * nb * 32 * 4)
+               + align(2 * 2 * nb * 32 * 4))
+    assert lib.seer_gate_workspace_size(ctypes.byref(s), 32, 1, 1) == want_kv

@@ -1,0 +1,115 @@
+"""GPU parity of the block-sparse / dense attention (C ABI via the binding)
+against the fp64 oracle, element by element, on seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import Shape
+from gpu_util import (check_close, check_lse, dev_bf16, dev_u8, host, say, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def _seer():
+    import learned_block_sparse_attngate_amd as seer
+    seer.load_library()
+    return seer
+
+
+def _run_full(shape, seed, mask, out_dtype, what):
+    seer = _seer()
+    say(f"[{what}] shape={shape} seed={seed} mask={'dense' if mask is None else 'sparse'} out={out_dtype}")
+    q, k, v = synth.gen_qkv(shape, seed)
+    out, lse = seer.seer_block_sparse_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v),
+                                               None if mask is None else dev_u8(mask),
+                                               out_dtype=out_dtype, want_lse=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(q, k, v, mask)
+    check_close(host(out), o_ref, f"{what} O")
+    check_lse(host(lse), l_ref, f"{what} LSE")
+    return out, lse
+
+
+CASES = [
+    # name, shape, seed, mask kind, out dtype
+    ("tiny_s512_c1", synth.WORKLOADS["tiny_s512"]["shape"], synth.WORKLOADS["tiny_s512"]["seed"], "workload", torch.float32),
+    ("ragged_s200_d64", Shape(1, 4, 2, 200, 64), 31, "tiny_noise", torch.float32),
+    ("ragged_s1000_d128", Shape(2, 4, 1, 1000, 128), 32, "p30_empty_noise", torch.bfloat16),
+    ("s1_single_token", Shape(1, 2, 2, 1, 128), 33, "tiny", torch.float32),
+    ("s65_two_blocks", Shape(1, 8, 8, 65, 64), 34, "tiny", torch.float32),
+    ("s4096_d128_p20", Shape(1, 4, 1, 4096, 128), 35, "p20", torch.float32),
+]
+
+
+def _mask_for(kind, shape, seed):
+    if kind == "workload":
+        return synth.workload_mask("tiny_s512").mask
+    if kind == "tiny":
+        return synth.gen_tiny_mask(shape, seed + 1).mask
+    if kind == "tiny_noise":
+        return synth.gen_random_upper_noise(synth.gen_tiny_mask(shape, seed + 1, p_keep=0.5).mask, seed + 2)
+    if kind == "p30_empty_noise":
+        rng = np.random.Generator(np.random.PCG64(seed))
+        nb = shape.nb
+        m = (rng.random((shape.batch, shape.heads_q, nb, nb)) < 0.3).astype(np.uint8)
+        m = np.tril(m)
+        m[0, 1, 5, :] = 0              # an empty row: O = 0, LSE = -inf
+        m[1, 3, 0, :] = 0
+        return synth.gen_random_upper_noise(m, seed + 3)
+    if kind == "p20":
+        return synth.gen_block_mask(shape, seed + 1, 0.8).mask
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("name,shape,seed,kind,dt", CASES, ids=[c[0] for c in CASES])
+def test_sparse_matches_oracle(name, shape, seed, kind, dt):
+    _run_full(shape, seed, _mask_for(kind, shape, seed), dt, name)
+
+
+@pytest.mark.parametrize("shape", [Shape(1, 4, 2, 777, 128), Shape(1, 2, 1, 300, 64)], ids=["d128_s777", "d64_s300"])
+def test_dense_matches_oracle(shape):
+    _run_full(shape, 40, None, torch.float32, "dense")
+
+
+def test_all_ones_mask_equals_dense_bitwise():
+    seer = _seer()
+    shape = Shape(1, 4, 2, 1000, 128)
+    q, k, v = (dev_bf16(x) for x in synth.gen_qkv(shape, 41))
+    ones = torch.ones((1, 4, shape.nb, shape.nb), dtype=torch.uint8, device="cuda")
+    a, la = seer.seer_block_sparse_attn_fwd(q, k, v, ones, out_dtype=torch.float32, want_lse=True)
+    b, lb = seer.seer_block_sparse_attn_fwd(q, k, v, None, out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_deterministic_reruns():
+    seer = _seer()
+    shape = Shape(1, 8, 2, 2048, 128)
+    q, k, v = (dev_bf16(x) for x in synth.gen_qkv(shape, 42))
+    m = dev_u8(synth.gen_block_mask(shape, 43, 0.7).mask)
+    a, _ = seer.seer_block_sparse_attn_fwd(q, k, v, m)
+    b, _ = seer.seer_block_sparse_attn_fwd(q, k, v, m)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_llama8b_s8k_50_sampled():
+    """The 8k, 50%-sparse Llama-3.1-8B-shaped layer, full GPU run, oracle on sampled query blocks."""
+    seer = _seer()
+    w = synth.WORKLOADS["llama8b_s8k_50"]
+    shape = w["shape"]
+    say(f"[llama8b_s8k_50] shape={shape} seed={w['seed']}")
+    q, k, v = synth.gen_qkv(shape, w["seed"])
+    minfo = synth.workload_mask("llama8b_s8k_50")
+    out, lse = seer.seer_block_sparse_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_u8(minfo.mask),
+                                               out_dtype=torch.bfloat16, want_lse=True)
+    torch.cuda.synchronize()
+    out_h, lse_h = host(out), host(lse)
+    rows = sample_rows(1, shape.heads_q, shape.nb, 3, 7)
+    o_ref, l_ref = oracle.attention_rows(q, k, v, minfo.mask, rows)
+    got = np.concatenate([out_h[b, h, 64 * i:64 * i + 64] for (b, h, i) in rows])
+    got_l = np.concatenate([lse_h[b, h, 64 * i:64 * i + 64] for (b, h, i) in rows])
+    check_close(got, np.concatenate(o_ref), "8k O (sampled)")
+    check_lse(got_l, np.concatenate(l_ref), "8k LSE (sampled)")

@@ -1,0 +1,161 @@
+"""GPU parity of the ground-truth kernel and of the AttnGate (scores, masks)
+against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import Shape
+from gpu_util import MASK_BAND, check_close, check_lse, dev_bf16, dev_f32, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _seer():
+    import learned_block_sparse_attngate_amd as seer
+    seer.load_library()
+    return seer
+
+
+# ---------------------------------------------------------------------------
+# ground truth
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape,dt", [(Shape(1, 2, 1, 200, 64), torch.float32),
+                                      (Shape(1, 4, 2, 1000, 128), torch.bfloat16),
+                                      (Shape(2, 2, 2, 64, 128), torch.float32)],
+                         ids=["s200_d64", "s1000_d128", "s64_b2"])
+def test_gt_matches_oracle(shape, dt):
+    seer = _seer()
+    say(f"[gt] shape={shape}")
+    q, k, v = synth.gen_qkv(shape, 50)
+    out, lse, gt = seer.seer_attn_maxpool_gt(dev_bf16(q), dev_bf16(k), dev_bf16(v), out_dtype=dt, want_lse=True)
+    torch.cuda.synchronize()
+    gt_ref = oracle.maxpool_gt(q, k)
+    o_ref, l_ref = oracle.attention(q, k, v, None)
+    g = host(gt)
+    check_close(g, gt_ref, "gt", max_abs=1e-4, mean_abs=1e-6)
+    rel = np.abs(g - gt_ref)[gt_ref > 1e-6] / gt_ref[gt_ref > 1e-6]
+    say(f"  gt max relative error on entries > 1e-6: {rel.max():.3e}")
+    assert rel.max() < 2e-2
+    assert np.all(g[..., np.triu_indices(shape.nb, 1)[0], np.triu_indices(shape.nb, 1)[1]] == 0.0)
+    check_close(host(out), o_ref, "gt-kernel O")
+    check_lse(host(lse), l_ref, "gt-kernel LSE")
+
+
+def test_gt_output_equals_dense_bitwise():
+    seer = _seer()
+    shape = Shape(1, 4, 2, 700, 128)
+    q, k, v = (dev_bf16(x) for x in synth.gen_qkv(shape, 51))
+    a, la, _ = seer.seer_attn_maxpool_gt(q, k, v, out_dtype=torch.float32, want_lse=True)
+    b, lb = seer.seer_block_sparse_attn_fwd(q, k, v, None, out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+# ---------------------------------------------------------------------------
+# gate
+# ---------------------------------------------------------------------------
+def _gate_inputs(shape, seed, dg, per_kv=False):
+    q, k, v, _ = synth.gen_planted_qk(shape, seed)
+    hw = shape.heads_kv if per_kv else shape.heads_q
+    wq, wk = synth.gen_gate_weights(shape.heads_q, shape.head_dim, dg, seed + 1, heads_w_k=hw)
+    return q, k, wq, wk
+
+
+def _check_threshold_mask(got_mask, scores_ref, T, what):
+    want = oracle.threshold_mask(scores_ref, T)
+    band = np.abs(scores_ref - T) <= MASK_BAND
+    diff = (got_mask != want) & ~band
+    say(f"  {what}: {int(want.sum())} active blocks, {int(band.sum())} in the band, {int(diff.sum())} mismatches")
+    assert not diff.any(), f"{what}: mask differs from the oracle outside the {MASK_BAND} band"
+
+
+GATE_CASES = [
+    ("s2500_d128_dg128", Shape(1, 4, 2, 64 * 40 - 60, 128), 128, False),
+    ("s4096_d64_dg64_kvw", Shape(2, 4, 1, 4096, 64), 64, True),
+    ("s640_d128_dg48", Shape(1, 2, 2, 640, 128), 48, False),
+]
+
+
+@pytest.mark.parametrize("name,shape,dg,per_kv", GATE_CASES, ids=[c[0] for c in GATE_CASES])
+def test_gate_threshold_matches_oracle(name, shape, dg, per_kv):
+    seer = _seer()
+    say(f"[gate threshold {name}] shape={shape} dg={dg} per_kv={per_kv}")
+    q, k, wq, wk = _gate_inputs(shape, 60, dg, per_kv)
+    sc_ref = oracle.gate_scores(q, k, wq, wk, wk_per_kv_head=per_kv)
+    nb = shape.nb
+    for T in (5e-4, 0.6 / nb, 1.2 / nb, 0.05):
+        mask, scores = seer.seer_gate_fwd(dev_bf16(q), dev_bf16(k), dev_f32(wq), dev_f32(wk), mode="threshold",
+                                          threshold=T, wk_per_kv_head=per_kv)
+        torch.cuda.synchronize()
+        s = host(scores)
+        err = np.abs(s - sc_ref)
+        say(f"  T={T:.3e} scores max-abs {err.max():.3e}, max rel {(err / np.maximum(sc_ref, 1e-30)).max():.3e}")
+        assert err.max() < 1e-5
+        _check_threshold_mask(mask.cpu().numpy(), sc_ref, T, f"T={T:.3e}")
+
+
+@pytest.mark.parametrize("topk", [1, 5, [2, 7, 3, 40]], ids=["k1", "k5", "per_head"])
+def test_gate_topk_matches_oracle(topk):
+    seer = _seer()
+    shape = Shape(1, 4, 2, 64 * 37, 128)
+    q, k, wq, wk = _gate_inputs(shape, 61, 128)
+    sc_ref = oracle.gate_scores(q, k, wq, wk)
+    mask, scores = seer.seer_gate_fwd(dev_bf16(q), dev_bf16(k), dev_f32(wq), dev_f32(wk), mode="topk", topk=topk)
+    torch.cuda.synchronize()
+    got = mask.cpu().numpy()
+    ks = np.broadcast_to(np.asarray(topk), (4,))
+    nb = shape.nb
+    want = oracle.topk_mask(sc_ref, topk)
+    bad = 0
+    for h in range(4):
+        for i in range(nb):
+            kk = min(int(ks[h]), i + 1)
+            assert int(got[0, h, i].sum()) == kk
+            assert not got[0, h, i, i + 1:].any()
+            row = sc_ref[0, h, i, :i + 1]
+            kth = np.sort(row)[::-1][kk - 1]
+            outside = np.abs(row - kth) > MASK_BAND
+            bad += int(((got[0, h, i, :i + 1] != want[0, h, i, :i + 1]) & outside).sum())
+    say(f"  top-k {topk}: {bad} mismatches outside the band")
+    assert bad == 0
+
+
+def test_gate_flat_scores_ties_and_strictness():
+    """W_q = 0 gives score 1/(i+1) exactly; T = 0.25 drops row 3 (strict >), top-k keeps the lowest j."""
+    seer = _seer()
+    shape = Shape(1, 2, 1, 64 * 12, 128)
+    q, k, _ = synth.gen_qkv(shape, 62, want_v=False)
+    wq = np.zeros((2, 128, 128), np.float32)
+    wk = synth.gen_gate_weights(2, 128, 128, 63)[1]
+    mask, scores = seer.seer_gate_fwd(dev_bf16(q), dev_bf16(k), dev_f32(wq), dev_f32(wk), threshold=0.25)
+    torch.cuda.synchronize()
+    s = host(scores)
+    assert np.all(s[0, :, 3, :4] == 0.25)
+    m = mask.cpu().numpy()
+    assert m[0, :, :3].sum() == 2 * 6 and m[0, :, 3:].sum() == 0
+    mask2, _ = seer.seer_gate_fwd(dev_bf16(q), dev_bf16(k), dev_f32(wq), dev_f32(wk), mode="topk", topk=3)
+    torch.cuda.synchronize()
+    m2 = mask2.cpu().numpy()
+    for i in range(12):
+        want = np.zeros(12, np.uint8)
+        want[:min(3, i + 1)] = 1
+        assert np.array_equal(m2[0, 0, i], want)
+
+
+def test_gate_to_sparse_attention_end_to_end():
+    """Gate mask -> block-sparse attention, checked against the oracle's own gate + attention."""
+    seer = _seer()
+    shape = Shape(1, 4, 2, 64 * 24, 128)
+    q, k, wq, wk = _gate_inputs(shape, 64, 128)
+    _, _, v = synth.gen_qkv(shape, 65)
+    T = 1.0 / shape.nb
+    mask, _ = seer.seer_gate_fwd(dev_bf16(q), dev_bf16(k), dev_f32(wq), dev_f32(wk), threshold=T)
+    out, _ = seer.seer_block_sparse_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), mask, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    sc_ref = oracle.gate_scores(q, k, wq, wk)
+    m_gpu = mask.cpu().numpy()
+    _check_threshold_mask(m_gpu, sc_ref, T, "e2e mask")
+    o_ref, _ = oracle.attention(q, k, v, m_gpu)
+    check_close(host(out), o_ref, "e2e O")
