@@ -28,9 +28,14 @@ BLOCK = 64
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     """fp32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat_in, flat_out = x.reshape(-1), out.reshape(-1)
+    step = 1 << 24                        # bounded temporaries for large tensors
+    for a in range(0, flat_in.size, step):
+        u = flat_in[a:a + step].view(np.uint32)
+        # finite inputs only: the carry never leaves 32 bits below the NaN range
+        flat_out[a:a + step] = ((u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) >> 16).astype(np.uint16)
+    return out
 
 
 def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
