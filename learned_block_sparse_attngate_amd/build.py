@@ -13,6 +13,7 @@ import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB_NAME = "libseer.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["attn_kernels.hip", "gate_kernels.hip", "seer_api.hip"]
@@ -23,6 +24,7 @@ HIPCC_FLAGS = [
     # keep fp32 arithmetic on unpacked VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    f"-I{INCLUDE}",
 ]
 
 

@@ -14,23 +14,28 @@
 //
 // Design for CDNA4:
 //  * one workgroup = one (batch, query head, query block) row = 64 queries,
-//    2 wavefronts x 32 queries; Q stays in registers for the whole row;
+//    2 wavefronts x 32 queries, two workgroups per SIMD so that one wave's
+//    MFMA work overlaps the other's softmax; Q stays in registers;
 //  * both contractions use v_mfma_f32_32x32x16_bf16 with the matrix roles
 //    chosen so the softmax is lane-local: S^T = K Q^T puts one query per lane
 //    (32 of its keys in the lane, the other 32 in lane l^32), and
 //    O^T = V^T P^T consumes the S^T registers directly as the B operand, so P
 //    never goes through LDS;
-//  * K and V tiles are staged through LDS with XOR swizzles that keep the
-//    16-byte MFMA operand reads conflict-free; V is transposed in registers on
-//    its way into LDS (keys permuted so each lane reads one 16-byte chunk);
-//  * the next tile is fetched from HBM into registers while the current one is
-//    computed;
+//  * K and V tiles move HBM -> LDS with global_load_lds_dwordx4 (no register
+//    staging); the XOR swizzle is applied on the source side so the LDS image
+//    is conflict-free for the 16-byte K operand reads and for the
+//    ds_read_b64_tr_b16 transposing reads that build the V^T operand;
+//  * each wave copies the tile's operands from LDS into registers, then the
+//    single LDS buffer is released and the next tile's copy is issued, so the
+//    HBM/L2 latency of tile n+1 overlaps the softmax and P.V of tile n;
 //  * the active key blocks of a row are compacted on chip from the mask row
 //    into an LDS list (ascending), so masked tiles cost neither time nor HBM
 //    traffic and no separate compaction launch or workspace is needed;
 //  * rows are launched heaviest first (descending query block) and, when the
 //    head count allows, the query heads of one KV head are kept on one XCD so
 //    that they share K/V tiles in that XCD's L2.
+#include <type_traits>
+
 #include "seer_device.h"
 #include "seer_internal.h"
 
@@ -42,20 +47,19 @@ constexpr int kThreads = 128;          // 2 wavefronts
 constexpr int kListCap = 2048;         // mask columns compacted per pass
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag by
+constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer resource, dword 3
 
 enum Mode { kSparse = 0, kDense = 1, kDenseGt = 2 };
 
-// Position <-> key permutation inside each 16-key group of a V^T row: swap
-// bits 2 and 3. The 32x32 S^T accumulator gives lane half h the keys
-// {8j + 4h + c}; storing V^T with this permutation lets that lane half fetch
-// its 8 keys of a 16-key MFMA step as one contiguous 16-byte chunk.
-__device__ __forceinline__ int key_of_pos(int p) {
-  return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
-}
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-// XOR swizzle of 16-byte chunks.
-__device__ __forceinline__ int swz_k(int row) { return row & 7; }
-__device__ __forceinline__ int swz_v(int row) { return (row ^ (row >> 3)) & 7; }
+// 16-byte-chunk XOR swizzles (chunk index within a row of the LDS tile).
+//  K: the 32x32x16 A-operand read has 16 consecutive keys at one logical chunk.
+//  V: a ds_read_b64_tr_b16 reads 8 consecutive keys x 4 consecutive chunks.
+template <int D> __device__ __forceinline__ int swz_k(int row) { return row & (D / 8 - 1); }
+template <int D> __device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * (row & 1); }
 
 __device__ __forceinline__ int bsum_exclusive(int x, int lane, int wave, int* wsum, int& total) {
   int inc = wave_inclusive_scan(x, lane);
@@ -67,15 +71,15 @@ __device__ __forceinline__ int bsum_exclusive(int x, int lane, int wave, int* ws
 }
 
 template <int D, int MODE>
-__global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_fwd_kernel(AttnArgs p) {
-  constexpr int CPR = D / 8;               // 16-byte chunks per K row
-  constexpr int RG = kThreads / CPR;       // rows covered per load pass
-  constexpr int RPT = kBlock / RG;         // K rows (V positions) per thread
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
+  constexpr int CPR = D / 8;               // 16-byte chunks per K/V row
   constexpr int KS = D / 16;               // MFMA k-steps for S^T
   constexpr int MT = D / 32;               // MFMA m-tiles for O^T
+  constexpr int RPI = 64 / CPR;            // tile rows per global_load_lds instruction
+  constexpr int NDMA = 32 / RPI;           // instructions per wave per operand (32 rows)
 
-  __shared__ uint4 Ks[kBlock * CPR];       // K tile  [64 keys][D]   (swizzled chunks)
-  __shared__ uint4 Vt[D * 8];              // V^T tile [D][64 keys]  (permuted, swizzled)
+  __shared__ uint4 Ks[kBlock * CPR];       // K tile [64 keys][D], swizzled chunks
+  __shared__ uint4 Vs[kBlock * CPR];       // V tile [64 keys][D], swizzled chunks
   __shared__ uint16_t list[MODE == kSparse ? kListCap : 1];
   __shared__ int wsum[2];
   __shared__ float lse_s[MODE == kDenseGt ? kBlock : 1];
@@ -86,13 +90,31 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_fwd_kernel(At
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
-  // ---- which row: heaviest (last) query blocks first --------------------
+  // ---- which row ---------------------------------------------------------
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+  // L2); all orders below launch the heaviest rows (last query blocks) first.
+  //  0: heads interleaved, all KV groups at once;
+  //  1: the query heads of one KV group on one XCD;
+  //  2: KV-group major: every XCD works on the same KV group at a time, so
+  //     the K/V working set is one group (it stays in the Infinity Cache);
+  //  3: KV-group major, then head major inside the group.
   const int BH = p.B * p.Hq;
   const int w = blockIdx.x;
-  const int qb = p.nb - 1 - w / BH;
-  int local = w % BH;
-  if (p.sched == 1) local = (local & 7) * (BH >> 3) + (local >> 3);  // heads of a KV group on one XCD
-  const int bh = local;
+  int qb, bh;
+  if (p.sched >= 2) {
+    const int R = p.group * p.nb;                 // rows per (batch, KV group)
+    const int gi = w / R, r = w - gi * R;         // gi = b * Hkv + g
+    int hig;
+    if (p.sched == 2) { qb = p.nb - 1 - r / p.group; hig = r % p.group; }
+    else { hig = r / p.nb; qb = p.nb - 1 - r % p.nb; }
+    const int bb = gi / p.Hkv, gg = gi - bb * p.Hkv;
+    bh = bb * p.Hq + gg * p.group + hig;
+  } else {
+    qb = p.nb - 1 - w / BH;
+    int local = w % BH;
+    if (p.sched == 1) local = (local & 7) * (BH >> 3) + (local >> 3);
+    bh = local;
+  }
   const int b = bh / p.Hq;
   const int h = bh - b * p.Hq;
   const int g = h / p.group;
@@ -119,78 +141,109 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_fwd_kernel(At
 #pragma unroll
   for (int i = 0; i < MT; ++i) oacc[i] = f32x16_t{};
 
-  // load-thread geometry
-  const int lc = tid % CPR;                       // 16-byte chunk (8 dims) this thread moves
-  const int lr = tid / CPR;                       // row group
-
-  uint4 kreg[RPT], vreg[RPT];
-  auto fetch = [&](int kb) {
+  // ---- HBM -> LDS copy of one K/V tile; this wave moves rows 32w .. 32w+31 --
+  // buffer_load_dwordx4 ... lds: instruction i, lane l writes LDS bytes
+  // [1024 i + 16 l) of this wave's half: tile row r = 32w + RPI*i + l/CPR,
+  // physical chunk l%CPR, holding logical chunk (l%CPR) ^ swz(r). With the
+  // swizzles above the V chunk does not depend on i and the K chunk takes four
+  // values, so a few per-lane byte offsets address every instruction. The
+  // buffer resource starts at the tile and ends at the head's last row, so rows
+  // past the sequence (ragged last tile) read as zeros: their scores are masked
+  // by causality and their P is 0.
+  uint32_t kofs[4], vofs;
+  {
+    const int r0 = 32 * wave + lane / CPR;                  // row for i = 0
+    const int pc = lane % CPR;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = r0 + RPI * v;                             // swz_k(r) for i = v (mod 4)
+      kofs[v] = static_cast<uint32_t>(r0 * 2 * D + 16 * (pc ^ swz_k<D>(r)));
+    }
+    vofs = static_cast<uint32_t>(r0 * 2 * D + 16 * (pc ^ swz_v<D>(r0)));
+  }
+  auto issue_tile = [&](int kb) {
     const int key0 = kb * kBlock;
+    const int nbytes = (p.S - key0) * 2 * D;
+    const auto kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kg + static_cast<size_t>(key0) * D), 0,
+                                                      nbytes, kBufferWord3);
+    const auto vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Vg + static_cast<size_t>(key0) * D), 0,
+                                                      nbytes, kBufferWord3);
+    char* kl = reinterpret_cast<char*>(Ks) + 32 * wave * D * 2;
+    char* vl = reinterpret_cast<char*>(Vs) + 32 * wave * D * 2;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int kr = lr + RG * i;                 // K row in the tile
-      const int kk = key0 + kr;
-      kreg[i] = kk < p.S ? *reinterpret_cast<const uint4*>(Kg + static_cast<size_t>(kk) * D + 8 * lc)
-                         : make_uint4(0, 0, 0, 0);
-      const int vk = key0 + key_of_pos(RPT * lr + i);
-      vreg[i] = vk < p.S ? *reinterpret_cast<const uint4*>(Vg + static_cast<size_t>(vk) * D + 8 * lc)
-                         : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto stage = [&]() {
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int kr = lr + RG * i;
-      Ks[kr * CPR + (lc ^ swz_k(kr))] = kreg[i];
-    }
-    // transpose 8 dims x RPT positions in registers, write RPT*2 bytes per dim
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int dim = 8 * lc + j;
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t pk[RPT / 2];
-#pragma unroll
-      for (int pp = 0; pp < RPT / 2; ++pp) {
-        const uint32_t lo = reinterpret_cast<const uint32_t*>(&vreg[2 * pp])[j >> 1];
-        const uint32_t hi = reinterpret_cast<const uint32_t*>(&vreg[2 * pp + 1])[j >> 1];
-        pk[pp] = __builtin_amdgcn_perm(hi, lo, sel);
-      }
-      if constexpr (RPT == 8) {
-        Vt[dim * 8 + (lr ^ swz_v(dim))] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      } else {  // RPT == 4: half a chunk
-        uint2* dst = reinterpret_cast<uint2*>(&Vt[dim * 8 + ((lr >> 1) ^ swz_v(dim))]) + (lr & 1);
-        *dst = make_uint2(pk[0], pk[1]);
-      }
+    for (int i = 0; i < NDMA; ++i) {
+      const uint32_t step = static_cast<uint32_t>(RPI * i * 2 * D);
+      const uint32_t ko = (D == 128 ? kofs[i & 3] : kofs[0]) + step;  // D = 64: swz_k(r) = r & 7 is i-invariant
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(kl + 1024 * i), 16, ko, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(vl + 1024 * i), 16, vofs + step, 0, 0, 0);
     }
   };
 
   const long long ntri_off = static_cast<long long>(qb) * (qb + 1) / 2;  // ground-truth scratch offset of this row
-  auto compute = [&](int kb) {
-    // S^T = K Q^T  (32 keys x 32 queries per m-tile, two m-tiles)
+
+  // One tile. On entry the tile is in LDS (this wave's copy completed and the
+  // workgroup synchronized); `next` >= 0 is issued as soon as both waves have
+  // pulled their operands out of LDS.
+  auto compute = [&](auto diag_tag, int kb, int next) {
+    constexpr bool kDiag = decltype(diag_tag)::value;   // the diagonal tile needs element causality
+    // operands of S^T = K Q^T: A = K rows (32 keys x 16 dims per m-tile / k-step)
+    uint4 ka[2][KS];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int key = 32 * mt + l32;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ka[mt][ks] = Ks[key * CPR + ((2 * ks + hl) ^ swz_k<D>(key))];
+    }
     f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int key = 32 * mt + l32;
-        const uint4 a = Ks[key * CPR + ((2 * ks + hl) ^ swz_k(key))];
-        sacc[mt] = mfma_32x32x16(a, qreg[ks], sacc[mt]);
+      for (int mt = 0; mt < 2; ++mt) sacc[mt] = mfma_32x32x16(ka[mt][ks], qreg[ks], sacc[mt]);
+    // keep the V^T reads below the S MFMAs so K and V operands are never live together
+    __builtin_amdgcn_sched_barrier(0);
+
+    // operands of O^T = V^T P^T: A = V^T (32 dims x 16 keys), two transposing
+    // reads of 4 keys each; key order matches the S^T accumulator layout
+    uint4 va[4][MT];
+    {
+      const int G = lane >> 4, j = (lane >> 2) & 3, a = lane & 3;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          uint32_t half[4];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int key = 16 * ks + 8 * u + 4 * (G >> 1) + j;
+            const int ch = 4 * mt + 2 * (G & 1) + (a >> 1);
+            const int off = key * (2 * D) + ((ch ^ swz_v<D>(key)) << 4) + ((a & 1) << 3);
+            const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t*)(reinterpret_cast<char*>(Vs) + off));
+            const uint2 r2 = __builtin_bit_cast(uint2, r);
+            half[2 * u] = r2.x;
+            half[2 * u + 1] = r2.y;
+          }
+          va[ks][mt] = make_uint4(half[0], half[1], half[2], half[3]);
+        }
       }
     }
+
+    // both waves hold their operands: release the buffer, start the next copy
+    __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): all LDS reads returned
+    __syncthreads();
+    if (next >= 0) issue_tile(next);
+
     // element causality on the diagonal tile; row max
-    const bool diag = (kb == qb);
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float s = sacc[mt][r];
-        if (diag) {
+        if constexpr (kDiag) {
           const int key = 32 * mt + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key > q_local) s = -INFINITY;
+          if (key > q_local) sacc[mt][r] = -INFINITY;
         }
-        sacc[mt][r] = s;
-        mx = fmaxf(mx, s);
+        mx = fmaxf(mx, sacc[mt][r]);
       }
     }
     mx = pair_max(mx) * c;                         // row max of this tile, log2 units
@@ -202,7 +255,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_fwd_kernel(At
     const bool upd = mx > m + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(upd)) {
       const float mn = upd ? mx : m;
-      const float alpha = exp2f(m - mn);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);   // m = -inf on the first tile: alpha = 0
       lsum *= alpha;
 #pragma unroll
       for (int i = 0; i < MT; ++i) oacc[i] *= alpha;
@@ -218,7 +271,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_fwd_kernel(At
         float e[8];
 #pragma unroll
         for (int s8 = 0; s8 < 8; ++s8) {
-          e[s8] = exp2f(fmaf(sacc[mt][8 * hh + s8], c, -m));
+          e[s8] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][8 * hh + s8], c, -m));
           ls += e[s8];
         }
         pb[2 * mt + hh] = make_uint4(pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
@@ -228,23 +281,28 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_fwd_kernel(At
     lsum += ls;
     // O^T += V^T P^T  (32 dims x 32 queries per m-tile, 4 k-steps of 16 keys)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int dim = 32 * mt + l32;
-        const uint4 a = Vt[dim * 8 + ((2 * ks + hl) ^ swz_v(dim))];
-        oacc[mt] = mfma_32x32x16(a, pb[ks], oacc[mt]);
-      }
-    }
+      for (int mt = 0; mt < MT; ++mt) oacc[mt] = mfma_32x32x16(va[ks][mt], pb[ks], oacc[mt]);
+  };
+
+  // wait for this wave's copy of the current tile, then make both halves visible
+  auto tile_ready = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0f70);           // vmcnt(0)
+    __syncthreads();
   };
 
   // ---- main loop over active key blocks -----------------------------------
+  // The diagonal block (the only one needing element causality) goes first,
+  // then the other active blocks in ascending order; dense rows use the same
+  // order, so an all-ones mask reproduces the dense kernel bit for bit.
   if constexpr (MODE == kSparse) {
     const uint8_t* mrow = p.mask + (static_cast<size_t>(bh) * p.nb + qb) * p.nb;
-    const int ncol = qb + 1;                    // causal candidates 0..qb
-    for (int c0 = 0; c0 < ncol; c0 += kListCap) {
+    const bool diag_on = __builtin_amdgcn_readfirstlane(static_cast<int>(mrow[qb])) != 0;
+    const int ncol = qb;                        // off-diagonal causal candidates 0..qb-1
+    // compaction of columns [c0, c1): thread owns 16 consecutive columns
+    auto compact = [&](int c0) {
       const int c1 = min(ncol, c0 + kListCap);
-      // compaction: thread owns 16 consecutive columns
       const int j0 = c0 + 16 * tid;
       uint32_t bits = 0;
       if (j0 < c1) {
@@ -267,27 +325,42 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_fwd_kernel(At
         list[pos++] = static_cast<uint16_t>(j0 + e);
       }
       __syncthreads();
-      if (cnt_total > 0) {
-        fetch(list[0]);
-        for (int n = 0; n < cnt_total; ++n) {
-          const int kb = list[n];
-          __syncthreads();
-          stage();
-          __syncthreads();
-          if (n + 1 < cnt_total) fetch(list[n + 1]);
-          compute(kb);
+      return cnt_total;
+    };
+    int c0 = 0;
+    int cnt = compact(0);
+    bool issued = false;                        // list[0] of the current pass already in flight
+    if (diag_on) {
+      issue_tile(qb);
+      tile_ready();
+      const int first = cnt > 0 ? __builtin_amdgcn_readfirstlane(list[0]) : -1;
+      compute(std::true_type{}, qb, first);
+      issued = cnt > 0;
+    }
+    while (true) {
+      if (cnt > 0) {
+        int kb = __builtin_amdgcn_readfirstlane(list[0]);   // list entries are wave-uniform
+        if (!issued) issue_tile(kb);
+        for (int n = 0; n < cnt; ++n) {
+          const int next = n + 1 < cnt ? __builtin_amdgcn_readfirstlane(list[n + 1]) : -1;
+          tile_ready();
+          compute(std::false_type{}, kb, next);
+          kb = next;
         }
       }
-      __syncthreads();                            // list and wsum reused by the next pass
+      c0 += kListCap;
+      if (c0 >= ncol) break;
+      __syncthreads();                          // list and wsum are reused by the next pass
+      cnt = compact(c0);
+      issued = false;
     }
   } else {
-    fetch(0);
-    for (int kb = 0; kb <= qb; ++kb) {
-      __syncthreads();
-      stage();
-      __syncthreads();
-      if (kb < qb) fetch(kb + 1);
-      compute(kb);
+    issue_tile(qb);
+    tile_ready();
+    compute(std::true_type{}, qb, qb > 0 ? 0 : -1);
+    for (int kb = 0; kb < qb; ++kb) {
+      tile_ready();
+      compute(std::false_type{}, kb, kb + 1 < qb ? kb + 1 : -1);
     }
   }
 

@@ -10,7 +10,7 @@
 #include <mutex>
 #include <string>
 
-#include "../../include/seer.h"
+#include "seer.h"
 #include "seer_internal.h"
 
 namespace {
@@ -80,17 +80,21 @@ seer_status check_device() {
   return SEER_OK;
 }
 
-int attn_sched(const seer_shape* s) {
+// Workgroup order of the attention kernels (see attn_kernels.hip). Measured on
+// MI355X at 32k and 128k tokens: KV-group-major order keeps one group's K/V
+// in the Infinity Cache; for block-sparse rows, head-major inside the group
+// additionally keeps rows of similar density together. SEER_ATTN_SCHED=0..3
+// overrides the choice (results are identical, only the order changes).
+int attn_sched(int mode) {
   static int env = [] {
     const char* v = getenv("SEER_ATTN_SCHED");
     return v ? atoi(v) : -1;
   }();
-  const int bh = s->batch * s->heads_q;
-  if (env == 0) return 0;
-  return (bh % 8 == 0) ? 1 : 0;
+  if (env >= 0 && env <= 3) return env;
+  return mode == 0 ? 3 : 2;
 }
 
-seer::AttnArgs attn_args(const seer_shape* s, const void* q, const void* k, const void* v) {
+seer::AttnArgs attn_args(const seer_shape* s, const void* q, const void* k, const void* v, int mode) {
   seer::AttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -104,7 +108,7 @@ seer::AttnArgs attn_args(const seer_shape* s, const void* q, const void* k, cons
   a.group = s->heads_q / s->heads_kv;
   a.ntri = static_cast<long long>(a.nb) * (a.nb + 1) / 2;
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(s->head_dim)));
-  a.sched = attn_sched(s);
+  a.sched = attn_sched(mode);
   return a;
 }
 
@@ -257,7 +261,7 @@ seer_status seer_block_sparse_attn_fwd(const seer_shape* shape, const void* q, c
   if ((st = check_qkv(q, k, v)) != SEER_OK) return st;
   if ((st = check_out(out, out_dtype, lse)) != SEER_OK) return st;
   if ((st = check_device()) != SEER_OK) return st;
-  seer::AttnArgs a = attn_args(shape, q, k, v);
+  seer::AttnArgs a = attn_args(shape, q, k, v, block_mask ? 0 : 1);
   a.mask = block_mask;
   a.out = out;
   a.lse = lse;
@@ -292,7 +296,7 @@ seer_status seer_attn_maxpool_gt(const seer_shape* shape, const void* q, const v
     return fail(SEER_ERR_WORKSPACE, "workspace must be %zu bytes, 16-byte aligned (got %zu at %p)", need,
                 workspace_bytes, workspace);
   if ((st = check_device()) != SEER_OK) return st;
-  seer::AttnArgs a = attn_args(shape, q, k, v);
+  seer::AttnArgs a = attn_args(shape, q, k, v, 2);
   a.out = out;
   a.lse = lse;
   a.out_bf16 = out_dtype == SEER_BF16;

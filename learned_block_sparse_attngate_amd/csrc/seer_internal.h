@@ -21,7 +21,7 @@ struct AttnArgs {
   long long ntri;      // nb(nb+1)/2
   float scale_log2;    // log2(e) / sqrt(D)
   int out_bf16;
-  int sched;           // 0: heads interleaved across XCDs, 1: a KV group's heads on one XCD
+  int sched;           // workgroup order, see attn_fwd_kernel
 };
 
 // mode: 0 block-sparse (mask), 1 dense causal, 2 dense causal + ground-truth maxima
