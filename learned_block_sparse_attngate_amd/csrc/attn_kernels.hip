@@ -21,19 +21,24 @@
 //    (32 of its keys in the lane, the other 32 in lane l^32), and
 //    O^T = V^T P^T consumes the S^T registers directly as the B operand, so P
 //    never goes through LDS;
-//  * K and V tiles move HBM -> LDS with global_load_lds_dwordx4 (no register
-//    staging); the XOR swizzle is applied on the source side so the LDS image
-//    is conflict-free for the 16-byte K operand reads and for the
+//  * K and V tiles move HBM -> LDS with buffer_load_dwordx4 ... lds (no
+//    register staging); the XOR swizzle is applied on the source side so the
+//    LDS image is conflict-free for the 16-byte K operand reads and for the
 //    ds_read_b64_tr_b16 transposing reads that build the V^T operand;
-//  * each wave copies the tile's operands from LDS into registers, then the
-//    single LDS buffer is released and the next tile's copy is issued, so the
-//    HBM/L2 latency of tile n+1 overlaps the softmax and P.V of tile n;
+//  * K and V have one LDS buffer each and are refilled independently: the K
+//    copy of the next tile starts as soon as both waves hold this tile's K
+//    operands, the V copy as soon as they hold its V operands, so each copy
+//    overlaps roughly one full tile of work. The operand reads are
+//    inline-assembly blocks that wait for their own results before they end;
+//    this keeps the compiler from inserting a wait for every copy in flight
+//    before each LDS read, and the copies are tracked with explicit vmcnt
+//    waits instead;
 //  * the active key blocks of a row are compacted on chip from the mask row
 //    into an LDS list (ascending), so masked tiles cost neither time nor HBM
-//    traffic and no separate compaction launch or workspace is needed;
-//  * rows are launched heaviest first (descending query block) and, when the
-//    head count allows, the query heads of one KV head are kept on one XCD so
-//    that they share K/V tiles in that XCD's L2.
+//    traffic and no separate compaction launch or workspace is needed; the
+//    diagonal tile's copy is started before the compaction;
+//  * the workgroup order keeps one KV group's K/V hot at a time and launches
+//    the heaviest rows first.
 #include <type_traits>
 
 #include "seer_device.h"
@@ -43,17 +48,17 @@ namespace seer {
 
 namespace {
 
-constexpr int kThreads = 128;          // 2 wavefronts
-constexpr int kListCap = 2048;         // mask columns compacted per pass
+constexpr int kThreads = 128;            // 2 wavefronts
+constexpr int kListCap = 2048;           // mask columns compacted per pass
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag by
-constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer resource, dword 3
+constexpr float kRescaleSlack = 8.0f;    // log2 units the running max may lag by
+constexpr int kBufferWord3 = 0x00020000; // gfx9-family raw buffer resource, dword 3
 
 enum Mode { kSparse = 0, kDense = 1, kDenseGt = 2 };
 
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // 16-byte-chunk XOR swizzles (chunk index within a row of the LDS tile).
 //  K: the 32x32x16 A-operand read has 16 consecutive keys at one logical chunk.
@@ -61,13 +66,37 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 template <int D> __device__ __forceinline__ int swz_k(int row) { return row & (D / 8 - 1); }
 template <int D> __device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * (row & 1); }
 
-__device__ __forceinline__ int bsum_exclusive(int x, int lane, int wave, int* wsum, int& total) {
-  int inc = wave_inclusive_scan(x, lane);
-  if (lane == kWave - 1) wsum[wave] = inc;
-  __syncthreads();
-  int w0 = wsum[0];
-  total = w0 + wsum[1];
-  return inc - x + (wave == 1 ? w0 : 0);
+// Workgroup barrier without a memory fence. Inside the tile pipeline the
+// copies into LDS are ordered with explicit vmcnt waits and the LDS reads
+// with lgkmcnt waits; a fence would also wait for every copy in flight.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left at their maxima)
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0f70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0f71); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0f74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0f75); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0f78); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0f79); break;
+  }
+}
+
+// LDS reads outside the compiler's view of the copies in flight; each waits
+// for its own result before returning.
+__device__ __forceinline__ uint32_t lds_read_u16(uint32_t addr) {
+  uint32_t v;
+  asm volatile("ds_read_u16 %0, %1\n s_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ uint32_t lds_read_u32(uint32_t addr) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n s_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)p));
 }
 
 template <int D, int MODE>
@@ -75,8 +104,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   constexpr int CPR = D / 8;               // 16-byte chunks per K/V row
   constexpr int KS = D / 16;               // MFMA k-steps for S^T
   constexpr int MT = D / 32;               // MFMA m-tiles for O^T
-  constexpr int RPI = 64 / CPR;            // tile rows per global_load_lds instruction
-  constexpr int NDMA = 32 / RPI;           // instructions per wave per operand (32 rows)
+  constexpr int RPI = 64 / CPR;            // tile rows per copy instruction
+  constexpr int NDMA = 32 / RPI;           // copy instructions per wave per operand (32 rows)
 
   __shared__ uint4 Ks[kBlock * CPR];       // K tile [64 keys][D], swizzled chunks
   __shared__ uint4 Vs[kBlock * CPR];       // V tile [64 keys][D], swizzled chunks
@@ -96,7 +125,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   //  0: heads interleaved, all KV groups at once;
   //  1: the query heads of one KV group on one XCD;
   //  2: KV-group major: every XCD works on the same KV group at a time, so
-  //     the K/V working set is one group (it stays in the Infinity Cache);
+  //     the K/V working set is one group;
   //  3: KV-group major, then head major inside the group.
   const int BH = p.B * p.Hq;
   const int w = blockIdx.x;
@@ -122,6 +151,64 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   const uint16_t* __restrict__ Kg = p.k + kv_off;
   const uint16_t* __restrict__ Vg = p.v + kv_off;
 
+  // ---- HBM -> LDS copies ---------------------------------------------------
+  // Instruction i, lane l writes LDS bytes [1024 i + 16 l) of this wave's half
+  // (rows 32w .. 32w+31): tile row r = 32w + RPI*i + l/CPR, physical chunk
+  // l%CPR, holding logical chunk (l%CPR) ^ swz(r). With the swizzles above the
+  // V chunk does not depend on i and the K chunk takes four values, so a few
+  // per-lane byte offsets address every instruction. The buffer resource starts
+  // at the tile and ends at the head's last row, so rows past the sequence
+  // (ragged last tile) read as zeros: their scores are masked by causality and
+  // their P is 0.
+  uint32_t kofs[4], vofs;
+  {
+    const int r0 = 32 * wave + lane / CPR;
+    const int pc = lane % CPR;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) kofs[v] = static_cast<uint32_t>(r0 * 2 * D + 16 * (pc ^ swz_k<D>(r0 + RPI * v)));
+    vofs = static_cast<uint32_t>(r0 * 2 * D + 16 * (pc ^ swz_v<D>(r0)));
+  }
+  auto issue_k = [&](int kb) {
+    const int key0 = kb * kBlock;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kg + static_cast<size_t>(key0) * D), 0,
+                                                      (p.S - key0) * 2 * D, kBufferWord3);
+    char* dst = reinterpret_cast<char*>(Ks) + 32 * wave * D * 2;
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const uint32_t ko = (D == 128 ? kofs[i & 3] : kofs[0]) + static_cast<uint32_t>(RPI * i * 2 * D);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + 1024 * i), 16, ko, 0, 0, 0);
+    }
+  };
+  auto issue_v = [&](int kb) {
+    const int key0 = kb * kBlock;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Vg + static_cast<size_t>(key0) * D), 0,
+                                                      (p.S - key0) * 2 * D, kBufferWord3);
+    char* dst = reinterpret_cast<char*>(Vs) + 32 * wave * D * 2;
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + 1024 * i), 16,
+                                               vofs + static_cast<uint32_t>(RPI * i * 2 * D), 0, 0, 0);
+  };
+
+  // LDS byte addresses of the operand reads (loop invariant)
+  uint32_t kaddr[KS], vaddr[MT];
+  {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kaddr[ks] = lds_addr(Ks) + l32 * 2 * D + 16 * ((2 * ks + hl) ^ swz_k<D>(l32));
+    // transposing reads: within each 16-lane group, lane 4j+a points at 4
+    // dims of key j; the instruction hands lane i the 4 keys of dim i
+    const int G = lane >> 4, j = (lane >> 2) & 3, a = lane & 3;
+    const int key = 4 * (G >> 1) + j;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      vaddr[mt] = lds_addr(Vs) + key * 2 * D + 16 * ((4 * mt + 2 * (G & 1) + (a >> 1)) ^ swz_v<D>(key)) + 8 * (a & 1);
+  }
+
+  // the diagonal tile is processed first; start its copy before anything else
+  issue_k(qb);
+  issue_v(qb);
+
   // ---- Q fragment (B operand of S^T = K Q^T), resident for the row ------
   const int q_local = wave * 32 + l32;            // query row within the block
   const int t = qb * kBlock + q_local;            // query position
@@ -141,97 +228,57 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
 #pragma unroll
   for (int i = 0; i < MT; ++i) oacc[i] = f32x16_t{};
 
-  // ---- HBM -> LDS copy of one K/V tile; this wave moves rows 32w .. 32w+31 --
-  // buffer_load_dwordx4 ... lds: instruction i, lane l writes LDS bytes
-  // [1024 i + 16 l) of this wave's half: tile row r = 32w + RPI*i + l/CPR,
-  // physical chunk l%CPR, holding logical chunk (l%CPR) ^ swz(r). With the
-  // swizzles above the V chunk does not depend on i and the K chunk takes four
-  // values, so a few per-lane byte offsets address every instruction. The
-  // buffer resource starts at the tile and ends at the head's last row, so rows
-  // past the sequence (ragged last tile) read as zeros: their scores are masked
-  // by causality and their P is 0.
-  uint32_t kofs[4], vofs;
-  {
-    const int r0 = 32 * wave + lane / CPR;                  // row for i = 0
-    const int pc = lane % CPR;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = r0 + RPI * v;                             // swz_k(r) for i = v (mod 4)
-      kofs[v] = static_cast<uint32_t>(r0 * 2 * D + 16 * (pc ^ swz_k<D>(r)));
-    }
-    vofs = static_cast<uint32_t>(r0 * 2 * D + 16 * (pc ^ swz_v<D>(r0)));
-  }
-  auto issue_tile = [&](int kb) {
-    const int key0 = kb * kBlock;
-    const int nbytes = (p.S - key0) * 2 * D;
-    const auto kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kg + static_cast<size_t>(key0) * D), 0,
-                                                      nbytes, kBufferWord3);
-    const auto vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Vg + static_cast<size_t>(key0) * D), 0,
-                                                      nbytes, kBufferWord3);
-    char* kl = reinterpret_cast<char*>(Ks) + 32 * wave * D * 2;
-    char* vl = reinterpret_cast<char*>(Vs) + 32 * wave * D * 2;
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const uint32_t step = static_cast<uint32_t>(RPI * i * 2 * D);
-      const uint32_t ko = (D == 128 ? kofs[i & 3] : kofs[0]) + step;  // D = 64: swz_k(r) = r & 7 is i-invariant
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(kl + 1024 * i), 16, ko, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(vl + 1024 * i), 16, vofs + step, 0, 0, 0);
-    }
-  };
-
   const long long ntri_off = static_cast<long long>(qb) * (qb + 1) / 2;  // ground-truth scratch offset of this row
 
-  // One tile. On entry the tile is in LDS (this wave's copy completed and the
-  // workgroup synchronized); `next` >= 0 is issued as soon as both waves have
-  // pulled their operands out of LDS.
-  auto compute = [&](auto diag_tag, int kb, int next) {
+  // One tile. On entry the copies of tile kb are in flight or landed, K issued
+  // before V. `first`: nothing but this tile's V copy was issued after its K
+  // copy. `stores_pending`: ground-truth stores issued after the last V copy.
+  int stores_pending = 0;
+  auto compute = [&](auto diag_tag, int kb, int next, bool first) {
     constexpr bool kDiag = decltype(diag_tag)::value;   // the diagonal tile needs element causality
-    // operands of S^T = K Q^T: A = K rows (32 keys x 16 dims per m-tile / k-step)
-    uint4 ka[2][KS];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int key = 32 * mt + l32;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) ka[mt][ks] = Ks[key * CPR + ((2 * ks + hl) ^ swz_k<D>(key))];
+    // ---- K: wait for the copy (only V of this tile and newer stores may be outstanding)
+    wait_vmcnt(first ? NDMA : NDMA + stores_pending);
+    wg_barrier();
+    u32x4_t kr[2 * KS];                           // kr[2 ks + mt]: keys 32 mt + l32, dims 16 ks + 8 hl ..
+    if constexpr (D == 128) {
+      asm volatile(
+          "ds_read_b128 %0, %16\n ds_read_b128 %1, %16 offset:8192\n"
+          "ds_read_b128 %2, %17\n ds_read_b128 %3, %17 offset:8192\n"
+          "ds_read_b128 %4, %18\n ds_read_b128 %5, %18 offset:8192\n"
+          "ds_read_b128 %6, %19\n ds_read_b128 %7, %19 offset:8192\n"
+          "ds_read_b128 %8, %20\n ds_read_b128 %9, %20 offset:8192\n"
+          "ds_read_b128 %10, %21\n ds_read_b128 %11, %21 offset:8192\n"
+          "ds_read_b128 %12, %22\n ds_read_b128 %13, %22 offset:8192\n"
+          "ds_read_b128 %14, %23\n ds_read_b128 %15, %23 offset:8192\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(kr[4]), "=&v"(kr[5]), "=&v"(kr[6]),
+            "=&v"(kr[7]), "=&v"(kr[8]), "=&v"(kr[9]), "=&v"(kr[10]), "=&v"(kr[11]), "=&v"(kr[12]), "=&v"(kr[13]),
+            "=&v"(kr[14]), "=&v"(kr[15])
+          : "v"(kaddr[0]), "v"(kaddr[1]), "v"(kaddr[2]), "v"(kaddr[3]), "v"(kaddr[4]), "v"(kaddr[5]),
+            "v"(kaddr[6]), "v"(kaddr[7])
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %8\n ds_read_b128 %1, %8 offset:4096\n"
+          "ds_read_b128 %2, %9\n ds_read_b128 %3, %9 offset:4096\n"
+          "ds_read_b128 %4, %10\n ds_read_b128 %5, %10 offset:4096\n"
+          "ds_read_b128 %6, %11\n ds_read_b128 %7, %11 offset:4096\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(kr[4]), "=&v"(kr[5]), "=&v"(kr[6]),
+            "=&v"(kr[7])
+          : "v"(kaddr[0]), "v"(kaddr[1]), "v"(kaddr[2]), "v"(kaddr[3])
+          : "memory");
     }
+    wg_barrier();                                  // both waves hold K: refill the K buffer
+    if (next >= 0) issue_k(next);
+
+    // ---- S^T = K Q^T (32 keys x 32 queries per m-tile, two m-tiles)
     f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) sacc[mt] = mfma_32x32x16(ka[mt][ks], qreg[ks], sacc[mt]);
-    // keep the V^T reads below the S MFMAs so K and V operands are never live together
-    __builtin_amdgcn_sched_barrier(0);
-
-    // operands of O^T = V^T P^T: A = V^T (32 dims x 16 keys), two transposing
-    // reads of 4 keys each; key order matches the S^T accumulator layout
-    uint4 va[4][MT];
-    {
-      const int G = lane >> 4, j = (lane >> 2) & 3, a = lane & 3;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          uint32_t half[4];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int key = 16 * ks + 8 * u + 4 * (G >> 1) + j;
-            const int ch = 4 * mt + 2 * (G & 1) + (a >> 1);
-            const int off = key * (2 * D) + ((ch ^ swz_v<D>(key)) << 4) + ((a & 1) << 3);
-            const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4_t*)(reinterpret_cast<char*>(Vs) + off));
-            const uint2 r2 = __builtin_bit_cast(uint2, r);
-            half[2 * u] = r2.x;
-            half[2 * u + 1] = r2.y;
-          }
-          va[ks][mt] = make_uint4(half[0], half[1], half[2], half[3]);
-        }
-      }
-    }
-
-    // both waves hold their operands: release the buffer, start the next copy
-    __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): all LDS reads returned
-    __syncthreads();
-    if (next >= 0) issue_tile(next);
+      for (int mt = 0; mt < 2; ++mt)
+        sacc[mt] = mfma_32x32x16(__builtin_bit_cast(uint4, kr[2 * ks + mt]), qreg[ks], sacc[mt]);
 
     // element causality on the diagonal tile; row max
     float mx = -INFINITY;
@@ -247,10 +294,63 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
       }
     }
     mx = pair_max(mx) * c;                         // row max of this tile, log2 units
+    int stores_now = 0;
     if constexpr (MODE == kDenseGt) {
-      if (hl == 0)
-        p.rmax[((static_cast<size_t>(bh) * p.ntri + ntri_off + kb) << 6) + q_local] = mx;
+      if (hl == 0) p.rmax[((static_cast<size_t>(bh) * p.ntri + ntri_off + kb) << 6) + q_local] = mx;
+      stores_now = 1;
     }
+
+    // ---- V: wait for the copy (the K copy of `next` and this tile's store may be newer)
+    wait_vmcnt((next >= 0 ? NDMA : 0) + stores_now);
+    wg_barrier();
+    u32x2_t vr[8 * MT];                            // vr[(ks MT + mt) 2 + u]: dims 32 mt + .., keys 16 ks + 8 u + ..
+    if constexpr (D == 128) {
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %32\n ds_read_b64_tr_b16 %1, %32 offset:2048\n"
+          "ds_read_b64_tr_b16 %2, %33\n ds_read_b64_tr_b16 %3, %33 offset:2048\n"
+          "ds_read_b64_tr_b16 %4, %34\n ds_read_b64_tr_b16 %5, %34 offset:2048\n"
+          "ds_read_b64_tr_b16 %6, %35\n ds_read_b64_tr_b16 %7, %35 offset:2048\n"
+          "ds_read_b64_tr_b16 %8, %32 offset:4096\n ds_read_b64_tr_b16 %9, %32 offset:6144\n"
+          "ds_read_b64_tr_b16 %10, %33 offset:4096\n ds_read_b64_tr_b16 %11, %33 offset:6144\n"
+          "ds_read_b64_tr_b16 %12, %34 offset:4096\n ds_read_b64_tr_b16 %13, %34 offset:6144\n"
+          "ds_read_b64_tr_b16 %14, %35 offset:4096\n ds_read_b64_tr_b16 %15, %35 offset:6144\n"
+          "ds_read_b64_tr_b16 %16, %32 offset:8192\n ds_read_b64_tr_b16 %17, %32 offset:10240\n"
+          "ds_read_b64_tr_b16 %18, %33 offset:8192\n ds_read_b64_tr_b16 %19, %33 offset:10240\n"
+          "ds_read_b64_tr_b16 %20, %34 offset:8192\n ds_read_b64_tr_b16 %21, %34 offset:10240\n"
+          "ds_read_b64_tr_b16 %22, %35 offset:8192\n ds_read_b64_tr_b16 %23, %35 offset:10240\n"
+          "ds_read_b64_tr_b16 %24, %32 offset:12288\n ds_read_b64_tr_b16 %25, %32 offset:14336\n"
+          "ds_read_b64_tr_b16 %26, %33 offset:12288\n ds_read_b64_tr_b16 %27, %33 offset:14336\n"
+          "ds_read_b64_tr_b16 %28, %34 offset:12288\n ds_read_b64_tr_b16 %29, %34 offset:14336\n"
+          "ds_read_b64_tr_b16 %30, %35 offset:12288\n ds_read_b64_tr_b16 %31, %35 offset:14336\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]),
+            "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]), "=&v"(vr[12]), "=&v"(vr[13]),
+            "=&v"(vr[14]), "=&v"(vr[15]), "=&v"(vr[16]), "=&v"(vr[17]), "=&v"(vr[18]), "=&v"(vr[19]),
+            "=&v"(vr[20]), "=&v"(vr[21]), "=&v"(vr[22]), "=&v"(vr[23]), "=&v"(vr[24]), "=&v"(vr[25]),
+            "=&v"(vr[26]), "=&v"(vr[27]), "=&v"(vr[28]), "=&v"(vr[29]), "=&v"(vr[30]), "=&v"(vr[31])
+          : "v"(vaddr[0]), "v"(vaddr[1]), "v"(vaddr[2]), "v"(vaddr[3])
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %16\n ds_read_b64_tr_b16 %1, %16 offset:1024\n"
+          "ds_read_b64_tr_b16 %2, %17\n ds_read_b64_tr_b16 %3, %17 offset:1024\n"
+          "ds_read_b64_tr_b16 %4, %16 offset:2048\n ds_read_b64_tr_b16 %5, %16 offset:3072\n"
+          "ds_read_b64_tr_b16 %6, %17 offset:2048\n ds_read_b64_tr_b16 %7, %17 offset:3072\n"
+          "ds_read_b64_tr_b16 %8, %16 offset:4096\n ds_read_b64_tr_b16 %9, %16 offset:5120\n"
+          "ds_read_b64_tr_b16 %10, %17 offset:4096\n ds_read_b64_tr_b16 %11, %17 offset:5120\n"
+          "ds_read_b64_tr_b16 %12, %16 offset:6144\n ds_read_b64_tr_b16 %13, %16 offset:7168\n"
+          "ds_read_b64_tr_b16 %14, %17 offset:6144\n ds_read_b64_tr_b16 %15, %17 offset:7168\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]),
+            "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]), "=&v"(vr[12]), "=&v"(vr[13]),
+            "=&v"(vr[14]), "=&v"(vr[15])
+          : "v"(vaddr[0]), "v"(vaddr[1])
+          : "memory");
+    }
+    wg_barrier();                                  // both waves hold V: refill the V buffer
+    if (next >= 0) issue_v(next);
+    stores_pending = stores_now;
+
     // lazy rescale: move the running max only when it grows by > slack
     const bool upd = mx > m + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(upd)) {
@@ -279,17 +379,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
       }
     }
     lsum += ls;
-    // O^T += V^T P^T  (32 dims x 32 queries per m-tile, 4 k-steps of 16 keys)
+    // ---- O^T += V^T P^T (32 dims x 32 queries per m-tile, 4 k-steps of 16 keys)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) oacc[mt] = mfma_32x32x16(va[ks][mt], pb[ks], oacc[mt]);
-  };
-
-  // wait for this wave's copy of the current tile, then make both halves visible
-  auto tile_ready = [&]() {
-    __builtin_amdgcn_s_waitcnt(0x0f70);           // vmcnt(0)
-    __syncthreads();
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x2_t lo = vr[(ks * MT + mt) * 2], hi = vr[(ks * MT + mt) * 2 + 1];
+        oacc[mt] = mfma_32x32x16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[ks], oacc[mt]);
+      }
   };
 
   // ---- main loop over active key blocks -----------------------------------
@@ -298,10 +395,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   // order, so an all-ones mask reproduces the dense kernel bit for bit.
   if constexpr (MODE == kSparse) {
     const uint8_t* mrow = p.mask + (static_cast<size_t>(bh) * p.nb + qb) * p.nb;
-    const bool diag_on = __builtin_amdgcn_readfirstlane(static_cast<int>(mrow[qb])) != 0;
     const int ncol = qb;                        // off-diagonal causal candidates 0..qb-1
-    // compaction of columns [c0, c1): thread owns 16 consecutive columns
-    auto compact = [&](int c0) {
+    const uint32_t list_lds = lds_addr(list), wsum_lds = lds_addr(wsum);
+    // mask bytes of columns [c0, min(ncol, c0 + kListCap)) -> 16 flags per thread
+    auto load_bits = [&](int c0) {
       const int c1 = min(ncol, c0 + kListCap);
       const int j0 = c0 + 16 * tid;
       uint32_t bits = 0;
@@ -317,51 +414,63 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
             if (mrow[j0 + e]) bits |= 1u << e;
         }
       }
-      int cnt_total;
-      int pos = bsum_exclusive(__builtin_popcount(bits), lane, wave, wsum, cnt_total);
+      return bits;
+    };
+    // ascending list of the active columns; returns their count. Only
+    // fence-free barriers and LDS reads outside the compiler's tracking here:
+    // the diagonal tile's copy may be in flight.
+    auto compact = [&](int c0, uint32_t bits) {
+      const int cnt = __builtin_popcount(bits);
+      const int inc = wave_inclusive_scan(cnt, lane);
+      if (lane == kWave - 1) wsum[wave] = inc;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      wg_barrier();
+      const int w0 = static_cast<int>(lds_read_u32(wsum_lds));
+      const int total = w0 + static_cast<int>(lds_read_u32(wsum_lds + 4));
+      int pos = inc - cnt + (wave == 1 ? w0 : 0);
+      const int j0 = c0 + 16 * tid;
       while (bits) {
         const int e = __builtin_ctz(bits);
         bits &= bits - 1;
         list[pos++] = static_cast<uint16_t>(j0 + e);
       }
-      __syncthreads();
-      return cnt_total;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      wg_barrier();
+      return __builtin_amdgcn_readfirstlane(total);
     };
+    const bool diag_on = __builtin_amdgcn_readfirstlane(static_cast<int>(mrow[qb])) != 0;
     int c0 = 0;
-    int cnt = compact(0);
+    int cnt = compact(0, load_bits(0));
     bool issued = false;                        // list[0] of the current pass already in flight
     if (diag_on) {
-      issue_tile(qb);
-      tile_ready();
-      const int first = cnt > 0 ? __builtin_amdgcn_readfirstlane(list[0]) : -1;
-      compute(std::true_type{}, qb, first);
+      const int nxt = cnt > 0 ? __builtin_amdgcn_readfirstlane(static_cast<int>(lds_read_u16(list_lds))) : -1;
+      compute(std::true_type{}, qb, nxt, true);
       issued = cnt > 0;
+    } else {
+      wait_vmcnt(0);                            // the early copy of the diagonal tile is not used
+      wg_barrier();
     }
     while (true) {
       if (cnt > 0) {
-        int kb = __builtin_amdgcn_readfirstlane(list[0]);   // list entries are wave-uniform
-        if (!issued) issue_tile(kb);
+        int kb = __builtin_amdgcn_readfirstlane(static_cast<int>(lds_read_u16(list_lds)));
+        bool first = !issued;
+        if (!issued) { issue_k(kb); issue_v(kb); }
         for (int n = 0; n < cnt; ++n) {
-          const int next = n + 1 < cnt ? __builtin_amdgcn_readfirstlane(list[n + 1]) : -1;
-          tile_ready();
-          compute(std::false_type{}, kb, next);
+          const int next =
+              n + 1 < cnt ? __builtin_amdgcn_readfirstlane(static_cast<int>(lds_read_u16(list_lds + 2 * (n + 1)))) : -1;
+          compute(std::false_type{}, kb, next, first);
+          first = false;
           kb = next;
         }
       }
       c0 += kListCap;
       if (c0 >= ncol) break;
-      __syncthreads();                          // list and wsum are reused by the next pass
-      cnt = compact(c0);
+      cnt = compact(c0, load_bits(c0));         // no copy in flight here
       issued = false;
     }
   } else {
-    issue_tile(qb);
-    tile_ready();
-    compute(std::true_type{}, qb, qb > 0 ? 0 : -1);
-    for (int kb = 0; kb < qb; ++kb) {
-      tile_ready();
-      compute(std::false_type{}, kb, kb + 1 < qb ? kb + 1 : -1);
-    }
+    compute(std::true_type{}, qb, qb > 0 ? 0 : -1, true);
+    for (int kb = 0; kb < qb; ++kb) compute(std::false_type{}, kb, kb + 1 < qb ? kb + 1 : -1, false);
   }
 
   // ---- epilogue: normalize, store O and LSE --------------------------------
