@@ -133,8 +133,10 @@ def main():
         seer.seer_gate_fwd(q, k, wq, wk, mode="topk", topk=k_gate, scores=gate_scores, block_mask=gate_mask,
                            workspace=gate_ws)
 
+    attn_ws = torch.empty(max(seer.attn_workspace_bytes(B, Hq, Hkv, S, D), 16), dtype=torch.uint8, device=dev)
+
     def attn():
-        seer.seer_block_sparse_attn_fwd(q, k, v, mask, out=out)
+        seer.seer_block_sparse_attn_fwd(q, k, v, mask, out=out, workspace=attn_ws)
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

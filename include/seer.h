@@ -122,8 +122,15 @@ seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_
  *              attention over every block (the speedup denominator).
  * out          device [B,Hq,S,D] in out_dtype (fp32 or bf16)
  * lse          device fp32 [B,Hq,S] output, or NULL
- * workspace    may be NULL: seer_attn_workspace_size() is 0 (the active-block
- *              list of each row is compacted on chip)
+ * workspace    device scratch of at least seer_attn_workspace_size() bytes,
+ *              16-byte aligned, used only when block_mask is non-NULL. Rows
+ *              of more than 1024 blocks (seq_len > 65536) are processed in
+ *              key chunks of 512 blocks, so that the GPU works on one chunk
+ *              of K/V at a time, and leave per-chunk fp32 partial outputs
+ *              there that a second kernel merges (64 * (head_dim + 1) * 4
+ *              bytes per row and chunk). The size is 0, and workspace may be
+ *              NULL, when seq_len <= 65536. The active-block list of each row
+ *              is compacted on chip.
  * ---------------------------------------------------------------------- */
 size_t seer_attn_workspace_size(const seer_shape* shape);
 seer_status seer_block_sparse_attn_fwd(const seer_shape* shape, const void* q, const void* k,

@@ -5,7 +5,7 @@ thin ctypes binding over its C ABI (include/seer.h)."""
 from ._binding import (  # noqa: F401
     BLOCK, EXPORTED, LIB_PATH, SeerError, SeerShape, load_library, make_shape, nblocks,
     seer_gate_fwd, seer_block_sparse_attn_fwd, seer_attn_maxpool_gt,
-    gate_workspace_bytes, gt_workspace_bytes, version,
+    gate_workspace_bytes, gt_workspace_bytes, attn_workspace_bytes, version,
     SEER_OK, SEER_ERR_INVALID_ARG, SEER_ERR_SHAPE, SEER_ERR_UNSUPPORTED, SEER_ERR_WORKSPACE, SEER_ERR_HIP,
     SEER_MASK_THRESHOLD, SEER_MASK_TOPK, SEER_F32, SEER_BF16,
 )

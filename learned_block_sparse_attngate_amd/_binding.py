@@ -180,7 +180,8 @@ def seer_gate_fwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torc
 def seer_block_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                block_mask: Optional[torch.Tensor] = None, *,
                                out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
-                               lse: Optional[torch.Tensor] = None, want_lse: bool = False):
+                               lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                               workspace: Optional[torch.Tensor] = None):
     """Causal GQA block-sparse attention (block_mask=None: dense causal). Returns (out, lse or None)."""
     lib = load_library()
     _need(q, "q", torch.bfloat16)
@@ -201,8 +202,14 @@ def seer_block_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     dt = SEER_BF16 if out.dtype == torch.bfloat16 else SEER_F32
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out must be bfloat16 or float32")
+    ws_bytes = 0
+    if block_mask is not None:
+        workspace = _workspace(lib.seer_attn_workspace_size(ctypes.byref(shape)), dev, workspace)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    else:
+        workspace = None
     _check(lib.seer_block_sparse_attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_mask),
-                                          _ptr(out), dt, _ptr(lse), None, 0, _stream(dev)))
+                                          _ptr(out), dt, _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev)))
     return out, lse
 
 
@@ -233,6 +240,11 @@ def seer_attn_maxpool_gt(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     _check(lib.seer_attn_maxpool_gt(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(out), dt, _ptr(lse),
                                     _ptr(gt), _ptr(workspace), ws_bytes, _stream(dev)))
     return out, lse, gt
+
+
+def attn_workspace_bytes(batch, heads_q, heads_kv, seq_len, head_dim) -> int:
+    shape = make_shape(batch, heads_q, heads_kv, seq_len, head_dim)
+    return load_library().seer_attn_workspace_size(ctypes.byref(shape))
 
 
 def gt_workspace_bytes(batch, heads_q, heads_kv, seq_len, head_dim) -> int:

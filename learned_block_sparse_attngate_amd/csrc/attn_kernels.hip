@@ -35,10 +35,19 @@
 //    waits instead;
 //  * the active key blocks of a row are compacted on chip from the mask row
 //    into an LDS list (ascending), so masked tiles cost neither time nor HBM
-//    traffic and no separate compaction launch or workspace is needed; the
-//    diagonal tile's copy is started before the compaction;
+//    traffic and no separate compaction launch is needed; the diagonal tile's
+//    copy is started before the compaction;
 //  * the workgroup order keeps one KV group's K/V hot at a time and launches
-//    the heaviest rows first.
+//    the heaviest rows first;
+//  * block-sparse rows longer than 1024 blocks are cut into key chunks of 512
+//    blocks: a work item is (row, chunk), items go chunk by chunk, so all XCDs
+//    read one chunk of one KV group's K/V at a time; an item writes its
+//    normalized fp32 partial and log-sum-exp to the workspace and a second
+//    kernel merges the chunks of each row (split-KV); each item walks its
+//    tiles in a circular order phased by its dispatch slot, so the items
+//    resident on an XCD read neighbouring key blocks at the same time.
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "seer_device.h"
@@ -53,6 +62,8 @@ constexpr int kListCap = 2048;           // mask columns compacted per pass
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleSlack = 8.0f;    // log2 units the running max may lag by
 constexpr int kBufferWord3 = 0x00020000; // gfx9-family raw buffer resource, dword 3
+constexpr int kXcds = 8;                 // workgroups are dealt round-robin to the 8 XCDs
+constexpr int kSweepPhases = 128;        // resident workgroups per XCD (32 CUs x 4)
 
 enum Mode { kSparse = 0, kDense = 1, kDenseGt = 2 };
 
@@ -130,7 +141,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   const int BH = p.B * p.Hq;
   const int w = blockIdx.x;
   int qb, bh;
-  if (p.sched >= 2) {
+  int chunk = 0;                                  // block-sparse: key chunk of this work item
+  if constexpr (MODE == kSparse) {
+    // Key-chunked items: (batch, KV group) major, then chunk c ascending, then
+    // head, then query block descending. Consecutive items go round-robin over
+    // the XCDs, so all of them work on one C-block K/V chunk of one group at a
+    // time and that chunk stays in each XCD's L2.
+    const int gi = static_cast<int>(w / p.items_per_group);
+    long long r = w - gi * p.items_per_group;
+    int c = 0;
+    while (true) {
+      const long long n = static_cast<long long>(p.group) * (p.nb - c * p.chunk);   // items of chunk c
+      if (r < n) break;
+      r -= n;
+      ++c;
+    }
+    const int rows = p.nb - c * p.chunk;            // query blocks qb >= c*C
+    const int hig = static_cast<int>(r / rows);
+    qb = p.nb - 1 - static_cast<int>(r % rows);
+    chunk = c;
+    const int bb = gi / p.Hkv, gg = gi - bb * p.Hkv;
+    bh = bb * p.Hq + gg * p.group + hig;
+  } else if (p.sched >= 2) {
     const int R = p.group * p.nb;                 // rows per (batch, KV group)
     const int gi = w / R, r = w - gi * R;         // gi = b * Hkv + g
     int hig;
@@ -206,8 +238,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   }
 
   // the diagonal tile is processed first; start its copy before anything else
-  issue_k(qb);
-  issue_v(qb);
+  // (in block-sparse mode only the item whose chunk holds the diagonal has it)
+  if (MODE != kSparse || qb < (chunk + 1) * p.chunk) {
+    issue_k(qb);
+    issue_v(qb);
+  }
 
   // ---- Q fragment (B operand of S^T = K Q^T), resident for the row ------
   const int q_local = wave * 32 + l32;            // query row within the block
@@ -391,17 +426,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
 
   // ---- main loop over active key blocks -----------------------------------
   // The diagonal block (the only one needing element causality) goes first,
-  // then the other active blocks in ascending order; dense rows use the same
-  // order, so an all-ones mask reproduces the dense kernel bit for bit.
+  // then the other active blocks: in block-sparse mode in the circular order
+  // below, in dense mode ascending.
   if constexpr (MODE == kSparse) {
     const uint8_t* mrow = p.mask + (static_cast<size_t>(bh) * p.nb + qb) * p.nb;
-    const int ncol = qb;                        // off-diagonal causal candidates 0..qb-1
+    const int c0 = chunk * p.chunk;                     // this item's key blocks: [c0, c1) plus maybe the diagonal
+    const int c1 = min(qb, c0 + p.chunk);               // off-diagonal candidates (C <= kListCap)
+    const bool has_diag = qb < c0 + p.chunk;
     const uint32_t list_lds = lds_addr(list), wsum_lds = lds_addr(wsum);
-    // mask bytes of columns [c0, min(ncol, c0 + kListCap)) -> 16 flags per thread
-    auto load_bits = [&](int c0) {
-      const int c1 = min(ncol, c0 + kListCap);
+    // mask bytes of columns [c0, c1) -> 16 flags per thread
+    uint32_t bits = 0;
+    {
       const int j0 = c0 + 16 * tid;
-      uint32_t bits = 0;
       if (j0 < c1) {
         if (j0 + 16 <= c1 && ((reinterpret_cast<uintptr_t>(mrow + j0) & 15) == 0)) {
           const uint4 v4 = *reinterpret_cast<const uint4*>(mrow + j0);
@@ -414,20 +450,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
             if (mrow[j0 + e]) bits |= 1u << e;
         }
       }
-      return bits;
-    };
-    // ascending list of the active columns; returns their count. Only
-    // fence-free barriers and LDS reads outside the compiler's tracking here:
-    // the diagonal tile's copy may be in flight.
-    auto compact = [&](int c0, uint32_t bits) {
-      const int cnt = __builtin_popcount(bits);
-      const int inc = wave_inclusive_scan(cnt, lane);
+    }
+    const bool diag_on = has_diag && __builtin_amdgcn_readfirstlane(static_cast<int>(mrow[qb])) != 0;
+    // ascending list of the active columns. Only fence-free barriers and LDS
+    // reads outside the compiler's tracking here: the diagonal tile's copy may
+    // be in flight.
+    int cnt;
+    {
+      const int nset = __builtin_popcount(bits);
+      const int inc = wave_inclusive_scan(nset, lane);
       if (lane == kWave - 1) wsum[wave] = inc;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       wg_barrier();
       const int w0 = static_cast<int>(lds_read_u32(wsum_lds));
-      const int total = w0 + static_cast<int>(lds_read_u32(wsum_lds + 4));
-      int pos = inc - cnt + (wave == 1 ? w0 : 0);
+      cnt = __builtin_amdgcn_readfirstlane(w0 + static_cast<int>(lds_read_u32(wsum_lds + 4)));
+      int pos = inc - nset + (wave == 1 ? w0 : 0);
       const int j0 = c0 + 16 * tid;
       while (bits) {
         const int e = __builtin_ctz(bits);
@@ -436,37 +473,39 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       wg_barrier();
-      return __builtin_amdgcn_readfirstlane(total);
+    }
+    // Circular sweep: the list is walked starting at a position proportional
+    // to this workgroup's place in its XCD's dispatch sequence (one phase per
+    // resident slot) and wraps around. Workgroups of one XCD start one after
+    // another and walk the same key range at about the same speed, so the
+    // ones resident together read neighbouring key blocks at any moment and
+    // the XCD's L2 holds a narrow window of K/V instead of the whole range.
+    const int rot = p.rotate ? static_cast<int>((static_cast<unsigned>((w / kXcds) % kSweepPhases) *
+                                                 static_cast<unsigned>(cnt)) / kSweepPhases)
+                             : 0;
+    auto entry = [&](int n) {                   // n-th tile of the sweep
+      const int i = rot + n < cnt ? rot + n : rot + n - cnt;
+      return __builtin_amdgcn_readfirstlane(static_cast<int>(lds_read_u16(list_lds + 2 * i)));
     };
-    const bool diag_on = __builtin_amdgcn_readfirstlane(static_cast<int>(mrow[qb])) != 0;
-    int c0 = 0;
-    int cnt = compact(0, load_bits(0));
-    bool issued = false;                        // list[0] of the current pass already in flight
+    bool issued = false;                        // the sweep's first tile already in flight
     if (diag_on) {
-      const int nxt = cnt > 0 ? __builtin_amdgcn_readfirstlane(static_cast<int>(lds_read_u16(list_lds))) : -1;
+      const int nxt = cnt > 0 ? entry(0) : -1;
       compute(std::true_type{}, qb, nxt, true);
       issued = cnt > 0;
-    } else {
+    } else if (has_diag) {
       wait_vmcnt(0);                            // the early copy of the diagonal tile is not used
       wg_barrier();
     }
-    while (true) {
-      if (cnt > 0) {
-        int kb = __builtin_amdgcn_readfirstlane(static_cast<int>(lds_read_u16(list_lds)));
-        bool first = !issued;
-        if (!issued) { issue_k(kb); issue_v(kb); }
-        for (int n = 0; n < cnt; ++n) {
-          const int next =
-              n + 1 < cnt ? __builtin_amdgcn_readfirstlane(static_cast<int>(lds_read_u16(list_lds + 2 * (n + 1)))) : -1;
-          compute(std::false_type{}, kb, next, first);
-          first = false;
-          kb = next;
-        }
+    if (cnt > 0) {
+      int kb = entry(0);
+      bool first = !issued;
+      if (!issued) { issue_k(kb); issue_v(kb); }
+      for (int n = 0; n < cnt; ++n) {
+        const int next = n + 1 < cnt ? entry(n + 1) : -1;
+        compute(std::false_type{}, kb, next, first);
+        first = false;
+        kb = next;
       }
-      c0 += kListCap;
-      if (c0 >= ncol) break;
-      cnt = compact(c0, load_bits(c0));         // no copy in flight here
-      issued = false;
     }
   } else {
     compute(std::true_type{}, qb, qb > 0 ? 0 : -1, true);
@@ -477,6 +516,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   const float ltot = pair_sum(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   const float lse2 = ltot > 0.f ? m + __log2f(ltot) : -INFINITY;
+  if constexpr (MODE == kSparse) {
+    if (qb >= p.chunk) {
+      // row spans several chunks: normalized fp32 partial + its log2-sum-exp
+      float* po = p.part_o + (static_cast<size_t>(w) * kBlock + q_local) * D;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<float4*>(po + 32 * mt + 8 * r4 + 4 * hl) =
+              make_float4(oacc[mt][4 * r4] * inv, oacc[mt][4 * r4 + 1] * inv, oacc[mt][4 * r4 + 2] * inv,
+                          oacc[mt][4 * r4 + 3] * inv);
+      if (hl == 0) p.part_l[static_cast<size_t>(w) * kBlock + q_local] = lse2;
+      return;
+    }
+  }
   if (t_ok) {
     const size_t obase = (static_cast<size_t>(bh) * p.S + t) * D;
 #pragma unroll
@@ -521,18 +575,129 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   }
 }
 
+// Merge the per-chunk partials of rows spanning several key chunks:
+// O = sum_c w_c O_c / sum_c w_c, w_c = 2^(L_c - max L), LSE = max L + log2(sum w).
+// One workgroup per such row; thread t handles query t/4, dims 32*(t%4) ...
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs p) {
+  constexpr int DPT = D / 4;                    // dims per thread
+  const int rows = p.nb - p.chunk;              // query blocks qb >= C per head
+  const int bh = blockIdx.x / rows;
+  const int qb = p.chunk + blockIdx.x % rows;
+  const int b = bh / p.Hq, h = bh % p.Hq;
+  const int g = h / p.group, hig = h % p.group;
+  const long long gi = static_cast<long long>(b) * p.Hkv + g;
+  const int q = threadIdx.x >> 2, d0 = (threadIdx.x & 3) * DPT;
+  const int nchunks = qb / p.chunk + 1;
+  auto item = [&](int c) {                      // work-item index of (row, chunk c)
+    long long before = 0;
+    for (int cc = 0; cc < c; ++cc) before += static_cast<long long>(p.group) * (p.nb - cc * p.chunk);
+    const int rows_c = p.nb - c * p.chunk;
+    return gi * p.items_per_group + before + static_cast<long long>(hig) * rows_c + (p.nb - 1 - qb);
+  };
+  float lmax = -INFINITY;
+  for (int c = 0; c < nchunks; ++c) lmax = fmaxf(lmax, p.part_l[item(c) * kBlock + q]);
+  float acc[DPT];
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) acc[i] = 0.f;
+  float wsum = 0.f;
+  if (lmax > -INFINITY) {
+    for (int c = 0; c < nchunks; ++c) {
+      const long long it = item(c);
+      const float wc = __builtin_amdgcn_exp2f(p.part_l[it * kBlock + q] - lmax);
+      wsum += wc;
+      const float4* src = reinterpret_cast<const float4*>(p.part_o + (it * kBlock + q) * D + d0);
+#pragma unroll
+      for (int i = 0; i < DPT / 4; ++i) {
+        const float4 v = src[i];
+        acc[4 * i] = fmaf(wc, v.x, acc[4 * i]);
+        acc[4 * i + 1] = fmaf(wc, v.y, acc[4 * i + 1]);
+        acc[4 * i + 2] = fmaf(wc, v.z, acc[4 * i + 2]);
+        acc[4 * i + 3] = fmaf(wc, v.w, acc[4 * i + 3]);
+      }
+    }
+  }
+  const int t = qb * kBlock + q;
+  if (t >= p.S) return;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const size_t obase = (static_cast<size_t>(bh) * p.S + t) * D + d0;
+  if (p.out_bf16) {
+    uint16_t* o = static_cast<uint16_t*>(p.out) + obase;
+#pragma unroll
+    for (int i = 0; i < DPT / 4; ++i)
+      *reinterpret_cast<uint2*>(o + 4 * i) = make_uint2(pack_bf16x2(acc[4 * i] * inv, acc[4 * i + 1] * inv),
+                                                        pack_bf16x2(acc[4 * i + 2] * inv, acc[4 * i + 3] * inv));
+  } else {
+    float* o = static_cast<float*>(p.out) + obase;
+#pragma unroll
+    for (int i = 0; i < DPT / 4; ++i)
+      *reinterpret_cast<float4*>(o + 4 * i) =
+          make_float4(acc[4 * i] * inv, acc[4 * i + 1] * inv, acc[4 * i + 2] * inv, acc[4 * i + 3] * inv);
+  }
+  if (p.lse != nullptr && d0 == 0)
+    p.lse[static_cast<size_t>(bh) * p.S + t] = wsum > 0.f ? (lmax + __log2f(wsum)) * kLn2 : -INFINITY;
+}
+
 template <int D>
 hipError_t launch_d(const AttnArgs& a, int mode, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(a.B) * a.Hq * a.nb), block(kThreads);
-  switch (mode) {
-    case kSparse: hipLaunchKernelGGL((attn_fwd_kernel<D, kSparse>), grid, block, 0, st, a); break;
-    case kDense: hipLaunchKernelGGL((attn_fwd_kernel<D, kDense>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((attn_fwd_kernel<D, kDenseGt>), grid, block, 0, st, a); break;
+  const dim3 block(kThreads);
+  if (mode == kSparse) {
+    const dim3 grid(static_cast<unsigned>(static_cast<long long>(a.B) * a.Hkv * a.items_per_group));
+    hipLaunchKernelGGL((attn_fwd_kernel<D, kSparse>), grid, block, 0, st, a);
+    if (a.nchunk > 1) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const dim3 cgrid(static_cast<unsigned>(a.B) * a.Hq * (a.nb - a.chunk));
+      hipLaunchKernelGGL((attn_combine_kernel<D>), cgrid, dim3(256), 0, st, a);
+    }
+    return hipGetLastError();
   }
+  const dim3 grid(static_cast<unsigned>(a.B) * a.Hq * a.nb);
+  if (mode == kDense) hipLaunchKernelGGL((attn_fwd_kernel<D, kDense>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((attn_fwd_kernel<D, kDenseGt>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
+
+// Key blocks per chunk of the block-sparse work items. Up to 1024 blocks
+// (64k tokens) a row is one item; longer rows are cut into chunks of 512
+// blocks, which the XCDs sweep together. SEER_ATTN_CHUNK overrides the chunk
+// (rounded to a multiple of 16, at most the on-chip list capacity).
+int sparse_chunk_blocks(int nb) {
+  static const int forced = [] {
+    const char* v = getenv("SEER_ATTN_CHUNK");
+    if (v == nullptr) return 0;
+    int x = atoi(v);
+    if (x < 16) x = 16;
+    if (x > kListCap) x = kListCap;
+    return x / 16 * 16;
+  }();
+  if (forced) return forced;
+  return nb > 1024 ? 512 : kListCap;
+}
+
+// Circular sweep of each row's tiles (on by default; SEER_ATTN_ROTATE=0 turns
+// it off). It changes only the order in which a row's tiles are accumulated.
+int sparse_rotate(int nchunk) {
+  (void)nchunk;
+  static const int forced = [] {
+    const char* v = getenv("SEER_ATTN_ROTATE");
+    return v == nullptr ? -1 : (atoi(v) != 0);
+  }();
+  return forced >= 0 ? forced : 1;
+}
+
+long long sparse_items_per_group(int nb, int group, int chunk) {
+  const long long nc = (nb + chunk - 1) / chunk;
+  return static_cast<long long>(group) * (nc * nb - static_cast<long long>(chunk) * nc * (nc - 1) / 2);
+}
+
+size_t sparse_workspace_bytes(int B, int Hkv, int group, int nb, int D, int chunk) {
+  if (nb <= chunk) return 0;
+  const size_t items = static_cast<size_t>(B) * Hkv * sparse_items_per_group(nb, group, chunk);
+  return items * kBlock * (static_cast<size_t>(D) + 1) * sizeof(float);
+}
 
 hipError_t launch_attn(const AttnArgs& a, int mode, hipStream_t st) {
   if (a.D == 64) return launch_d<64>(a, mode, st);

@@ -243,15 +243,16 @@ seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_
 
 // ---------------------------------------------------------------------------
 size_t seer_attn_workspace_size(const seer_shape* shape) {
-  (void)shape;
-  return 0;
+  bool empty = false;
+  if (check_shape(shape, &empty) != SEER_OK || empty) return 0;
+  return seer::sparse_workspace_bytes(shape->batch, shape->heads_kv, shape->heads_q / shape->heads_kv,
+                                      static_cast<int>(nblocks(shape)), shape->head_dim,
+                                      seer::sparse_chunk_blocks(static_cast<int>(nblocks(shape))));
 }
 
 seer_status seer_block_sparse_attn_fwd(const seer_shape* shape, const void* q, const void* k, const void* v,
                                        const uint8_t* block_mask, void* out, seer_dtype out_dtype, float* lse,
                                        void* workspace, size_t workspace_bytes, void* hip_stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   bool empty = false;
   seer_status st = check_shape(shape, &empty);
   if (st != SEER_OK) return st;
@@ -260,8 +261,25 @@ seer_status seer_block_sparse_attn_fwd(const seer_shape* shape, const void* q, c
   if (empty) return ok();
   if ((st = check_qkv(q, k, v)) != SEER_OK) return st;
   if ((st = check_out(out, out_dtype, lse)) != SEER_OK) return st;
-  if ((st = check_device()) != SEER_OK) return st;
   seer::AttnArgs a = attn_args(shape, q, k, v, block_mask ? 0 : 1);
+  if (block_mask != nullptr) {
+    a.chunk = seer::sparse_chunk_blocks(a.nb);
+    a.nchunk = (a.nb + a.chunk - 1) / a.chunk;
+    a.rotate = seer::sparse_rotate(a.nchunk);
+    a.items_per_group = seer::sparse_items_per_group(a.nb, a.group, a.chunk);
+    const long long items = static_cast<long long>(a.B) * a.Hkv * a.items_per_group;
+    if (items > 0x7fffffffLL)
+      return fail(SEER_ERR_SHAPE, "%lld block-sparse work items exceed the launch limit", items);
+    const size_t need = seer::sparse_workspace_bytes(a.B, a.Hkv, a.group, a.nb, a.D, a.chunk);
+    if (need > 0) {
+      if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
+        return fail(SEER_ERR_WORKSPACE, "workspace must be %zu bytes, 16-byte aligned (got %zu at %p)", need,
+                    workspace_bytes, workspace);
+      a.part_o = static_cast<float*>(workspace);
+      a.part_l = a.part_o + static_cast<size_t>(items) * 64 * a.D;
+    }
+  }
+  if ((st = check_device()) != SEER_OK) return st;
   a.mask = block_mask;
   a.out = out;
   a.lse = lse;

@@ -21,11 +21,24 @@ struct AttnArgs {
   long long ntri;      // nb(nb+1)/2
   float scale_log2;    // log2(e) / sqrt(D)
   int out_bf16;
-  int sched;           // workgroup order, see attn_fwd_kernel
+  int sched;           // workgroup order of the dense kernels, see attn_fwd_kernel
+  // block-sparse mode: key-chunked work items
+  int chunk;           // key blocks per chunk (C)
+  int nchunk;          // chunks per sequence = ceil(nb / C)
+  long long items_per_group;  // work items per (batch, KV group)
+  float* part_o;       // [items][64][D] fp32 normalized partial outputs (rows spanning > 1 chunk)
+  float* part_l;       // [items][64] fp32 partial log2-sum-exp
+  int rotate;          // block-sparse: walk each row's tiles in the XCD-phased circular order
 };
 
 // mode: 0 block-sparse (mask), 1 dense causal, 2 dense causal + ground-truth maxima
 hipError_t launch_attn(const AttnArgs& a, int mode, hipStream_t st);
+
+// Key-chunked block-sparse work: chunk size, item counts and workspace bytes.
+int sparse_chunk_blocks(int nb);
+int sparse_rotate(int nchunk);
+long long sparse_items_per_group(int nb, int group, int chunk);
+size_t sparse_workspace_bytes(int B, int Hkv, int group, int nb, int D, int chunk);
 
 struct GateArgs {
   const uint16_t* q;   // bf16 [B,Hq,S,D]

@@ -30,9 +30,9 @@ def _shape(b=1, hq=4, hkv=2, s=256, d=128, blk=64):
     return seer.make_shape(b, hq, hkv, s, d, blk)
 
 
-def _attn(shape, q=FAKE, k=FAKE, v=FAKE, mask=None, out=FAKE, dt=B.SEER_F32, lse=None):
+def _attn(shape, q=FAKE, k=FAKE, v=FAKE, mask=None, out=FAKE, dt=B.SEER_F32, lse=None, ws=None, ws_bytes=0):
     return _lib().seer_block_sparse_attn_fwd(ctypes.byref(shape) if shape is not None else None, q, k, v, mask,
-                                             out, dt, lse, None, 0, None)
+                                             out, dt, lse, ws, ws_bytes, None)
 
 
 def _gate(shape, dg=128, per_kv=0, mode=B.SEER_MASK_THRESHOLD, T=5e-4, k=4, per_head=None, scores=None,
@@ -89,6 +89,18 @@ def test_pointer_validation():
     assert _attn(_shape(), out=ctypes.c_void_p(0x10008), dt=B.SEER_F32) == B.SEER_ERR_INVALID_ARG
 
 
+def test_sparse_workspace_validation():
+    s = _shape(s=64 * 1200)                      # 1200 blocks: rows span up to three key chunks
+    need = _lib().seer_attn_workspace_size(ctypes.byref(s))
+    assert need > 0
+    assert _attn(s, mask=FAKE) == B.SEER_ERR_WORKSPACE
+    assert b"workspace" in _lib().seer_last_error()
+    assert _attn(s, mask=FAKE, ws=FAKE, ws_bytes=need - 1) == B.SEER_ERR_WORKSPACE
+    assert _attn(s, mask=FAKE, ws=ctypes.c_void_p(0x10008), ws_bytes=need) == B.SEER_ERR_WORKSPACE
+    # dense attention takes no workspace
+    assert _attn(s) != B.SEER_ERR_WORKSPACE
+
+
 def test_gate_validation():
     s = _shape()
     assert _gate(s, dg=100) == B.SEER_ERR_UNSUPPORTED
@@ -123,7 +135,16 @@ def test_workspace_sizes():
     s = _shape(b=2, hq=4, hkv=2, s=200, d=64)
     nb = 4
     align = lambda x: (x + 255) // 256 * 256
-    assert lib.seer_attn_workspace_size(ctypes.byref(s)) == 0
+    assert lib.seer_attn_workspace_size(ctypes.byref(s)) == 0   # every row within one key chunk
+    # rows of more than 1024 blocks are cut into key chunks of 512 blocks: chunk
+    # c holds the rows with query block >= 512 c (1100 + 588 + 76 rows per query
+    # head); each (row, chunk) item reserves a 64 x (D + 1) fp32 partial
+    s2 = _shape(b=2, hq=4, hkv=2, s=64 * 1100, d=128)
+    assert lib.seer_attn_workspace_size(ctypes.byref(s2)) == 2 * 4 * (1100 + 588 + 76) * 64 * 129 * 4
+    s3 = _shape(b=1, hq=2, hkv=1, s=64 * 1024, d=64)
+    assert lib.seer_attn_workspace_size(ctypes.byref(s3)) == 0
+    s4 = _shape(b=1, hq=2, hkv=1, s=64 * 1024 + 1, d=64)
+    assert lib.seer_attn_workspace_size(ctypes.byref(s4)) == 2 * (1025 + 513 + 1) * 64 * 65 * 4
     assert lib.seer_gt_workspace_size(ctypes.byref(s)) == align(2 * 4 * (nb * (nb + 1) // 2) * 64 * 4)
     want = (align(2 * 4 * nb * 64 * 4) + align(2 * 2 * nb * 192 * 4) + align(2 * 4 * nb * 32 * 4)
             + align(2 * 4 * nb * 32 * 4))
