@@ -43,7 +43,54 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-gib", type=float, default=0.0,
+                    help="run one plain device copy of this many GiB before the steps (counter calibration)")
     return ap.parse_args()
+
+
+COUNTERS = os.path.join(ROOT, "profiles", "attn_sparse_llama8b_s128k_90_counters.md")
+KERNEL_SRC = os.path.join(ROOT, "learned_block_sparse_attngate_amd", "csrc", "attn_kernels.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention call from the committed FETCH_SIZE / WRITE_SIZE
+    summary, or None if that summary is missing, is for another workload, or
+    was taken on a different version of the attention kernels' source."""
+    import hashlib
+    try:
+        text = open(COUNTERS).read()
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines() if line.startswith("- ") and ":" in line)
+    fields = {k[2:].strip(): v.strip().strip("`") for k, v in fields.items()}
+    if fields.get("workload") != workload or fields.get("attn_kernels.hip sha256") != src:
+        return None
+    try:
+        return int(fields["HBM bytes per call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def computed_peak():
+    """Dense bf16 MFMA peak from the agent's compute-unit count and maximum
+    engine clock as rocminfo reports them (4096 FLOP per clock per CU on
+    gfx950), or None if rocminfo is unavailable."""
+    import re
+    import subprocess
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+    except Exception:                                          # pragma: no cover
+        return None
+    for agent in txt.split("Agent ")[1:]:
+        if "gfx950" not in agent:
+            continue
+        cu = re.search(r"Compute Unit:\s+(\d+)", agent)
+        mhz = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", agent)
+        if cu and mhz:
+            cus, clk = int(cu.group(1)), int(mhz.group(1))
+            return {"cus": cus, "max_sclk_mhz": clk, "bf16_tflops": round(cus * 4096 * clk * 1e6 / 1e12, 1)}
+    return None
 
 
 def topk_for_sparsity(nb: int, s: float) -> int:
@@ -138,6 +185,16 @@ def main():
     def attn():
         seer.seer_block_sparse_attn_fwd(q, k, v, mask, out=out, workspace=attn_ws)
 
+    if args.copy_gib > 0:
+        # a plain copy of known size: the counters' reading for it calibrates FETCH_SIZE / WRITE_SIZE
+        n = int(args.copy_gib * (1 << 30)) // 4
+        src_buf = torch.ones(n, dtype=torch.float32, device=dev)
+        dst_buf = torch.empty_like(src_buf)
+        dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
+        print(f"[bench] copied {args.copy_gib} GiB device to device", file=sys.stderr, flush=True)
+
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         gate()
@@ -207,9 +264,11 @@ def main():
             "target_0.8/(1-s)": round(0.8 / (1.0 - s_real), 3),
             "ideal_1/(1-s)": round(1.0 / (1.0 - s_real), 3)},
         "dense_tflops": None if dense_ms is None else round(dense_flop / dense_ms / 1e9, 2),
-        "roofline": {"kernel": "attn_fwd_kernel<128, sparse>", "bound": "mfma", "achieved": round(achieved, 2),
+        "roofline": {"kernel": "seer_block_sparse_attn_fwd = attn_fwd_kernel<128, sparse> + attn_combine_kernel<128>",
+                     "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(args.workload)},
+        "peak_computed": computed_peak(),
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu:
