@@ -25,7 +25,11 @@ the design notes):
     row has <= k causal entries;
   * upper-triangle mask entries are ignored, any non-zero byte means "compute";
   * a query whose active key set is empty gets O = 0 and LSE = -inf;
-  * the ground truth is the raw max-pooled attention map (no renormalization).
+  * the ground truth is the raw max-pooled attention map (no renormalization);
+  * block RoPE: theta' = theta / block with theta the model's RoPE base, at
+    block positions, dims d and d + Dg/2 paired;
+  * distillation: gt rows are normalized to sum 1 before the divergence, and
+    the loss is the mean of the row divergences over all query-block rows.
 
 Inputs may be bfloat16 bit patterns (uint16 arrays, as produced by the
 seeded generators) or float arrays; they are widened exactly to float64.
@@ -92,16 +96,46 @@ def pool_k(k, block: int = BLOCK) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Block-level RoPE of the gate ([E] section 3.4, "Block-Level RoPE: Enabling
+# Length Generalization": the gate takes Q and K before the model's rotary
+# embedding and, after its own projections, applies a separate rotary
+# embedding whose base theta' is the model's base theta divided by the block
+# size, at block positions). The pages' formula is read literally: theta is
+# the base, so the angle of pair d at block position i is
+# i * (theta / block) ** (-2 d / Dg). Dims d and d + Dg/2 form a pair (the
+# rotate-half layout of the Llama models the pages evaluate).
+# --------------------------------------------------------------------------
+def block_rope(x, theta: float, block: int = BLOCK, positions=None) -> np.ndarray:
+    """Rotate gate vectors x [..., n, Dg] (Dg even) by their block positions.
+
+    positions defaults to 0 .. n-1 (the block index of each row); passing the
+    negated positions applies the inverse rotation.
+    """
+    x = as_f64(x)
+    n, dg = x.shape[-2], x.shape[-1]
+    half = dg // 2
+    pos = np.arange(n, dtype=np.float64) if positions is None else np.asarray(positions, dtype=np.float64)
+    inv_freq = (theta / block) ** (-2.0 * np.arange(half, dtype=np.float64) / dg)
+    ang = pos[:, None] * inv_freq[None, :]                   # [n, Dg/2]
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+# --------------------------------------------------------------------------
 # AttnGate: projections and the block-level score ([E] section 3.4,
 # "Linear transformation" and "Scoring via multiplication", the score
 # equation: softmax((W_q P_q(Q)) (W_k P_k(K))^T / sqrt(d)), row-wise)
 # --------------------------------------------------------------------------
-def gate_scores(q, k, w_q, w_k, block: int = BLOCK, wk_per_kv_head: bool = False) -> np.ndarray:
+def gate_scores(q, k, w_q, w_k, block: int = BLOCK, wk_per_kv_head: bool = False,
+                rope_theta=None) -> np.ndarray:
     """Gate score [B, Hq, nb, nb]; row i is a softmax over key blocks j <= i, 0 above.
 
     q: [B, Hq, S, D]; k: [B, Hkv, S, D]; w_q: [Hq, D, Dg];
     w_k: [Hq, 3D, Dg] (one per query head) or [Hkv, 3D, Dg] (wk_per_kv_head).
     The pooled query of head h meets the pooled key of its KV head g = h // G.
+    rope_theta: if given, the projected Q' and K' are rotated by block_rope
+    (the gate then expects pre-RoPE Q and K).
     """
     w_q = as_f64(w_q)
     w_k = as_f64(w_k)
@@ -122,12 +156,77 @@ def gate_scores(q, k, w_q, w_k, block: int = BLOCK, wk_per_kv_head: bool = False
             kp = kp_cache[g]                                  # [nb, 3D]
             qg = qp @ w_q[h]                                  # [nb, Dg]
             kg = kp @ (w_k[g] if wk_per_kv_head else w_k[h])  # [nb, Dg]
+            if rope_theta is not None:
+                qg = block_rope(qg, rope_theta, block)
+                kg = block_rope(kg, rope_theta, block)
             z = (qg @ kg.T) * scale
             z = np.where(causal, z, -np.inf)
             z = z - z.max(axis=1, keepdims=True)
             e = np.exp(z)
             out[b, h] = e / e.sum(axis=1, keepdims=True)
     return out
+
+
+# --------------------------------------------------------------------------
+# Self-distillation step of the gate ([E] section 3.4, "Training Procedure":
+# loss = D_KL(gt || score) with gt the 2D-maxpooled attention map and score
+# the gate's output, both read as distributions over the key blocks of a query
+# block). Readings: each causal row of gt is divided by its sum to give the
+# target distribution p (the map itself is not normalized); terms with
+# p_ij = 0 contribute 0; the loss is the mean of the row divergences over all
+# B * Hq * nb query-block rows. The gradient is the derivative of that loss
+# with respect to W_q and W_k.
+# --------------------------------------------------------------------------
+def gate_distill(q, k, w_q, w_k, gt, block: int = BLOCK, wk_per_kv_head: bool = False, rope_theta=None):
+    """Loss and weight gradients of one distillation step.
+
+    Same inputs as gate_scores plus gt [B, Hq, nb, nb] (raw max-pooled map,
+    causal rows with a positive sum). Returns (loss, grad_wq [Hq, D, Dg],
+    grad_wk shaped like w_k), float64.
+    """
+    w_q = as_f64(w_q)
+    w_k = as_f64(w_k)
+    gt = np.asarray(gt, dtype=np.float64)
+    B, Hq, S, D = np.shape(q)
+    Hkv = np.shape(k)[1]
+    G = Hq // Hkv
+    nb = n_blocks(S, block)
+    scale = 1.0 / np.sqrt(D)
+    causal = np.tril(np.ones((nb, nb), dtype=bool))
+    n_rows = B * Hq * nb
+    neg_pos = -np.arange(nb, dtype=np.float64)
+    loss = 0.0
+    grad_wq = np.zeros_like(w_q)
+    grad_wk = np.zeros_like(w_k)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            wk_idx = g if wk_per_kv_head else h
+            qp = pool_q(np.asarray(q)[b, h], block)          # [nb, D]
+            kp = pool_k(np.asarray(k)[b, g], block)          # [nb, 3D]
+            qg = qp @ w_q[h]
+            kg = kp @ w_k[wk_idx]
+            if rope_theta is not None:
+                qg = block_rope(qg, rope_theta, block)
+                kg = block_rope(kg, rope_theta, block)
+            z = np.where(causal, (qg @ kg.T) * scale, -np.inf)
+            zmax = z.max(axis=1, keepdims=True)
+            log_score = z - (zmax + np.log(np.exp(z - zmax).sum(axis=1, keepdims=True)))
+            score = np.exp(log_score)                        # 0 above the diagonal
+            target = np.where(causal, gt[b, h], 0.0)
+            p = target / target.sum(axis=1, keepdims=True)
+            pos = p > 0
+            loss += float(np.sum(p[pos] * (np.log(p[pos]) - log_score[pos])))
+            # d loss / d z = (score - p) / n_rows on causal entries (softmax + KL)
+            dz = np.where(causal, score - p, 0.0) / n_rows
+            dqg = (dz @ kg) * scale
+            dkg = (dz.T @ qg) * scale
+            if rope_theta is not None:                        # rotations are orthogonal: back-rotate
+                dqg = block_rope(dqg, rope_theta, block, positions=neg_pos)
+                dkg = block_rope(dkg, rope_theta, block, positions=neg_pos)
+            grad_wq[h] += qp.T @ dqg
+            grad_wk[wk_idx] += kp.T @ dkg
+    return loss / n_rows, grad_wq, grad_wk
 
 
 # --------------------------------------------------------------------------

@@ -409,6 +409,147 @@ def pin_topk_bruteforce(O):
                 assert m[0, h, i, j] == (1 if j in keep else 0)
 
 
+# ----------------------------------------------------------------------------
+# block-level RoPE of the gate
+# ----------------------------------------------------------------------------
+def pin_rope_hand_complex(O):
+    """theta = 6400, block 64 gives base 100, so the two pair frequencies of a
+    Dg = 4 vector are 100^0 = 1 and 100^(-1/2) = 0.1 (worked by hand). Pair d
+    is the complex number x[d] + i x[d + 2]; a rotation multiplies it by
+    exp(i * position * frequency)."""
+    import cmath
+    x = np.array([[1.0, 2.0, 3.0, 4.0]] * 4)
+    got = O.block_rope(x, 6400.0, 64)
+    freqs = [1.0, 0.1]
+    for pos in range(4):
+        for d in range(2):
+            z = complex(x[pos, d], x[pos, d + 2]) * cmath.exp(1j * pos * freqs[d])
+            assert abs(got[pos, d] - z.real) < 1e-14 and abs(got[pos, d + 2] - z.imag) < 1e-14
+
+
+def pin_rope_relative_and_orthogonal(O):
+    """Rotated dot products depend only on the position difference; rotations
+    keep norms; the negated positions undo the rotation."""
+    rng = np.random.default_rng(5)
+    qv = rng.standard_normal((1, 16))
+    kv = rng.standard_normal((1, 16))
+    for (i, j, shift) in [(3, 1, 5), (7, 7, 11), (2, 9, 40)]:
+        a = O.block_rope(qv, 5e5, 64, positions=[i])[0] @ O.block_rope(kv, 5e5, 64, positions=[j])[0]
+        b = O.block_rope(qv, 5e5, 64, positions=[i + shift])[0] @ O.block_rope(kv, 5e5, 64, positions=[j + shift])[0]
+        assert abs(a - b) < 1e-12
+    x = rng.standard_normal((6, 16))
+    r = O.block_rope(x, 1e4, 64)
+    assert np.abs(np.linalg.norm(r, axis=1) - np.linalg.norm(x, axis=1)).max() < 1e-12
+    back = O.block_rope(r, 1e4, 64, positions=-np.arange(6))
+    assert np.abs(back - x).max() < 1e-12
+    assert np.abs(r[0] - x[0]).max() == 0.0              # position 0: no rotation
+
+
+def pin_gate_rope_complex_bruteforce(O):
+    """Gate scores with block RoPE equal a brute force written with complex
+    numbers: logit(i, j) = Re(sum_d zq_d conj(zk_d) e^(i (i - j) f_d)) / sqrt(D),
+    zq = Q'_i pairs, zk = K'_j pairs, f_d = (theta/64)^(-2d/Dg); pooling by torch."""
+    import cmath
+    shape = Shape(1, 2, 1, 64 * 6 - 9, 8)
+    q, k, _ = _qkv(shape, 26)
+    rng = np.random.default_rng(6)
+    wq = rng.standard_normal((2, 8, 8)) / 2.0
+    wk = rng.standard_normal((2, 24, 8)) / 2.0
+    theta = 5e5
+    sc = O.gate_scores(q, k, wq, wk, rope_theta=theta)
+    nb, dg = 6, 8
+    f = [(theta / 64.0) ** (-2.0 * d / dg) for d in range(dg // 2)]
+    pad = 64 * nb - shape.seq_len
+    for h in range(2):
+        tq = torch.from_numpy(q[0, h])
+        tk = torch.from_numpy(k[0, 0])
+        # ragged last block: mean / max / min over the tokens it has
+        qp = np.stack([tq[64 * i:64 * i + 64].mean(0).numpy() for i in range(nb)])
+        kp = np.stack([np.concatenate([tk[64 * i:64 * i + 64].max(0).values.numpy(),
+                                       tk[64 * i:64 * i + 64].min(0).values.numpy(),
+                                       tk[64 * i:64 * i + 64].mean(0).numpy()]) for i in range(nb)])
+        assert pad > 0
+        qg = qp @ wq[h]
+        kg = kp @ wk[h]
+        for i in range(nb):
+            logits = []
+            for j in range(i + 1):
+                acc = 0.0
+                for d in range(dg // 2):
+                    zq = complex(qg[i, d], qg[i, d + dg // 2])
+                    zk = complex(kg[j, d], kg[j, d + dg // 2])
+                    acc += (zq * zk.conjugate() * cmath.exp(1j * (i - j) * f[d])).real
+                logits.append(acc / math.sqrt(8))
+            mx = max(logits)
+            e = [math.exp(z - mx) for z in logits]
+            for j in range(nb):
+                want = e[j] / sum(e) if j <= i else 0.0
+                assert abs(sc[0, h, i, j] - want) < 1e-13
+
+
+# ----------------------------------------------------------------------------
+# distillation step (KL of the row-normalized ground truth and the gate score)
+# ----------------------------------------------------------------------------
+def _distill_case(seed, per_kv):
+    shape = Shape(1, 4, 2, 64 * 5 - 7, 8)
+    q, k, _ = _qkv(shape, seed)
+    rng = np.random.default_rng(seed)
+    wq = rng.standard_normal((4, 8, 4)) / 2.0
+    wk = rng.standard_normal((2 if per_kv else 4, 24, 4)) / 2.0
+    nb = 5
+    gt = np.tril(rng.random((1, 4, nb, nb)) + 0.01)
+    gt[0, 1, 3, :2] = 0.0                       # zero entries contribute nothing
+    return q, k, wq, wk, gt
+
+
+def pin_distill_finite_differences(O):
+    """Analytic gradients equal central differences of the loss (fp64, with and
+    without block RoPE, W_k per query head and per KV head)."""
+    for seed, per_kv, theta in [(31, False, None), (32, True, 5e5), (33, False, 1e4)]:
+        q, k, wq, wk, gt = _distill_case(seed, per_kv)
+        loss, gq, gk = O.gate_distill(q, k, wq, wk, gt, wk_per_kv_head=per_kv, rope_theta=theta)
+        rng = np.random.default_rng(seed + 100)
+        eps = 1e-6
+        for w, g, which in [(wq, gq, "q"), (wk, gk, "k")]:
+            for _ in range(6):
+                idx = tuple(int(rng.integers(n)) for n in w.shape)
+                wp, wm = w.copy(), w.copy()
+                wp[idx] += eps
+                wm[idx] -= eps
+                args_p = (wp, wk) if which == "q" else (wq, wp)
+                args_m = (wm, wk) if which == "q" else (wq, wm)
+                lp = O.gate_distill(q, k, *args_p, gt, wk_per_kv_head=per_kv, rope_theta=theta)[0]
+                lm = O.gate_distill(q, k, *args_m, gt, wk_per_kv_head=per_kv, rope_theta=theta)[0]
+                fd = (lp - lm) / (2 * eps)
+                assert abs(fd - g[idx]) <= 1e-7 + 1e-5 * abs(fd), (which, idx, fd, g[idx])
+
+
+def pin_distill_loss_definition(O):
+    """The loss is the mean over query-block rows of sum_j p log(p / score),
+    with p the gt row divided by its sum (pure-Python brute force on the
+    oracle's own, separately pinned, gate scores); it is 0 with zero gradients
+    when gt is the gate's own score, and it ignores a positive scale per row."""
+    q, k, wq, wk, gt = _distill_case(34, False)
+    loss, _, _ = O.gate_distill(q, k, wq, wk, gt, rope_theta=5e5)
+    sc = O.gate_scores(q, k, wq, wk, rope_theta=5e5)
+    total, rows = 0.0, 0
+    for h in range(4):
+        for i in range(5):
+            row = [gt[0, h, i, j] for j in range(i + 1)]
+            tot = sum(row)
+            for j in range(i + 1):
+                pj = row[j] / tot
+                if pj > 0:
+                    total += pj * math.log(pj / sc[0, h, i, j])
+            rows += 1
+    assert abs(loss - total / rows) < 1e-13
+    assert loss > 0
+    scaled = gt * np.random.default_rng(7).uniform(0.5, 3.0, size=(1, 4, 5, 1))
+    assert abs(O.gate_distill(q, k, wq, wk, scaled, rope_theta=5e5)[0] - loss) < 1e-13
+    self_loss, gq, gk = O.gate_distill(q, k, wq, wk, sc, rope_theta=5e5)
+    assert abs(self_loss) < 1e-14 and np.abs(gq).max() < 1e-14 and np.abs(gk).max() < 1e-14
+
+
 ATTENTION_PINS = [pin_dense_matches_torch_sdpa, pin_probabilities_via_one_hot_v,
                   pin_constant_v_and_empty_rows, pin_q_zero_closed_form, pin_single_block_row,
                   pin_gqa_equals_mha, pin_bruteforce_python_loops]
@@ -418,4 +559,6 @@ GATE_PINS = [pin_gate_hand_example, pin_gate_rows_sum_to_one, pin_gate_wq_zero_c
              pin_pool_matches_torch, pin_pool_k_constant_blocks, pin_gate_gqa_equals_mha]
 MASK_PINS = [pin_threshold_strict, pin_threshold_nesting, pin_topk_counts, pin_topk_ties_low_index,
              pin_topk_bruteforce]
-ALL_PINS = ATTENTION_PINS + GT_PINS + GATE_PINS + MASK_PINS
+ROPE_PINS = [pin_rope_hand_complex, pin_rope_relative_and_orthogonal, pin_gate_rope_complex_bruteforce]
+DISTILL_PINS = [pin_distill_finite_differences, pin_distill_loss_definition]
+ALL_PINS = ATTENTION_PINS + GT_PINS + GATE_PINS + MASK_PINS + ROPE_PINS + DISTILL_PINS

@@ -53,6 +53,23 @@ MUTATIONS = [
     ("gt_scale_dropped", "scale = 1.0 / np.sqrt(D)", "scale = 1.0", 2),
     ("gt_gqa_head_map", "g = h // G\n        t0, t1", "g = h % Hkv\n        t0, t1", 1),
     ("gt_upper_not_zero", "for j in range(i + 1):\n            a, bb", "for j in range(nb):\n            a, bb", 0),
+    ("rope_sign_flipped", "x2 * c + x1 * s", "x2 * c - x1 * s", 0),
+    ("rope_interleaved_pairs", "x1, x2 = x[..., :half], x[..., half:]", "x1, x2 = x[..., 0::2], x[..., 1::2]", 0),
+    ("rope_base_not_divided", "inv_freq = (theta / block) **", "inv_freq = theta **", 0),
+    ("rope_frequency_exponent", "** (-2.0 * np.arange(half, dtype=np.float64) / dg)",
+     "** (-1.0 * np.arange(half, dtype=np.float64) / dg)", 0),
+    ("gate_rope_key_not_rotated", "                kg = block_rope(kg, rope_theta, block)\n            z = (qg",
+     "                kg = kg\n            z = (qg", 0),
+    ("distill_gt_not_normalized", "p = target / target.sum(axis=1, keepdims=True)", "p = target", 0),
+    ("distill_gradient_sign", "dz = np.where(causal, score - p, 0.0) / n_rows",
+     "dz = np.where(causal, p - score, 0.0) / n_rows", 0),
+    ("distill_grad_scale_dropped", "dqg = (dz @ kg) * scale", "dqg = (dz @ kg)", 0),
+    ("distill_key_grad_untransposed", "dkg = (dz.T @ qg) * scale", "dkg = (dz @ qg) * scale", 0),
+    ("distill_no_back_rotation", "dqg = block_rope(dqg, rope_theta, block, positions=neg_pos)",
+     "dqg = block_rope(dqg, rope_theta, block)", 0),
+    ("distill_sum_not_mean", "return loss / n_rows, grad_wq, grad_wk", "return loss, grad_wq, grad_wk", 0),
+    ("distill_kl_reversed", "loss += float(np.sum(p[pos] * (np.log(p[pos]) - log_score[pos])))",
+     "loss += float(np.sum(score[pos] * (log_score[pos] - np.log(p[pos]))))", 0),
 ]
 
 
