@@ -29,7 +29,8 @@ the design notes):
   * block RoPE: theta' = theta / block with theta the model's RoPE base, at
     block positions, dims d and d + Dg/2 paired;
   * distillation: gt rows are normalized to sum 1 before the divergence, and
-    the loss is the mean of the row divergences over all query-block rows.
+    the loss is the mean of the row divergences over all query-block rows; a
+    row whose gt sums to 0 has no target and contributes nothing.
 
 Inputs may be bfloat16 bit patterns (uint16 arrays, as produced by the
 seeded generators) or float arrays; they are widened exactly to float64.
@@ -180,9 +181,8 @@ def gate_scores(q, k, w_q, w_k, block: int = BLOCK, wk_per_kv_head: bool = False
 def gate_distill(q, k, w_q, w_k, gt, block: int = BLOCK, wk_per_kv_head: bool = False, rope_theta=None):
     """Loss and weight gradients of one distillation step.
 
-    Same inputs as gate_scores plus gt [B, Hq, nb, nb] (raw max-pooled map,
-    causal rows with a positive sum). Returns (loss, grad_wq [Hq, D, Dg],
-    grad_wk shaped like w_k), float64.
+    Same inputs as gate_scores plus gt [B, Hq, nb, nb] (raw max-pooled map).
+    Returns (loss, grad_wq [Hq, D, Dg], grad_wk shaped like w_k), float64.
     """
     w_q = as_f64(w_q)
     w_k = as_f64(w_k)
@@ -214,11 +214,13 @@ def gate_distill(q, k, w_q, w_k, gt, block: int = BLOCK, wk_per_kv_head: bool = 
             log_score = z - (zmax + np.log(np.exp(z - zmax).sum(axis=1, keepdims=True)))
             score = np.exp(log_score)                        # 0 above the diagonal
             target = np.where(causal, gt[b, h], 0.0)
-            p = target / target.sum(axis=1, keepdims=True)
+            tsum = target.sum(axis=1, keepdims=True)
+            valid = tsum > 0                                  # rows without target mass contribute nothing
+            p = np.where(valid, target / np.where(valid, tsum, 1.0), 0.0)
             pos = p > 0
             loss += float(np.sum(p[pos] * (np.log(p[pos]) - log_score[pos])))
-            # d loss / d z = (score - p) / n_rows on causal entries (softmax + KL)
-            dz = np.where(causal, score - p, 0.0) / n_rows
+            # d loss / d z = (score - p) / n_rows on causal entries of valid rows (softmax + KL)
+            dz = np.where(causal & valid, score - p, 0.0) / n_rows
             dqg = (dz @ kg) * scale
             dkg = (dz.T @ qg) * scale
             if rope_theta is not None:                        # rotations are orthogonal: back-rotate

@@ -548,6 +548,16 @@ def pin_distill_loss_definition(O):
     assert abs(O.gate_distill(q, k, wq, wk, scaled, rope_theta=5e5)[0] - loss) < 1e-13
     self_loss, gq, gk = O.gate_distill(q, k, wq, wk, sc, rope_theta=5e5)
     assert abs(self_loss) < 1e-14 and np.abs(gq).max() < 1e-14 and np.abs(gk).max() < 1e-14
+    # a row with no ground-truth mass has no target: it adds nothing to the loss
+    # (which stays a mean over all rows) and nothing to the gradient
+    gz = gt.copy()
+    gz[0, 2, 3, :] = 0.0
+    lz, gqz, _ = O.gate_distill(q, k, wq, wk, gz, rope_theta=5e5)
+    row = [gt[0, 2, 3, j] / sum(gt[0, 2, 3, :4]) for j in range(4)]
+    drop = sum(pj * math.log(pj / sc[0, 2, 3, j]) for j, pj in enumerate(row) if pj > 0)
+    assert abs(lz - (loss - drop / rows)) < 1e-13
+    lo, gqo, gko = O.gate_distill(q, k, wq, wk, np.zeros_like(gt), rope_theta=5e5)
+    assert lo == 0.0 and np.abs(gqo).max() == 0.0 and np.abs(gko).max() == 0.0
 
 
 ATTENTION_PINS = [pin_dense_matches_torch_sdpa, pin_probabilities_via_one_hot_v,

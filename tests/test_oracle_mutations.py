@@ -60,9 +60,12 @@ MUTATIONS = [
      "** (-1.0 * np.arange(half, dtype=np.float64) / dg)", 0),
     ("gate_rope_key_not_rotated", "                kg = block_rope(kg, rope_theta, block)\n            z = (qg",
      "                kg = kg\n            z = (qg", 0),
-    ("distill_gt_not_normalized", "p = target / target.sum(axis=1, keepdims=True)", "p = target", 0),
-    ("distill_gradient_sign", "dz = np.where(causal, score - p, 0.0) / n_rows",
-     "dz = np.where(causal, p - score, 0.0) / n_rows", 0),
+    ("distill_gt_not_normalized", "p = np.where(valid, target / np.where(valid, tsum, 1.0), 0.0)",
+     "p = np.where(valid, target, 0.0)", 0),
+    ("distill_gradient_sign", "dz = np.where(causal & valid, score - p, 0.0) / n_rows",
+     "dz = np.where(causal & valid, p - score, 0.0) / n_rows", 0),
+    ("distill_empty_row_gradient", "dz = np.where(causal & valid, score - p, 0.0) / n_rows",
+     "dz = np.where(causal, score - p, 0.0) / n_rows", 0),
     ("distill_grad_scale_dropped", "dqg = (dz @ kg) * scale", "dqg = (dz @ kg)", 0),
     ("distill_key_grad_untransposed", "dkg = (dz.T @ qg) * scale", "dkg = (dz @ qg) * scale", 0),
     ("distill_no_back_rotation", "dqg = block_rope(dqg, rope_theta, block, positions=neg_pos)",
