@@ -1,7 +1,8 @@
 """Benchmark of the SeerAttention hot path on one MI355X.
 
 One step = the whole prefill hot path on one batch of synthetic input:
-  seer_gate_fwd (Q/K pooling, projections, causal block softmax, top-k mask)
+  seer_gate_fwd (Q/K pooling, projections, block-level RoPE with the model's
+  base 500000, causal block softmax, top-k mask)
   + seer_block_sparse_attn_fwd with the workload's block mask.
 The default workload is the Llama-3.1-8B-shaped layer at 128k tokens with a
 seeded 90%-sparse causal block mask (diagonal + sink + 4 vertical stripes +
@@ -43,6 +44,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip timing the ground-truth kernel and the gate's distillation step")
+    ap.add_argument("--rope-theta", type=float, default=5e5,
+                    help="RoPE base for the gate's block-level RoPE (0: none); Llama-3.1 uses 500000")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="run one plain device copy of this many GiB before the steps (counter calibration)")
     return ap.parse_args()
@@ -177,7 +182,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def gate():
-        seer.seer_gate_fwd(q, k, wq, wk, mode="topk", topk=k_gate, scores=gate_scores, block_mask=gate_mask,
+        seer.seer_gate_fwd(q, k, wq, wk, mode="topk", topk=k_gate, rope_theta=args.rope_theta,
+                           scores=gate_scores, block_mask=gate_mask,
                            workspace=gate_ws)
 
     attn_ws = torch.empty(max(seer.attn_workspace_bytes(B, Hq, Hkv, S, D), 16), dtype=torch.uint8, device=dev)
@@ -235,6 +241,41 @@ def main():
         print(f"[bench] dense {dense_ms:.3f} ms ({dense_flop / dense_ms / 1e9:.1f} TFLOP/s)", file=sys.stderr,
               flush=True)
 
+    gt_ms = distill_ms = None
+    if not args.no_train:
+        # training path: dense attention with the 2D-maxpooled map, then one
+        # distillation step of the gate on that map (not part of `value`)
+        print("[bench] ground-truth kernel and distillation step", file=sys.stderr, flush=True)
+        gt = torch.empty((B, Hq, nb, nb), dtype=torch.float32, device=dev)
+        gt_ws = torch.empty(seer.gt_workspace_bytes(B, Hq, Hkv, S, D), dtype=torch.uint8, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        seer.seer_attn_maxpool_gt(q, k, v, out=out, gt=gt, workspace=gt_ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gt_ms = e0.elapsed_time(e1)
+        del gt_ws
+        d_ws = torch.empty(seer.distill_workspace_bytes(B, Hq, Hkv, S, D, 128), dtype=torch.uint8, device=dev)
+        d_out = (torch.empty(1, dtype=torch.float32, device=dev), torch.empty_like(wq), torch.empty_like(wk))
+
+        def distill():
+            seer.seer_gate_distill_bwd(q, k, wq, wk, gt, rope_theta=args.rope_theta, loss=d_out[0],
+                                       grad_wq=d_out[1], grad_wk=d_out[2], workspace=d_ws)
+        distill()
+        torch.cuda.synchronize()
+        dts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            distill()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            dts.append(e0.elapsed_time(e1))
+        distill_ms = float(np.median(dts))
+        print(f"[bench] dense + ground truth {gt_ms:.3f} ms, distillation step {distill_ms:.3f} ms "
+              f"(loss {float(d_out[0].item()):.5f})", file=sys.stderr, flush=True)
+        del d_ws, gt
+
     ms_step = float(np.mean(step_ms))
     attn_avg = float(np.mean(attn_ms))
     gate_avg = float(np.mean(gate_ms))
@@ -255,9 +296,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "heads_q": Hq, "heads_kv": Hkv, "seq_len": S,
                    "head_dim": D, "block": 64, "mask": "seeded diag+sink+4 stripes+random, per-head s in [0.8,0.97]",
-                   "realized_sparsity": round(s_real, 5), "executed_tiles": tiles, "gate_topk": k_gate},
+                   "realized_sparsity": round(s_real, 5), "executed_tiles": tiles, "gate_topk": k_gate,
+                   "gate_rope_theta": args.rope_theta},
         "breakdown_ms": {"gate": round(gate_avg, 4), "sparse_attention": round(attn_avg, 4),
-                         "dense_attention": None if dense_ms is None else round(dense_ms, 4)},
+                         "dense_attention": None if dense_ms is None else round(dense_ms, 4),
+                         "dense_attention_with_gt_map": None if gt_ms is None else round(gt_ms, 4),
+                         "gate_distillation_step": None if distill_ms is None else round(distill_ms, 4)},
         "speedup_vs_dense": None if dense_ms is None else {
             "kernel": round(dense_ms / attn_avg, 3),
             "with_gate": round(dense_ms / ms_step, 3),

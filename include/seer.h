@@ -79,6 +79,12 @@ typedef enum seer_dtype { SEER_F32 = 0, SEER_BF16 = 1 } seer_dtype;
  *   Q'[b,h,i]  = Qp[b,h,i] . w_q[h]                                    (D -> gate_dim)
  *   K'[b,h,j]  = Kp[b,g(h),j] . w_k[h]   (w_k per query head), or
  *               Kp[b,g(h),j] . w_k[g(h)] (wk_per_kv_head != 0)        (3D -> gate_dim)
+ *   with rope_theta > 0 (block-level RoPE, [E] section 3.4 "Block-Level
+ *   RoPE"; q and k are then the model's Q and K BEFORE its own rotary
+ *   embedding): Q'_i and K'_j are rotated at their block positions i and j,
+ *   dims d and d + gate_dim/2 forming a pair, by the angle
+ *   pos * (rope_theta / 64)^(-2d / gate_dim)  (the model's RoPE base divided
+ *   by the block size); rope_theta = 0 leaves them unrotated
  *   score[b,h,i,j] = softmax over j <= i of Q'_i . K'_j / sqrt(D); 0 for j > i
  *   mask[b,h,i,j]  = 1 if the block is selected, else 0 (also 0 for j > i)
  *     threshold: score > threshold (strict)
@@ -90,6 +96,7 @@ typedef enum seer_dtype { SEER_F32 = 0, SEER_BF16 = 1 } seer_dtype;
  * k            device bf16 [B,Hkv,S,D]
  * w_q          device fp32 [Hq,D,gate_dim]
  * w_k          device fp32 [Hq,3D,gate_dim] or [Hkv,3D,gate_dim]
+ * rope_theta   0, or the base of the model's RoPE (> 0, finite), e.g. 500000
  * threshold    used in SEER_MASK_THRESHOLD mode; must be finite
  * topk_k       uniform k for SEER_MASK_TOPK (>= 1) when topk_per_head is NULL
  * topk_per_head HOST array of Hq values of k (>= 1), or NULL; read during the call
@@ -100,10 +107,38 @@ typedef enum seer_dtype { SEER_F32 = 0, SEER_BF16 = 1 } seer_dtype;
 size_t seer_gate_workspace_size(const seer_shape* shape, int32_t gate_dim, int32_t wk_per_kv_head,
                                 int32_t want_scores);
 seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_per_kv_head,
-                          const void* q, const void* k, const float* w_q, const float* w_k,
+                          float rope_theta, const void* q, const void* k, const float* w_q, const float* w_k,
                           seer_mask_mode mode, float threshold, int32_t topk_k,
                           const int32_t* topk_per_head, float* scores, uint8_t* block_mask,
                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * One self-distillation step of the gate ([E] section 3.4, "Training
+ * Procedure": loss = D_KL(gt || score), gt the 2D-maxpooled attention map of
+ * seer_attn_maxpool_gt and score the gate's output, both read as
+ * distributions over the key blocks of a query block).
+ *
+ *   score      = the gate score of seer_gate_fwd (same q, k, weights, rope_theta)
+ *   p[b,h,i,:] = gt[b,h,i,j] / sum_{j<=i} gt[b,h,i,j] over the causal entries
+ *   loss       = (1 / (B Hq nb)) * sum_{b,h,i} sum_{j<=i, p>0} p log(p / score)
+ *   grad_wq    = d loss / d w_q,  grad_wk = d loss / d w_k   (overwritten)
+ *   A row of gt whose causal entries sum to 0 adds 0 to the loss and to the
+ *   gradients. Everything is computed in fp32; the loss is summed in fp64.
+ *
+ * gt           device fp32 [B,Hq,nb,nb] (entries above the diagonal ignored)
+ * loss         device fp32 [1] output
+ * grad_wq      device fp32 [Hq,D,gate_dim] output
+ * grad_wk      device fp32, shaped like w_k, output
+ * workspace    device scratch of at least seer_gate_distill_workspace_size()
+ *              bytes, 256-byte aligned
+ * Other arguments as for seer_gate_fwd.
+ * ---------------------------------------------------------------------- */
+size_t seer_gate_distill_workspace_size(const seer_shape* shape, int32_t gate_dim, int32_t wk_per_kv_head);
+seer_status seer_gate_distill_bwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_per_kv_head,
+                                  float rope_theta, const void* q, const void* k, const float* w_q,
+                                  const float* w_k, const float* gt, float* loss, float* grad_wq,
+                                  float* grad_wk, void* workspace, size_t workspace_bytes,
+                                  void* hip_stream);
 
 /* ------------------------------------------------------------------------
  * Causal GQA block-sparse attention forward ([E] section 3.4, "Block-sparse

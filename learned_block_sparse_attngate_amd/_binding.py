@@ -32,6 +32,7 @@ BLOCK = 64
 # Every symbol include/seer.h declares (checked by the CPU tests).
 EXPORTED = (
     "seer_gate_workspace_size", "seer_gate_fwd",
+    "seer_gate_distill_workspace_size", "seer_gate_distill_bwd",
     "seer_attn_workspace_size", "seer_block_sparse_attn_fwd",
     "seer_gt_workspace_size", "seer_attn_maxpool_gt",
     "seer_status_string", "seer_last_error", "seer_version",
@@ -64,9 +65,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     shp = ctypes.POINTER(SeerShape)
     lib.seer_gate_workspace_size.argtypes = [shp, i32, i32, i32]
     lib.seer_gate_workspace_size.restype = sz
-    lib.seer_gate_fwd.argtypes = [shp, i32, i32, vp, vp, vp, vp, ctypes.c_int, f32, i32,
+    lib.seer_gate_fwd.argtypes = [shp, i32, i32, f32, vp, vp, vp, vp, ctypes.c_int, f32, i32,
                                   ctypes.POINTER(i32), vp, vp, vp, sz, vp]
     lib.seer_gate_fwd.restype = ctypes.c_int
+    lib.seer_gate_distill_workspace_size.argtypes = [shp, i32, i32]
+    lib.seer_gate_distill_workspace_size.restype = sz
+    lib.seer_gate_distill_bwd.argtypes = [shp, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.seer_gate_distill_bwd.restype = ctypes.c_int
     lib.seer_attn_workspace_size.argtypes = [shp]
     lib.seer_attn_workspace_size.restype = sz
     lib.seer_block_sparse_attn_fwd.argtypes = [shp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, sz, vp]
@@ -134,9 +139,13 @@ def nblocks(seq_len: int) -> int:
 def seer_gate_fwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor, *,
                   mode: str = "threshold", threshold: float = 5e-4,
                   topk: Union[int, Sequence[int], None] = None, wk_per_kv_head: bool = False,
+                  rope_theta: float = 0.0,
                   want_scores: bool = True, scores: Optional[torch.Tensor] = None,
                   block_mask: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
-    """AttnGate scores and block mask. Returns (block_mask uint8, scores fp32 or None)."""
+    """AttnGate scores and block mask. Returns (block_mask uint8, scores fp32 or None).
+
+    rope_theta > 0 turns on the gate's block-level RoPE (q and k are then the
+    model's pre-RoPE Q and K; rope_theta is the model's RoPE base)."""
     lib = load_library()
     _need(q, "q", torch.bfloat16)
     _need(k, "k", torch.bfloat16)
@@ -171,7 +180,8 @@ def seer_gate_fwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torc
     nbytes = lib.seer_gate_workspace_size(ctypes.byref(shape), Dg, int(wk_per_kv_head), int(scores is not None))
     workspace = _workspace(nbytes, dev, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.seer_gate_fwd(ctypes.byref(shape), Dg, int(wk_per_kv_head), _ptr(q), _ptr(k), _ptr(w_q), _ptr(w_k),
+    _check(lib.seer_gate_fwd(ctypes.byref(shape), Dg, int(wk_per_kv_head), float(rope_theta),
+                             _ptr(q), _ptr(k), _ptr(w_q), _ptr(w_k),
                              m, float(threshold), int(k_uniform), per_head, _ptr(scores), _ptr(block_mask),
                              _ptr(workspace), ws_bytes, _stream(dev)))
     return block_mask, scores
@@ -240,6 +250,46 @@ def seer_attn_maxpool_gt(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     _check(lib.seer_attn_maxpool_gt(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(out), dt, _ptr(lse),
                                     _ptr(gt), _ptr(workspace), ws_bytes, _stream(dev)))
     return out, lse, gt
+
+
+def seer_gate_distill_bwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                          gt: torch.Tensor, *, wk_per_kv_head: bool = False, rope_theta: float = 0.0,
+                          loss: Optional[torch.Tensor] = None, grad_wq: Optional[torch.Tensor] = None,
+                          grad_wk: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """One distillation step of the gate: KL(row-normalized gt || score) averaged
+    over query-block rows, and its gradients. Returns (loss [1], grad_wq, grad_wk)."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16)
+    _need(w_q, "w_q", torch.float32)
+    _need(w_k, "w_k", torch.float32)
+    _need(gt, "gt", torch.float32)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    Dg = w_q.shape[-1]
+    nb = nblocks(S)
+    if tuple(gt.shape) != (B, Hq, nb, nb):
+        raise ValueError(f"gt must be {(B, Hq, nb, nb)}, got {tuple(gt.shape)}")
+    shape = make_shape(B, Hq, Hkv, S, D)
+    dev = q.device
+    if loss is None:
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+    if grad_wq is None:
+        grad_wq = torch.empty_like(w_q)
+    if grad_wk is None:
+        grad_wk = torch.empty_like(w_k)
+    nbytes = lib.seer_gate_distill_workspace_size(ctypes.byref(shape), Dg, int(wk_per_kv_head))
+    workspace = _workspace(nbytes, dev, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.seer_gate_distill_bwd(ctypes.byref(shape), Dg, int(wk_per_kv_head), float(rope_theta), _ptr(q),
+                                     _ptr(k), _ptr(w_q), _ptr(w_k), _ptr(gt), _ptr(loss), _ptr(grad_wq),
+                                     _ptr(grad_wk), _ptr(workspace), ws_bytes, _stream(dev)))
+    return loss, grad_wq, grad_wk
+
+
+def distill_workspace_bytes(batch, heads_q, heads_kv, seq_len, head_dim, gate_dim, wk_per_kv_head=False) -> int:
+    shape = make_shape(batch, heads_q, heads_kv, seq_len, head_dim)
+    return load_library().seer_gate_distill_workspace_size(ctypes.byref(shape), gate_dim, int(wk_per_kv_head))
 
 
 def attn_workspace_bytes(batch, heads_q, heads_kv, seq_len, head_dim) -> int:

@@ -100,33 +100,32 @@ __global__ __launch_bounds__(kPoolThreads) void gate_pool_kernel(GateArgs a) {
 constexpr int kGT = 256;
 constexpr int kBM = 64, kBN = 64, kBK = 16;
 
-template <bool B_T>
-__device__ __forceinline__ void gemm_tile(const float* __restrict__ A, int lda, const float* __restrict__ B,
-                                          int ldb, float* __restrict__ C, int ldc, int M, int N, int K,
-                                          int m0, int n0, float alpha, bool causal_only) {
+// acc += A(m0 .. m0+63, k) * Bm(k, n0 .. n0+63) over k in [k0, k1), where
+// A(m, k) = A[m*lda + k] (A_T = false) or A[k*lda + m] (A_T = true).
+template <bool A_T, bool B_T>
+__device__ __forceinline__ void gemm_accum(float (&acc)[4][4], const float* __restrict__ A, int lda,
+                                           const float* __restrict__ B, int ldb, int M, int N, int k0, int k1,
+                                           int m0, int n0) {
   __shared__ float As[kBK][kBM + 4];
   __shared__ float Bs[kBK][kBN + 4];
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
-  float acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-
-  for (int k0 = 0; k0 < K; k0 += kBK) {
+  for (int kb = k0; kb < k1; kb += kBK) {
     // A tile 64 x 16 (stored transposed), B tile 16 x 64
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int idx = tid + kGT * e;         // 0..1023
-      const int am = idx >> 4, ak = idx & 15;
-      const int gm = m0 + am, gk = k0 + ak;
-      As[ak][am] = (gm < M && gk < K) ? A[static_cast<size_t>(gm) * lda + gk] : 0.f;
+      int am, ak;
+      if (A_T) { ak = idx >> 6; am = idx & 63; } else { am = idx >> 4; ak = idx & 15; }
+      const int gm = m0 + am, gk = kb + ak;
+      float av = 0.f;
+      if (gm < M && gk < k1) av = A_T ? A[static_cast<size_t>(gk) * lda + gm] : A[static_cast<size_t>(gm) * lda + gk];
+      As[ak][am] = av;
       int bk, bn;
       if (B_T) { bn = idx >> 4; bk = idx & 15; } else { bk = idx >> 6; bn = idx & 63; }
-      const int gn = n0 + bn, gk2 = k0 + bk;
+      const int gn = n0 + bn, gk2 = kb + bk;
       float bv = 0.f;
-      if (gn < N && gk2 < K) bv = B_T ? B[static_cast<size_t>(gn) * ldb + gk2] : B[static_cast<size_t>(gk2) * ldb + gn];
+      if (gn < N && gk2 < k1) bv = B_T ? B[static_cast<size_t>(gn) * ldb + gk2] : B[static_cast<size_t>(gk2) * ldb + gn];
       Bs[bk][bn] = bv;
     }
     __syncthreads();
@@ -144,6 +143,12 @@ __device__ __forceinline__ void gemm_tile(const float* __restrict__ A, int lda, 
     }
     __syncthreads();
   }
+}
+
+__device__ __forceinline__ void gemm_store(const float (&acc)[4][4], float* __restrict__ C, int ldc, int M, int N,
+                                           int m0, int n0, float alpha, bool causal_only) {
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int gm = m0 + ty * 4 + i;
@@ -155,6 +160,16 @@ __device__ __forceinline__ void gemm_tile(const float* __restrict__ A, int lda, 
       C[static_cast<size_t>(gm) * ldc + gn] = acc[i][j] * alpha;
     }
   }
+}
+
+// C = alpha * A Bm over the full K (one 64 x 64 tile)
+template <bool B_T>
+__device__ __forceinline__ void gemm_tile(const float* __restrict__ A, int lda, const float* __restrict__ B,
+                                          int ldb, float* __restrict__ C, int ldc, int M, int N, int K,
+                                          int m0, int n0, float alpha, bool causal_only) {
+  float acc[4][4] = {};
+  gemm_accum<false, B_T>(acc, A, lda, B, ldb, M, N, 0, K, m0, n0);
+  gemm_store(acc, C, ldc, M, N, m0, n0, alpha, causal_only);
 }
 
 // Projections. blockIdx.z: 0 .. B*Hq-1 are Q' (one per query head), the rest
@@ -329,9 +344,157 @@ __global__ __launch_bounds__(kST) void gate_softmax_mask_kernel(GateArgs a, Topk
   for (int j = n + tid; j < a.nb; j += kST) mrow[j] = 0;
 }
 
-}  // namespace
+// ---------------------------------------------------------------------------
+// Block-level RoPE ("SeerAttention: Learning Intrinsic Sparse Attention in
+// Your LLMs", explainer section 3.4, "Block-Level RoPE"): the projected Q' and
+// K' rows are rotated at their block position i with base theta' = theta / 64,
+// dims d and d + Dg/2 forming a pair: angle = i * theta'^(-2d/Dg). In place,
+// one thread per (row, pair); the angle, its sine and cosine and the rotation
+// are computed in fp64 so that long sequences keep the angle exact. `sign` =
+// -1 rotates back (the transpose, used by the gradient).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gate_rope_kernel(float* __restrict__ x, int rows, int nb, int dg,
+                                                        double base, double sign) {
+  const int half = dg / 2;
+  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;   // over nb * half
+  const int z = blockIdx.y;
+  if (z >= rows || idx >= static_cast<long long>(nb) * half) return;
+  const int i = static_cast<int>(idx / half), d = static_cast<int>(idx - static_cast<long long>(i) * half);
+  const double ang = sign * static_cast<double>(i) * pow(base, -2.0 * d / dg);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  float* r = x + (static_cast<size_t>(z) * nb + i) * dg;
+  const double x1 = r[d], x2 = r[d + half];
+  r[d] = static_cast<float>(x1 * cs - x2 * sn);
+  r[d + half] = static_cast<float>(x2 * cs + x1 * sn);
+}
 
-hipError_t launch_gate(const GateArgs& a, const TopkTable& tk, hipStream_t st) {
+// ---------------------------------------------------------------------------
+// Self-distillation step (same page, "Training Procedure": loss =
+// D_KL(gt || score)). One workgroup per row (b, h, i) of the block logits z:
+// with p = gt row / its sum and log score = z - logsumexp(z) over j <= i,
+//   row_loss = sum_{p_j > 0} p_j (log p_j - log score_j),
+//   dz_j = (score_j - p_j) / (B Hq nb) for j <= i, 0 above the diagonal,
+// dz overwriting the logits in place. A row whose ground truth sums to 0 has
+// no target distribution and contributes nothing (loss 0, dz 0).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kST) void gate_kl_kernel(GateArgs a) {
+  __shared__ float red[kST / kWave];
+  const int i = blockIdx.x;
+  const int z = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int n = i + 1;
+  float* zrow = a.scores + (static_cast<size_t>(z) * a.nb + i) * a.nb;
+  const float* grow = a.gt + (static_cast<size_t>(z) * a.nb + i) * a.nb;
+  float mx = -INFINITY, gsum = 0.f;
+  for (int j = tid; j < n; j += kST) {
+    mx = fmaxf(mx, zrow[j]);
+    gsum += grow[j];
+  }
+  mx = block_reduce_max(mx, red);
+  gsum = block_reduce_sum(gsum, red);
+  float l = 0.f;
+  for (int j = tid; j < n; j += kST) l += expf(zrow[j] - mx);
+  l = block_reduce_sum(l, red);
+  const float lse = mx + logf(l);
+  const bool valid = gsum > 0.f;             // a row without ground-truth mass contributes nothing
+  const float inv_g = valid ? 1.0f / gsum : 0.f;
+  const float inv_rows = 1.0f / (static_cast<float>(a.B) * a.Hq * a.nb);
+  float kl = 0.f;
+  for (int j = tid; j < a.nb; j += kST) {
+    float dz = 0.f;
+    if (j < n) {
+      const float ls = zrow[j] - lse;
+      const float pj = grow[j] * inv_g;
+      if (pj > 0.f) kl += pj * (logf(pj) - ls);
+      dz = valid ? (expf(ls) - pj) * inv_rows : 0.f;
+    }
+    zrow[j] = dz;
+  }
+  kl = block_reduce_sum(kl, red);
+  if (tid == 0) a.row_loss[static_cast<size_t>(z) * a.nb + i] = kl;
+}
+
+// dQ'[z] = dz[z] K'[b, hk] / sqrt(D) and dK'[z] = dz[z]^T Q'[z] / sqrt(D) for
+// every query head z = b Hq + h (dz lower triangular: the k range is cut to
+// the causal part). blockIdx.z < B Hq: dQ', else dK'.
+__global__ __launch_bounds__(kGT) void gate_dproj_kernel(GateArgs a) {
+  const int nq = a.B * a.Hq;
+  const int zz = blockIdx.z;
+  const int z = zz < nq ? zz : zz - nq;
+  const int b = z / a.Hq, h = z % a.Hq;
+  const int hwk = a.wk_per_kv ? a.Hkv : a.Hq;
+  const int hk = a.wk_per_kv ? h / a.group : h;
+  const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * kBN;
+  const float* dz = a.scores + static_cast<size_t>(z) * a.nb * a.nb;
+  float acc[4][4] = {};
+  if (zz < nq) {
+    const float* kg = a.kg + (static_cast<size_t>(b) * hwk + hk) * a.nb * a.Dg;
+    gemm_accum<false, false>(acc, dz, a.nb, kg, a.Dg, a.nb, a.Dg, 0, min(a.nb, m0 + kBM), m0, n0);
+    gemm_store(acc, a.dqg + static_cast<size_t>(z) * a.nb * a.Dg, a.Dg, a.nb, a.Dg, m0, n0, a.scale, false);
+  } else {
+    const float* qg = a.qg + static_cast<size_t>(z) * a.nb * a.Dg;
+    gemm_accum<true, false>(acc, dz, a.nb, qg, a.Dg, a.nb, a.Dg, m0 / kBK * kBK, a.nb, m0, n0);
+    gemm_store(acc, a.dkg + static_cast<size_t>(z) * a.nb * a.Dg, a.Dg, a.nb, a.Dg, m0, n0, a.scale, false);
+  }
+}
+
+// Weight gradients: dW_q[h] = sum_b Qp[b,h]^T dQ'[b,h] (D x Dg) and
+// dW_k[w] = sum_b sum_{h -> w} Kp[b,g(h)]^T dK'[b,h] (3D x Dg), where h -> w
+// are the query heads using W_k[w] (one, or the G heads of KV group w).
+// blockIdx.z < Hq: W_q of head z, else W_k index z - Hq.
+__global__ __launch_bounds__(kGT) void gate_dweight_kernel(GateArgs a) {
+  const int zz = blockIdx.z;
+  const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * kBN;
+  float acc[4][4] = {};
+  if (zz < a.Hq) {
+    if (m0 >= a.D) return;                   // uniform per workgroup
+    for (int b = 0; b < a.B; ++b) {
+      const size_t zq = static_cast<size_t>(b) * a.Hq + zz;
+      gemm_accum<true, false>(acc, a.qp + zq * a.nb * a.D, a.D, a.dqg + zq * a.nb * a.Dg, a.Dg, a.D, a.Dg, 0,
+                              a.nb, m0, n0);
+    }
+    gemm_store(acc, a.grad_wq + static_cast<size_t>(zz) * a.D * a.Dg, a.Dg, a.D, a.Dg, m0, n0, 1.0f, false);
+  } else {
+    const int w = zz - a.Hq;
+    const int K3 = 3 * a.D;
+    if (m0 >= K3) return;
+    const int h0 = a.wk_per_kv ? w * a.group : w, h1 = a.wk_per_kv ? h0 + a.group : w + 1;
+    for (int b = 0; b < a.B; ++b)
+      for (int h = h0; h < h1; ++h) {
+        const int g = h / a.group;
+        const size_t zq = static_cast<size_t>(b) * a.Hq + h;
+        gemm_accum<true, false>(acc, a.kp + (static_cast<size_t>(b) * a.Hkv + g) * a.nb * K3, K3,
+                                a.dkg + zq * a.nb * a.Dg, a.Dg, K3, a.Dg, 0, a.nb, m0, n0);
+      }
+    gemm_store(acc, a.grad_wk + static_cast<size_t>(w) * K3 * a.Dg, a.Dg, K3, a.Dg, m0, n0, 1.0f, false);
+  }
+}
+
+// loss = mean of the row divergences: one workgroup, fixed summation order, fp64
+__global__ __launch_bounds__(kST) void gate_loss_kernel(GateArgs a) {
+  __shared__ double red[kST];
+  const long long n = static_cast<long long>(a.B) * a.Hq * a.nb;
+  double s = 0.0;
+  for (long long r = threadIdx.x; r < n; r += kST) s += a.row_loss[r];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = kST / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.loss[0] = static_cast<float>(red[0] / static_cast<double>(n));
+}
+
+hipError_t launch_rope(const GateArgs& a, float* x, int rows, double sign, hipStream_t st) {
+  const long long n = static_cast<long long>(a.nb) * (a.Dg / 2);
+  dim3 g(static_cast<unsigned>((n + 255) / 256), rows);
+  hipLaunchKernelGGL(gate_rope_kernel, g, dim3(256), 0, st, x, rows, a.nb, a.Dg, a.rope_base, sign);
+  return hipGetLastError();
+}
+
+// pool, projections, optional block RoPE, causal logits (shared by both calls)
+hipError_t launch_gate_logits(const GateArgs& a, hipStream_t st) {
   const int H = a.Hq + a.Hkv;
   dim3 gp(a.nb, a.B * H);
   if (a.D == 64) hipLaunchKernelGGL(gate_pool_kernel<64>, gp, dim3(kPoolThreads), 0, st, a);
@@ -344,13 +507,45 @@ hipError_t launch_gate(const GateArgs& a, const TopkTable& tk, hipStream_t st) {
   hipLaunchKernelGGL(gate_proj_kernel, gj, dim3(kGT), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
+  if (a.rope_base > 0.0) {
+    if ((e = launch_rope(a, a.qg, a.B * a.Hq, 1.0, st)) != hipSuccess) return e;
+    if ((e = launch_rope(a, a.kg, a.B * hwk, 1.0, st)) != hipSuccess) return e;
+  }
+
   const int T = (a.nb + kBM - 1) / kBM;
   dim3 gl(T * (T + 1) / 2, a.B * a.Hq);
   hipLaunchKernelGGL(gate_logits_kernel, gl, dim3(kGT), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return hipGetLastError();
+}
 
+}  // namespace
+
+hipError_t launch_gate(const GateArgs& a, const TopkTable& tk, hipStream_t st) {
+  hipError_t e = launch_gate_logits(a, st);
+  if (e != hipSuccess) return e;
   dim3 gs(a.nb, a.B * a.Hq);
   hipLaunchKernelGGL(gate_softmax_mask_kernel, gs, dim3(kST), static_cast<size_t>(a.nb) * sizeof(float), st, a, tk);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_distill(const GateArgs& a, hipStream_t st) {
+  hipError_t e = launch_gate_logits(a, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gate_kl_kernel, dim3(a.nb, a.B * a.Hq), dim3(kST), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int nq = a.B * a.Hq;
+  dim3 gd((a.nb + kBM - 1) / kBM, (a.Dg + kBN - 1) / kBN, 2 * nq);
+  hipLaunchKernelGGL(gate_dproj_kernel, gd, dim3(kGT), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.rope_base > 0.0) {
+    if ((e = launch_rope(a, a.dqg, nq, -1.0, st)) != hipSuccess) return e;
+    if ((e = launch_rope(a, a.dkg, nq, -1.0, st)) != hipSuccess) return e;
+  }
+  const int hwk = a.wk_per_kv ? a.Hkv : a.Hq;
+  dim3 gw((3 * a.D + kBM - 1) / kBM, (a.Dg + kBN - 1) / kBN, a.Hq + hwk);
+  hipLaunchKernelGGL(gate_dweight_kernel, gw, dim3(kGT), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(gate_loss_kernel, dim3(1), dim3(kST), 0, st, a);
   return hipGetLastError();
 }
 

@@ -146,6 +146,30 @@ GateLayout gate_layout(const seer_shape* s, int dg, int wk_per_kv, bool want_sco
   return L;
 }
 
+struct DistillLayout {
+  GateLayout g;       // pooled, projected and logits (scores segment always present)
+  size_t dqg, dkg, row_loss, total;
+};
+
+DistillLayout distill_layout(const seer_shape* s, int dg, int wk_per_kv) {
+  const size_t B = s->batch, Hq = s->heads_q, nb = nblocks(s);
+  DistillLayout L{};
+  L.g = gate_layout(s, dg, wk_per_kv, false);
+  size_t off = L.g.total;
+  L.dqg = off; off += align_up(B * Hq * nb * dg * 4);
+  L.dkg = off; off += align_up(B * Hq * nb * dg * 4);
+  L.row_loss = off; off += align_up(B * Hq * nb * 4);
+  L.total = off;
+  return L;
+}
+
+seer_status check_rope(float rope_theta) {
+  if (!isfinite(rope_theta) || rope_theta < 0.f)
+    return fail(SEER_ERR_INVALID_ARG, "rope_theta must be 0 (no RoPE) or a finite positive base (got %g)",
+                static_cast<double>(rope_theta));
+  return SEER_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,8 +198,8 @@ size_t seer_gate_workspace_size(const seer_shape* shape, int32_t gate_dim, int32
   return gate_layout(shape, gate_dim, wk_per_kv_head != 0, want_scores != 0).total;
 }
 
-seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_per_kv_head, const void* q,
-                          const void* k, const float* w_q, const float* w_k, seer_mask_mode mode,
+seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_per_kv_head, float rope_theta,
+                          const void* q, const void* k, const float* w_q, const float* w_k, seer_mask_mode mode,
                           float threshold, int32_t topk_k, const int32_t* topk_per_head, float* scores,
                           uint8_t* block_mask, void* workspace, size_t workspace_bytes, void* hip_stream) {
   bool empty = false;
@@ -187,6 +211,7 @@ seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_
     return fail(SEER_ERR_INVALID_ARG, "mask mode %d is not SEER_MASK_THRESHOLD/SEER_MASK_TOPK", mode);
   if (mode == SEER_MASK_THRESHOLD && !isfinite(threshold))
     return fail(SEER_ERR_INVALID_ARG, "threshold must be finite");
+  if ((st = check_rope(rope_theta)) != SEER_OK) return st;
   seer::TopkTable tk{};
   if (mode == SEER_MASK_TOPK) {
     if (shape->heads_q > seer::kMaxTopkHeads)
@@ -236,8 +261,77 @@ seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_
   a.scale = static_cast<float>(1.0 / sqrt(static_cast<double>(shape->head_dim)));
   a.mode = mode == SEER_MASK_TOPK ? 1 : 0;
   a.threshold = threshold;
+  a.rope_base = rope_theta > 0.f ? static_cast<double>(rope_theta) / shape->block : 0.0;
   hipError_t e = seer::launch_gate(a, tk, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SEER_ERR_HIP, "gate launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+size_t seer_gate_distill_workspace_size(const seer_shape* shape, int32_t gate_dim, int32_t wk_per_kv_head) {
+  bool empty = false;
+  if (check_shape(shape, &empty) != SEER_OK || gate_dim <= 0) return 0;
+  return distill_layout(shape, gate_dim, wk_per_kv_head != 0).total;
+}
+
+seer_status seer_gate_distill_bwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_per_kv_head,
+                                  float rope_theta, const void* q, const void* k, const float* w_q,
+                                  const float* w_k, const float* gt, float* loss, float* grad_wq,
+                                  float* grad_wk, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  bool empty = false;
+  seer_status st = check_shape(shape, &empty);
+  if (st != SEER_OK) return st;
+  if (gate_dim < 16 || gate_dim > 256 || gate_dim % 16 != 0)
+    return fail(SEER_ERR_UNSUPPORTED, "gate_dim must be a multiple of 16 in [16, 256] (got %d)", gate_dim);
+  if ((st = check_rope(rope_theta)) != SEER_OK) return st;
+  if (nblocks(shape) > kMaxNbGate)
+    return fail(SEER_ERR_UNSUPPORTED, "the gate supports at most %d blocks per sequence", kMaxNbGate);
+  if (loss == nullptr || grad_wq == nullptr || grad_wk == nullptr)
+    return fail(SEER_ERR_INVALID_ARG, "loss, grad_wq and grad_wk must be non-NULL");
+  if (empty) return ok();
+  if ((st = check_qkv(q, k, k)) != SEER_OK) return st;
+  if (w_q == nullptr || w_k == nullptr || gt == nullptr)
+    return fail(SEER_ERR_INVALID_ARG, "w_q, w_k and gt must be non-NULL");
+  if (!aligned(gt, 4) || !aligned(loss, 4) || !aligned(grad_wq, 4) || !aligned(grad_wk, 4))
+    return fail(SEER_ERR_INVALID_ARG, "gt, loss and the gradients must be 4-byte aligned");
+  const DistillLayout L = distill_layout(shape, gate_dim, wk_per_kv_head != 0);
+  if (workspace == nullptr || workspace_bytes < L.total || !aligned(workspace, kAlign))
+    return fail(SEER_ERR_WORKSPACE, "workspace must be %zu bytes, 256-byte aligned (got %zu at %p)", L.total,
+                workspace_bytes, workspace);
+  st = check_device();
+  if (st != SEER_OK) return st;
+
+  char* ws = static_cast<char*>(workspace);
+  seer::GateArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.wq = w_q;
+  a.wk = w_k;
+  a.qp = reinterpret_cast<float*>(ws + L.g.qp);
+  a.kp = reinterpret_cast<float*>(ws + L.g.kp);
+  a.qg = reinterpret_cast<float*>(ws + L.g.qg);
+  a.kg = reinterpret_cast<float*>(ws + L.g.kg);
+  a.scores = reinterpret_cast<float*>(ws + L.g.scores);
+  a.dqg = reinterpret_cast<float*>(ws + L.dqg);
+  a.dkg = reinterpret_cast<float*>(ws + L.dkg);
+  a.row_loss = reinterpret_cast<float*>(ws + L.row_loss);
+  a.gt = gt;
+  a.loss = loss;
+  a.grad_wq = grad_wq;
+  a.grad_wk = grad_wk;
+  a.B = shape->batch;
+  a.Hq = shape->heads_q;
+  a.Hkv = shape->heads_kv;
+  a.S = shape->seq_len;
+  a.D = shape->head_dim;
+  a.nb = static_cast<int>(nblocks(shape));
+  a.Dg = gate_dim;
+  a.group = shape->heads_q / shape->heads_kv;
+  a.wk_per_kv = wk_per_kv_head != 0;
+  a.scale = static_cast<float>(1.0 / sqrt(static_cast<double>(shape->head_dim)));
+  a.rope_base = rope_theta > 0.f ? static_cast<double>(rope_theta) / shape->block : 0.0;
+  hipError_t e = seer::launch_gate_distill(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SEER_ERR_HIP, "distillation launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -56,6 +56,15 @@ struct GateArgs {
   float scale;         // 1/sqrt(D)
   int mode;            // 0 threshold, 1 top-k
   float threshold;
+  double rope_base;    // base theta / 64 of the gate's block RoPE; 0 = no RoPE
+  // distillation step
+  const float* gt;     // [B,Hq,nb,nb] 2D-maxpooled map
+  float* dqg;          // [B,Hq,nb,Dg] d loss / d Q' (rotated, then back-rotated in place)
+  float* dkg;          // [B,Hq,nb,Dg] d loss / d K' per query head
+  float* row_loss;     // [B*Hq*nb]
+  float* loss;         // [1]
+  float* grad_wq;      // [Hq,D,Dg]
+  float* grad_wk;      // [Hwk,3D,Dg]
 };
 
 constexpr int kMaxTopkHeads = 256;
@@ -64,5 +73,6 @@ struct TopkTable {
 };
 
 hipError_t launch_gate(const GateArgs& a, const TopkTable& tk, hipStream_t st);
+hipError_t launch_gate_distill(const GateArgs& a, hipStream_t st);
 
 }  // namespace seer

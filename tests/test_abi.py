@@ -36,9 +36,14 @@ def _attn(shape, q=FAKE, k=FAKE, v=FAKE, mask=None, out=FAKE, dt=B.SEER_F32, lse
 
 
 def _gate(shape, dg=128, per_kv=0, mode=B.SEER_MASK_THRESHOLD, T=5e-4, k=4, per_head=None, scores=None,
-          mask=FAKE, ws=FAKE, ws_bytes=1 << 40):
-    return _lib().seer_gate_fwd(ctypes.byref(shape), dg, per_kv, FAKE, FAKE, FAKE, FAKE, mode, T, k, per_head,
+          mask=FAKE, ws=FAKE, ws_bytes=1 << 40, rope=0.0):
+    return _lib().seer_gate_fwd(ctypes.byref(shape), dg, per_kv, rope, FAKE, FAKE, FAKE, FAKE, mode, T, k, per_head,
                                 scores, mask, ws, ws_bytes, None)
+
+
+def _distill(shape, dg=128, per_kv=0, rope=0.0, gt=FAKE, loss=FAKE, gq=FAKE, gk=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return _lib().seer_gate_distill_bwd(ctypes.byref(shape), dg, per_kv, rope, FAKE, FAKE, FAKE, FAKE, gt, loss,
+                                        gq, gk, ws, ws_bytes, None)
 
 
 def test_exports_every_declared_symbol():
@@ -99,6 +104,33 @@ def test_sparse_workspace_validation():
     assert _attn(s, mask=FAKE, ws=ctypes.c_void_p(0x10008), ws_bytes=need) == B.SEER_ERR_WORKSPACE
     # dense attention takes no workspace
     assert _attn(s) != B.SEER_ERR_WORKSPACE
+
+
+def test_gate_rope_and_distill_validation():
+    s = _shape()
+    for bad in (-1.0, math.inf, math.nan):
+        assert _gate(s, rope=bad) == B.SEER_ERR_INVALID_ARG
+        assert b"rope_theta" in _lib().seer_last_error()
+        assert _distill(s, rope=bad) == B.SEER_ERR_INVALID_ARG
+    assert _distill(s, dg=100) == B.SEER_ERR_UNSUPPORTED
+    assert _distill(s, loss=None) == B.SEER_ERR_INVALID_ARG
+    assert _distill(s, gt=None) == B.SEER_ERR_INVALID_ARG
+    assert _distill(s, gk=None) == B.SEER_ERR_INVALID_ARG
+    need = _lib().seer_gate_distill_workspace_size(ctypes.byref(s), 128, 0)
+    assert _distill(s, ws_bytes=need - 1) == B.SEER_ERR_WORKSPACE
+    assert _distill(_shape(s=0), gt=None, loss=FAKE) != B.SEER_ERR_WORKSPACE
+
+
+def test_distill_workspace_size():
+    # gate segments (pooled Q, pooled K, Q', K', logits) + dQ', dK' + row losses, 256-byte aligned
+    lib = _lib()
+    s = _shape(b=2, hq=4, hkv=2, s=200, d=64)
+    nb = 4
+    align = lambda x: (x + 255) // 256 * 256
+    gate = (align(2 * 4 * nb * 64 * 4) + align(2 * 2 * nb * 192 * 4) + align(2 * 4 * nb * 32 * 4)
+            + align(2 * 4 * nb * 32 * 4) + align(2 * 4 * nb * nb * 4))
+    want = gate + 2 * align(2 * 4 * nb * 32 * 4) + align(2 * 4 * nb * 4)
+    assert lib.seer_gate_distill_workspace_size(ctypes.byref(s), 32, 0) == want
 
 
 def test_gate_validation():
