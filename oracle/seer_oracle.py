@@ -30,7 +30,8 @@ the design notes):
     block positions, dims d and d + Dg/2 paired;
   * distillation: gt rows are normalized to sum 1 before the divergence, and
     the loss is the mean of the row divergences over all query-block rows; a
-    row whose gt sums to 0 has no target and contributes nothing.
+    row whose gt sums to 0 has no target and contributes nothing;
+  * decode gating: see the readings above decode_kcomp.
 
 Inputs may be bfloat16 bit patterns (uint16 arrays, as produced by the
 seeded generators) or float arrays; they are widened exactly to float64.
@@ -229,6 +230,130 @@ def gate_distill(q, k, w_q, w_k, gt, block: int = BLOCK, wk_per_kv_head: bool = 
             grad_wq[h] += qp.T @ dqg
             grad_wk[wk_idx] += kp.T @ dkg
     return loss / n_rows, grad_wq, grad_wk
+
+
+# --------------------------------------------------------------------------
+# Decode-stage gating ([R], the responses on decoding: for decode the gate
+# drops the query branch's pooling and linear map, so the query of each new
+# token meets a small compressed K cache -- pooled keys taken after the
+# model's RoPE -- and the gate is distilled against the attention map
+# max-pooled along the sequence only; the selected blocks' K and V are the
+# only ones read).
+# Readings: the decode query is the model's (post-RoPE) query of the newest
+# token and it sees every cached key; the compressed cache holds the keys
+# [max | min | avg]-pooled per block, as for the prefill gate, projected by
+# W_k to the head dimension D (W_k is 3D x D, one per query head or one per
+# KV head), so score_j = softmax over all blocks j of q . K'_j / sqrt(D); no
+# extra block-level RoPE; masks keep the blocks with score > T, or the k
+# largest scores (ties to the lower block index, all blocks if nb <= k).
+# --------------------------------------------------------------------------
+def decode_kcomp(k, w_k, heads_q: int, block: int = BLOCK, wk_per_kv_head: bool = False) -> np.ndarray:
+    """Compressed K cache K' [B, Hwk, nb, D] = pool_k(K) @ W_k.
+
+    k: [B, Hkv, S, D]; w_k: [Hwk, 3D, D] with Hwk = Hkv (wk_per_kv_head) or
+    heads_q (query head h uses the pooled keys of its KV head h // G).
+    """
+    w_k = as_f64(w_k)
+    B, Hkv = np.shape(k)[:2]
+    G = heads_q // Hkv
+    hwk = Hkv if wk_per_kv_head else heads_q
+    out = []
+    for b in range(B):
+        rows = []
+        for w in range(hwk):
+            g = w if wk_per_kv_head else w // G
+            rows.append(pool_k(np.asarray(k)[b, g], block) @ w_k[w])
+        out.append(np.stack(rows))
+    return np.stack(out)
+
+
+def decode_gate_scores(q, kcomp, wk_per_kv_head: bool = False) -> np.ndarray:
+    """Decode gate score [B, Hq, nb]: softmax over all key blocks j of q . K'_j / sqrt(D).
+
+    q: [B, Hq, D], one query per head; kcomp: [B, Hwk, nb, D] from decode_kcomp.
+    """
+    q = as_f64(q)
+    kcomp = np.asarray(kcomp, dtype=np.float64)
+    B, Hq, D = q.shape
+    hwk = kcomp.shape[1]
+    G = Hq // hwk if wk_per_kv_head else 1
+    out = np.zeros((B, Hq, kcomp.shape[2]))
+    for b in range(B):
+        for h in range(Hq):
+            z = kcomp[b, h // G if wk_per_kv_head else h] @ q[b, h] / np.sqrt(D)
+            e = np.exp(z - z.max())
+            out[b, h] = e / e.sum()
+    return out
+
+
+def decode_threshold_mask(scores, threshold: float) -> np.ndarray:
+    """uint8 [B, Hq, nb]: 1 where score > threshold (strict)."""
+    return (np.asarray(scores, dtype=np.float64) > threshold).astype(np.uint8)
+
+
+def decode_topk_mask(scores, k) -> np.ndarray:
+    """uint8 [B, Hq, nb] keeping the k largest scores of each (b, h) row, ties to the lower j."""
+    s = np.asarray(scores, dtype=np.float64)
+    B, H, nb = s.shape
+    ks = np.broadcast_to(np.asarray(k, dtype=np.int64), (H,))
+    out = np.zeros(s.shape, dtype=np.uint8)
+    for b in range(B):
+        for h in range(H):
+            order = np.argsort(-s[b, h], kind="stable")
+            out[b, h, order[:min(int(ks[h]), nb)]] = 1
+    return out
+
+
+def decode_attention(q, k, v, block_mask=None, block: int = BLOCK):
+    """One query per head against every cached key, restricted to active blocks.
+
+    q: [B, Hq, D]; k, v: [B, Hkv, S, D]; block_mask: [B, Hq, nb] (non-zero =
+    read the block) or None (all blocks). Returns (O [B, Hq, Dv], LSE [B, Hq]),
+    O = 0 and LSE = -inf when no block is active.
+    """
+    q = as_f64(q)
+    B, Hq, D = q.shape
+    Hkv, S = np.shape(k)[1], np.shape(k)[2]
+    G = Hq // Hkv
+    nb = n_blocks(S, block)
+    o = np.zeros((B, Hq, np.shape(v)[-1]))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            blocks = range(nb) if block_mask is None else [j for j in range(nb) if block_mask[b, h, j] != 0]
+            keys = [u for j in blocks for u in range(*_block_range(j, S, block))]
+            if not keys:
+                continue
+            kk = as_f64(np.asarray(k)[b, g, keys])
+            vv = as_f64(np.asarray(v)[b, g, keys])
+            s_ = kk @ q[b, h] / np.sqrt(D)
+            mx = s_.max()
+            e = np.exp(s_ - mx)
+            o[b, h] = e @ vv / e.sum()
+            lse[b, h] = mx + np.log(e.sum())
+    return o, lse
+
+
+def decode_gt(q, k, block: int = BLOCK) -> np.ndarray:
+    """1D max-pooled attention map [B, Hq, nb]: for each block j, the largest
+    attention probability of the decode query on a key of that block (full
+    attention over every cached key)."""
+    q = as_f64(q)
+    B, Hq, D = q.shape
+    Hkv, S = np.shape(k)[1], np.shape(k)[2]
+    G = Hq // Hkv
+    nb = n_blocks(S, block)
+    out = np.zeros((B, Hq, nb))
+    for b in range(B):
+        for h in range(Hq):
+            s_ = as_f64(np.asarray(k)[b, h // G]) @ q[b, h] / np.sqrt(D)
+            p = np.exp(s_ - s_.max())
+            p /= p.sum()
+            for j in range(nb):
+                a, e = _block_range(j, S, block)
+                out[b, h, j] = p[a:e].max()
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -560,6 +560,100 @@ def pin_distill_loss_definition(O):
     assert lo == 0.0 and np.abs(gqo).max() == 0.0 and np.abs(gko).max() == 0.0
 
 
+# ----------------------------------------------------------------------------
+# decode-stage gating
+# ----------------------------------------------------------------------------
+def pin_decode_attention_matches_sdpa_and_prefill(O):
+    """Dense decode attention equals torch SDPA (fp64, one query against every
+    key, GQA); with a block mask it equals the last row of the separately
+    pinned prefill attention given that mask row (the newest token of a
+    prefill sees exactly the cached keys)."""
+    shape = Shape(2, 4, 2, 64 * 5 - 11, 16)
+    q, k, v = _qkv(shape, 81)
+    qd = q[:, :, -1]
+    o, lse = O.decode_attention(qd, k, v, None)
+    ref = _sdpa(qd[:, :, None], k, v, causal=False)[:, :, 0]
+    assert np.abs(o - ref).max() < 1e-12
+    s_ = np.einsum("bhd,bhsd->bhs", qd, np.repeat(k, 2, axis=1)) / 4.0
+    assert np.abs(lse - np.log(np.exp(s_).sum(-1))).max() < 1e-12
+    rng = np.random.default_rng(3)
+    nb = shape.nb
+    m2 = (rng.random((2, 4, nb, nb)) < 0.5).astype(np.uint8)
+    m2[0, 1, nb - 1, :] = 0                        # empty row
+    od, ld = O.decode_attention(qd, k, v, m2[:, :, nb - 1])
+    rows = [(b, h, nb - 1) for b in range(2) for h in range(4)]
+    o_rows, l_rows = O.attention_rows(q, k, v, m2, rows)
+    for n, (b, h, _) in enumerate(rows):
+        assert np.abs(od[b, h] - o_rows[n][-1]).max() < 1e-12
+        assert (ld[b, h] == l_rows[n][-1]) or abs(ld[b, h] - l_rows[n][-1]) < 1e-12
+    assert ld[0, 1] == -np.inf and np.all(od[0, 1] == 0.0)
+
+
+def pin_decode_gt_bruteforce_and_2d(O):
+    """1D max-pooled map: pure-Python brute force, and equal to the last row of
+    the separately pinned 2D map when the last block holds only the newest token."""
+    shape = Shape(1, 2, 1, 64 * 3 + 1, 8)
+    q, k, _ = _qkv(shape, 82)
+    got = O.decode_gt(q[:, :, -1], k)
+    for h in range(2):
+        s_ = [sum(q[0, h, -1, d] * k[0, 0, u, d] for d in range(8)) / math.sqrt(8) for u in range(shape.seq_len)]
+        mx = max(s_)
+        e = [math.exp(x - mx) for x in s_]
+        tot = sum(e)
+        for j in range(4):
+            want = max(e[u] / tot for u in range(64 * j, min(64 * j + 64, shape.seq_len)))
+            assert abs(got[0, h, j] - want) < 1e-14
+    gt2 = O.maxpool_gt(q, k)
+    assert np.abs(got - gt2[:, :, -1, :]).max() < 1e-14
+
+
+def pin_decode_gate(O):
+    """Compressed cache = torch max/min/avg pooling then W_k (per query head and
+    per KV head); W_k = 0 gives uniform scores 1/nb; scores are a softmax of
+    q . K'_j / sqrt(D) over every block (brute force)."""
+    shape = Shape(1, 4, 2, 64 * 6 - 20, 8)
+    q, k, _ = _qkv(shape, 83)
+    rng = np.random.default_rng(8)
+    nb = shape.nb
+    for per_kv in (False, True):
+        hw = 2 if per_kv else 4
+        wk = rng.standard_normal((hw, 24, 8)) / 3.0
+        kc = O.decode_kcomp(k, wk, 4, wk_per_kv_head=per_kv)
+        for w in range(hw):
+            g = w if per_kv else w // 2
+            tk = torch.from_numpy(k[0, g])
+            kp = np.stack([np.concatenate([tk[64 * j:64 * j + 64].max(0).values.numpy(),
+                                           tk[64 * j:64 * j + 64].min(0).values.numpy(),
+                                           tk[64 * j:64 * j + 64].mean(0).numpy()]) for j in range(nb)])
+            assert np.abs(kc[0, w] - kp @ wk[w]).max() < 1e-12
+        sc = O.decode_gate_scores(q[:, :, -1], kc, wk_per_kv_head=per_kv)
+        for h in range(4):
+            w = h // 2 if per_kv else h
+            z = [sum(q[0, h, -1, d] * kc[0, w, j, d] for d in range(8)) / math.sqrt(8) for j in range(nb)]
+            mx = max(z)
+            e = [math.exp(x - mx) for x in z]
+            for j in range(nb):
+                assert abs(sc[0, h, j] - e[j] / sum(e)) < 1e-14
+    kc0 = O.decode_kcomp(k, np.zeros((4, 24, 8)), 4)
+    assert np.abs(O.decode_gate_scores(q[:, :, -1], kc0) - 1.0 / nb).max() < 1e-15
+
+
+def pin_decode_masks(O):
+    s_ = np.array([[[0.1, 0.3, 0.3, 0.05, 0.25]]])
+    assert O.decode_threshold_mask(s_, 0.25).tolist() == [[[0, 1, 1, 0, 0]]]
+    assert O.decode_topk_mask(s_, 2).tolist() == [[[0, 1, 1, 0, 0]]]
+    assert O.decode_topk_mask(s_, 3).tolist() == [[[0, 1, 1, 0, 1]]]
+    flat = np.full((1, 2, 6), 1.0 / 6)
+    assert O.decode_topk_mask(flat, [2, 9]).tolist() == [[[1, 1, 0, 0, 0, 0], [1] * 6]]
+    rng = np.random.default_rng(9)
+    sc = rng.random((2, 3, 40))
+    m = O.decode_topk_mask(sc, 7)
+    for b in range(2):
+        for h in range(3):
+            keep = set(sorted(range(40), key=lambda j: (-sc[b, h, j], j))[:7])
+            assert [int(x) for x in m[b, h]] == [1 if j in keep else 0 for j in range(40)]
+
+
 ATTENTION_PINS = [pin_dense_matches_torch_sdpa, pin_probabilities_via_one_hot_v,
                   pin_constant_v_and_empty_rows, pin_q_zero_closed_form, pin_single_block_row,
                   pin_gqa_equals_mha, pin_bruteforce_python_loops]
@@ -571,4 +665,6 @@ MASK_PINS = [pin_threshold_strict, pin_threshold_nesting, pin_topk_counts, pin_t
              pin_topk_bruteforce]
 ROPE_PINS = [pin_rope_hand_complex, pin_rope_relative_and_orthogonal, pin_gate_rope_complex_bruteforce]
 DISTILL_PINS = [pin_distill_finite_differences, pin_distill_loss_definition]
-ALL_PINS = ATTENTION_PINS + GT_PINS + GATE_PINS + MASK_PINS + ROPE_PINS + DISTILL_PINS
+DECODE_PINS = [pin_decode_attention_matches_sdpa_and_prefill, pin_decode_gt_bruteforce_and_2d, pin_decode_gate,
+               pin_decode_masks]
+ALL_PINS = ATTENTION_PINS + GT_PINS + GATE_PINS + MASK_PINS + ROPE_PINS + DISTILL_PINS + DECODE_PINS

@@ -71,6 +71,18 @@ MUTATIONS = [
     ("distill_no_back_rotation", "dqg = block_rope(dqg, rope_theta, block, positions=neg_pos)",
      "dqg = block_rope(dqg, rope_theta, block)", 0),
     ("distill_sum_not_mean", "return loss / n_rows, grad_wq, grad_wk", "return loss, grad_wq, grad_wk", 0),
+    ("decode_kcomp_wrong_group", "g = w if wk_per_kv_head else w // G", "g = w if wk_per_kv_head else w % Hkv", 0),
+    ("decode_gate_scale_dropped", "@ q[b, h] / np.sqrt(D)\n            e = np.exp(z - z.max())",
+     "@ q[b, h]\n            e = np.exp(z - z.max())", 0),
+    ("decode_threshold_not_strict", "return (np.asarray(scores, dtype=np.float64) > threshold)",
+     "return (np.asarray(scores, dtype=np.float64) >= threshold)", 0),
+    ("decode_topk_ascending", "order = np.argsort(-s[b, h], kind=\"stable\")",
+     "order = np.argsort(s[b, h], kind=\"stable\")", 0),
+    ("decode_attn_mask_ignored", "blocks = range(nb) if block_mask is None else",
+     "blocks = range(nb) if True else", 0),
+    ("decode_attn_lse_no_max", "lse[b, h] = mx + np.log(e.sum())", "lse[b, h] = np.log(e.sum())", 0),
+    ("decode_gt_unnormalized", "p /= p.sum()\n", "p /= 1.0\n", 0),
+    ("decode_gt_mean_not_max", "out[b, h, j] = p[a:e].max()", "out[b, h, j] = p[a:e].mean()", 0),
     ("distill_kl_reversed", "loss += float(np.sum(p[pos] * (np.log(p[pos]) - log_score[pos])))",
      "loss += float(np.sum(score[pos] * (log_score[pos] - np.log(p[pos]))))", 0),
 ]
