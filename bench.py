@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-train", action="store_true",
                     help="skip timing the ground-truth kernel and the gate's distillation step")
+    ap.add_argument("--no-decode", action="store_true", help="skip timing the decode stage")
     ap.add_argument("--rope-theta", type=float, default=5e5,
                     help="RoPE base for the gate's block-level RoPE (0: none); Llama-3.1 uses 500000")
     ap.add_argument("--copy-gib", type=float, default=0.0,
@@ -96,6 +97,69 @@ def computed_peak():
             cus, clk = int(cu.group(1)), int(mhz.group(1))
             return {"cus": cus, "max_sclk_mhz": clk, "bf16_tflops": round(cus * 4096 * clk * 1e6 / 1e12, 1)}
     return None
+
+
+def bench_decode(seer, torch, q, k, v, shape, stream, seed, reps: int = 50):
+    """Decode stage on the same K/V cache: the newest token's query, a compressed
+    K cache, a top-k decode gate keeping 10% of the blocks, and block-sparse
+    decode attention; dense decode attention on the same cache for the speedup.
+    The decode attention is bound by HBM reads of the selected K/V blocks."""
+    import synth
+    B, Hq, Hkv, S, D = shape.batch, shape.heads_q, shape.heads_kv, shape.seq_len, shape.head_dim
+    nb = shape.nb
+    dev = q.device
+    qd = q[:, :, -1].contiguous()
+    _, wk_np = synth.gen_gate_weights(Hq, D, D, seed + 200)
+    wk = torch.from_numpy(wk_np).to(dev)
+    kc = seer.seer_decode_compress_k(k, wk, Hq)
+    k_dec = max(1, nb // 10)
+    mask = torch.empty((B, Hq, nb), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(seer.decode_attn_workspace_bytes(B, Hq, Hkv, S, D), dtype=torch.uint8, device=dev)
+
+    def step():
+        seer.seer_decode_compress_k(k, wk, Hq, kcomp=kc, block_begin=nb - 1)   # the block the new token joined
+        seer.seer_decode_gate_fwd(qd, kc, S, Hkv, mode="topk", topk=k_dec, want_scores=False, block_mask=mask)
+        seer.seer_decode_attn_fwd(qd, k, v, mask, out=out, workspace=ws)
+
+    def sparse_attn():
+        seer.seer_decode_attn_fwd(qd, k, v, mask, out=out, workspace=ws)
+
+    def dense_attn():
+        seer.seer_decode_attn_fwd(qd, k, v, None, out=out, workspace=ws)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps          # microseconds
+
+    step_us = timed(step)
+    sparse_us = timed(sparse_attn)
+    dense_us = timed(dense_attn)
+    m = mask.cpu().numpy().astype(bool).reshape(B, Hkv, Hq // Hkv, nb)
+    union_blocks = int(m.any(axis=2).sum())               # blocks read: union over each KV group's heads
+    blk_bytes = 2 * 64 * D * 2                            # K + V of one block, bf16
+    sparse_bytes = union_blocks * blk_bytes + B * Hq * (nb + 4 * D)
+    dense_bytes = B * Hkv * nb * blk_bytes + B * Hq * 4 * D
+    print(f"[bench] decode step {step_us:.1f} us; decode attention sparse {sparse_us:.1f} us "
+          f"({sparse_bytes / sparse_us / 1e3:.0f} GB/s), dense {dense_us:.1f} us "
+          f"({dense_bytes / dense_us / 1e3:.0f} GB/s)", file=sys.stderr, flush=True)
+    return {"workload": f"newest token of the {S}-token cache, top-k {k_dec} of {nb} blocks per head",
+            "step_us": round(step_us, 2), "sparse_attention_us": round(sparse_us, 2),
+            "dense_attention_us": round(dense_us, 2), "speedup_attention": round(dense_us / sparse_us, 3),
+            "blocks_read_union": union_blocks, "blocks_selected": int(m.sum()),
+            "roofline": {"bound": "hbm", "achieved": round(sparse_bytes / sparse_us / 1e3, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(sparse_bytes / sparse_us / 1e3 / PEAK_HBM_GBS, 4),
+                         "bytes_per_call": sparse_bytes},
+            "dense_roofline_frac": round(dense_bytes / dense_us / 1e3 / PEAK_HBM_GBS, 4)}
 
 
 def topk_for_sparsity(nb: int, s: float) -> int:
@@ -276,6 +340,10 @@ def main():
               f"(loss {float(d_out[0].item()):.5f})", file=sys.stderr, flush=True)
         del d_ws, gt
 
+    decode = None
+    if not args.no_decode:
+        decode = bench_decode(seer, torch, q, k, v, shape, stream, w["seed"])
+
     ms_step = float(np.mean(step_ms))
     attn_avg = float(np.mean(attn_ms))
     gate_avg = float(np.mean(gate_ms))
@@ -312,6 +380,7 @@ def main():
                      "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(args.workload)},
+        "decode": decode,
         "peak_computed": computed_peak(),
         "wall_s_timed": round(wall, 3),
     }

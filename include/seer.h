@@ -196,6 +196,54 @@ seer_status seer_attn_maxpool_gt(const seer_shape* shape, const void* q, const v
                                  void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * Decode stage ([R], the responses on decoding: for decode the gate drops the
+ * query branch's pooling and linear map, each new token's query meets a small
+ * compressed K cache -- keys pooled after the model's RoPE -- and only the
+ * selected blocks' K and V are read; the gate is distilled against the
+ * attention map max-pooled along the sequence).
+ *
+ * shape->seq_len is the number of cached tokens S (the newest token's key and
+ * value included); nb = ceil(S / 64). The decode query q is [B,Hq,D] bf16,
+ * the query of the newest token (after the model's RoPE); it sees every
+ * cached key. k_cache, v_cache are [B,Hkv,S,D] bf16.
+ *
+ * seer_decode_compress_k: the compressed cache
+ *   kcomp[b,w,j,:] = [max | min | mean]_{t in block j} K[b,g(w),t,:] . w_k[w]
+ *   for blocks block_begin <= j < nb (the others are left as they are), with
+ *   w_k fp32 [Hwk,3D,D], Hwk = Hq (g(w) = w / (Hq/Hkv)) or, with
+ *   wk_per_kv_head, Hkv (g(w) = w). kcomp is device fp32
+ *   [B,Hwk,kcomp_blocks,D] with kcomp_blocks >= nb (room to grow): after
+ *   appending tokens, recompute from the first changed block.
+ * seer_decode_gate_fwd: score[b,h,j] = softmax over all j < nb of
+ *   q[b,h] . kcomp[b,w(h),j] / sqrt(D) (w(h) = h, or h / (Hq/Hkv) with
+ *   wk_per_kv_head); block_mask [B,Hq,nb] uint8 = score > threshold, or the
+ *   top-k per (b,h) (ties to the lower j, all blocks if nb <= k); scores
+ *   [B,Hq,nb] fp32 (required: it holds the logits, then the scores).
+ *   nb <= 16384. No workspace.
+ * seer_decode_attn_fwd: O[b,h] = sum_u softmax_u(q[b,h] . K[b,g,u] / sqrt(D))
+ *   V[b,g,u] over the keys of the blocks active in block_mask[b,h,:] (NULL:
+ *   every block); out [B,Hq,D] in out_dtype, lse [B,Hq] (natural log) or
+ *   NULL; a head with no active block gets O = 0, LSE = -inf. With
+ *   block_mask NULL, gt (fp32 [B,Hq,nb], or NULL) receives the 1D max-pooled
+ *   map gt[b,h,j] = max_{u in block j} softmax_u(...); gt must be NULL when a
+ *   mask is given. A block no query head of a KV group selects is not read.
+ *   Hq/Hkv <= 8. workspace: seer_decode_attn_workspace_size() bytes,
+ *   16-byte aligned (per-split partial results).
+ * ---------------------------------------------------------------------- */
+seer_status seer_decode_compress_k(const seer_shape* shape, int32_t wk_per_kv_head, const void* k_cache,
+                                   const float* w_k, int32_t block_begin, float* kcomp, int32_t kcomp_blocks,
+                                   void* hip_stream);
+seer_status seer_decode_gate_fwd(const seer_shape* shape, int32_t wk_per_kv_head, const void* q,
+                                 const float* kcomp, int32_t kcomp_blocks, seer_mask_mode mode,
+                                 float threshold, int32_t topk_k, const int32_t* topk_per_head,
+                                 float* scores, uint8_t* block_mask, void* hip_stream);
+size_t seer_decode_attn_workspace_size(const seer_shape* shape);
+seer_status seer_decode_attn_fwd(const seer_shape* shape, const void* q, const void* k_cache,
+                                 const void* v_cache, const uint8_t* block_mask, void* out,
+                                 seer_dtype out_dtype, float* lse, float* gt, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics.
  * seer_status_string: static name of a status code.
  * seer_last_error: message of the last failing call on this thread ("" if

@@ -35,6 +35,7 @@ EXPORTED = (
     "seer_gate_distill_workspace_size", "seer_gate_distill_bwd",
     "seer_attn_workspace_size", "seer_block_sparse_attn_fwd",
     "seer_gt_workspace_size", "seer_attn_maxpool_gt",
+    "seer_decode_compress_k", "seer_decode_gate_fwd", "seer_decode_attn_workspace_size", "seer_decode_attn_fwd",
     "seer_status_string", "seer_last_error", "seer_version",
 )
 
@@ -80,6 +81,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.seer_gt_workspace_size.restype = sz
     lib.seer_attn_maxpool_gt.argtypes = [shp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, sz, vp]
     lib.seer_attn_maxpool_gt.restype = ctypes.c_int
+    lib.seer_decode_compress_k.argtypes = [shp, i32, vp, vp, i32, vp, i32, vp]
+    lib.seer_decode_compress_k.restype = ctypes.c_int
+    lib.seer_decode_gate_fwd.argtypes = [shp, i32, vp, vp, i32, ctypes.c_int, f32, i32, ctypes.POINTER(i32), vp, vp,
+                                         vp]
+    lib.seer_decode_gate_fwd.restype = ctypes.c_int
+    lib.seer_decode_attn_workspace_size.argtypes = [shp]
+    lib.seer_decode_attn_workspace_size.restype = sz
+    lib.seer_decode_attn_fwd.argtypes = [shp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, sz, vp]
+    lib.seer_decode_attn_fwd.restype = ctypes.c_int
     lib.seer_status_string.argtypes = [ctypes.c_int]
     lib.seer_status_string.restype = ctypes.c_char_p
     lib.seer_last_error.argtypes = []
@@ -250,6 +260,105 @@ def seer_attn_maxpool_gt(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     _check(lib.seer_attn_maxpool_gt(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(out), dt, _ptr(lse),
                                     _ptr(gt), _ptr(workspace), ws_bytes, _stream(dev)))
     return out, lse, gt
+
+
+def _topk_args(mode: str, topk, heads_q: int):
+    if mode not in ("topk", "threshold"):
+        raise ValueError(f"mode must be 'threshold' or 'topk', got {mode!r}")
+    m = SEER_MASK_TOPK if mode == "topk" else SEER_MASK_THRESHOLD
+    per_head, k_uniform = None, 0
+    if m == SEER_MASK_TOPK:
+        if topk is None:
+            raise ValueError("topk mode needs topk")
+        if isinstance(topk, int):
+            k_uniform = topk
+        else:
+            if len(topk) != heads_q:
+                raise ValueError(f"per-head topk needs {heads_q} values")
+            per_head = (ctypes.c_int32 * len(topk))(*[int(x) for x in topk])
+    return m, k_uniform, per_head
+
+
+def seer_decode_compress_k(k_cache: torch.Tensor, w_k: torch.Tensor, heads_q: int, *, wk_per_kv_head: bool = False,
+                           block_begin: int = 0, kcomp: Optional[torch.Tensor] = None,
+                           capacity_blocks: Optional[int] = None):
+    """(Re)compute the compressed K cache of blocks >= block_begin. Returns kcomp
+    [B, Hwk, capacity_blocks, D] fp32."""
+    lib = load_library()
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(w_k, "w_k", torch.float32)
+    B, Hkv, S, D = k_cache.shape
+    nb = nblocks(S)
+    hwk = Hkv if wk_per_kv_head else heads_q
+    if kcomp is None:
+        kcomp = torch.empty((B, hwk, capacity_blocks or nb, D), dtype=torch.float32, device=k_cache.device)
+    _need(kcomp, "kcomp", torch.float32)
+    shape = make_shape(B, heads_q, Hkv, S, D)
+    _check(lib.seer_decode_compress_k(ctypes.byref(shape), int(wk_per_kv_head), _ptr(k_cache), _ptr(w_k),
+                                      int(block_begin), _ptr(kcomp), int(kcomp.shape[2]), _stream(k_cache.device)))
+    return kcomp
+
+
+def seer_decode_gate_fwd(q: torch.Tensor, kcomp: torch.Tensor, seq_len: int, heads_kv: int, *,
+                         wk_per_kv_head: bool = False, mode: str = "threshold", threshold: float = 5e-4,
+                         topk: Union[int, Sequence[int], None] = None, want_scores: bool = True,
+                         scores: Optional[torch.Tensor] = None, block_mask: Optional[torch.Tensor] = None):
+    """Decode gate for one query per head. Returns (block_mask [B,Hq,nb] uint8, scores or None)."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    _need(kcomp, "kcomp", torch.float32)
+    B, Hq, D = q.shape
+    nb = nblocks(seq_len)
+    dev = q.device
+    if block_mask is None:
+        block_mask = torch.empty((B, Hq, nb), dtype=torch.uint8, device=dev)
+    if scores is None:
+        scores = torch.empty((B, Hq, nb), dtype=torch.float32, device=dev)
+    m, k_uniform, per_head = _topk_args(mode, topk, Hq)
+    shape = make_shape(B, Hq, heads_kv, seq_len, D)
+    _check(lib.seer_decode_gate_fwd(ctypes.byref(shape), int(wk_per_kv_head), _ptr(q), _ptr(kcomp),
+                                    int(kcomp.shape[2]), m, float(threshold), int(k_uniform), per_head, _ptr(scores),
+                                    _ptr(block_mask), _stream(dev)))
+    return block_mask, (scores if want_scores else None)
+
+
+def seer_decode_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         block_mask: Optional[torch.Tensor] = None, *, out: Optional[torch.Tensor] = None,
+                         out_dtype: torch.dtype = torch.bfloat16, lse: Optional[torch.Tensor] = None,
+                         want_lse: bool = False, want_gt: bool = False, gt: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None):
+    """Decode attention of one query per head over the active blocks of the
+    cache. Returns (out [B,Hq,D], lse or None, gt [B,Hq,nb] or None)."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(v_cache, "v_cache", torch.bfloat16)
+    B, Hq, D = q.shape
+    Hkv, S = k_cache.shape[1], k_cache.shape[2]
+    nb = nblocks(S)
+    dev = q.device
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8)
+        if tuple(block_mask.shape) != (B, Hq, nb):
+            raise ValueError(f"block_mask must be {(B, Hq, nb)}, got {tuple(block_mask.shape)}")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if want_gt and gt is None:
+        gt = torch.empty((B, Hq, nb), dtype=torch.float32, device=dev)
+    dt = SEER_BF16 if out.dtype == torch.bfloat16 else SEER_F32
+    shape = make_shape(B, Hq, Hkv, S, D)
+    workspace = _workspace(lib.seer_decode_attn_workspace_size(ctypes.byref(shape)), dev, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.seer_decode_attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_mask),
+                                    _ptr(out), dt, _ptr(lse), _ptr(gt), _ptr(workspace), ws_bytes, _stream(dev)))
+    return out, lse, gt
+
+
+def decode_attn_workspace_bytes(batch, heads_q, heads_kv, seq_len, head_dim) -> int:
+    shape = make_shape(batch, heads_q, heads_kv, seq_len, head_dim)
+    return load_library().seer_decode_attn_workspace_size(ctypes.byref(shape))
 
 
 def seer_gate_distill_bwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,

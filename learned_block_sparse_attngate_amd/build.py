@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB_NAME = "libseer.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["attn_kernels.hip", "gate_kernels.hip", "seer_api.hip"]
+SOURCES = ["attn_kernels.hip", "gate_kernels.hip", "decode_kernels.hip", "seer_api.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

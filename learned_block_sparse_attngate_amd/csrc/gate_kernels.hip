@@ -1,5 +1,7 @@
-// AttnGate forward for gfx950: block pooling, per-head projections, causal
-// block-level softmax and the threshold / top-k block mask.
+// AttnGate for gfx950: block pooling, per-head projections, block-level RoPE,
+// causal block-level softmax and the threshold / top-k block mask; the
+// gate's self-distillation step; and the decode-stage gate (compressed K
+// cache, per-token scores and mask).
 //
 // Method ("SeerAttention: Learning Intrinsic Sparse Attention in Your LLMs",
 // explainer section 3.4, "AttnGate" and its score equation, "Pooling Method
@@ -23,6 +25,13 @@
 //  gate_softmax_mask one workgroup per score row: max / sum reductions, the
 //                   normalized row, and either the threshold or an exact
 //                   4-pass radix select for top-k (ties to the lower index).
+//  gate_rope        in-place block-level RoPE of Q' / K' (fp64 angles).
+//  gate_kl, gate_dproj, gate_dweight, gate_loss
+//                   the distillation step: KL rows and dz, dQ' / dK' GEMMs,
+//                   weight-gradient GEMMs, fixed-order loss reduction.
+//  decode_kcomp, decode_logits, decode_gate
+//                   decode stage: pooled and projected key blocks, 8 lanes
+//                   per logit, then the row softmax and mask.
 #include <math.h>
 
 #include "seer_device.h"
@@ -238,27 +247,20 @@ __device__ __forceinline__ float block_reduce_sum(float x, float* red) {
   return r;
 }
 
-__global__ __launch_bounds__(kST) void gate_softmax_mask_kernel(GateArgs a, TopkTable tk) {
-  extern __shared__ float row[];             // nb floats
+// Softmax of the n logits in row[] (LDS; overwritten with the probabilities),
+// written to srow[0 .. nb) (0 for j >= n) unless srow is null, then the mask
+// mrow[0 .. nb): probability > threshold (mode 0) or the k largest (ties to the
+// lower index, all n if k >= n); 0 for j >= n.
+__device__ void softmax_mask_row(float* row, float* srow, uint8_t* mrow, int n, int nb, int mode, float threshold,
+                                 int k) {
   __shared__ float red[kST / kWave];
   __shared__ int hist[256];
   __shared__ int sel_state[2];
   __shared__ int scan_tmp[kST / kWave];
-
-  const int i = blockIdx.x;
-  const int z = blockIdx.y;                  // b * Hq + h
-  const int h = z % a.Hq;
   const int tid = threadIdx.x;
-  const int n = i + 1;                       // causal entries of this row
-  float* srow = a.scores + (static_cast<size_t>(z) * a.nb + i) * a.nb;
-  uint8_t* mrow = a.mask + (static_cast<size_t>(z) * a.nb + i) * a.nb;
 
   float mx = -INFINITY;
-  for (int j = tid; j < n; j += kST) {
-    const float v = srow[j];
-    row[j] = v;
-    mx = fmaxf(mx, v);
-  }
+  for (int j = tid; j < n; j += kST) mx = fmaxf(mx, row[j]);
   mx = block_reduce_max(mx, red);
   float sum = 0.f;
   for (int j = tid; j < n; j += kST) {
@@ -268,29 +270,28 @@ __global__ __launch_bounds__(kST) void gate_softmax_mask_kernel(GateArgs a, Topk
   }
   sum = block_reduce_sum(sum, red);
   const float inv = 1.0f / sum;
-  for (int j = tid; j < a.nb; j += kST) {
+  for (int j = tid; j < nb; j += kST) {
     float s = 0.f;
     if (j < n) {
       s = row[j] * inv;
       row[j] = s;
     }
-    srow[j] = s;
+    if (srow != nullptr) srow[j] = s;
   }
   __syncthreads();
 
-  if (a.mode == 0) {
-    for (int j = tid; j < a.nb; j += kST) mrow[j] = (j < n && row[j] > a.threshold) ? 1 : 0;
+  if (mode == 0) {
+    for (int j = tid; j < nb; j += kST) mrow[j] = (j < n && row[j] > threshold) ? 1 : 0;
     return;
   }
 
   // ---- top-k --------------------------------------------------------------
-  const int k = tk.k[h];
   if (k >= n) {
-    for (int j = tid; j < a.nb; j += kST) mrow[j] = j < n ? 1 : 0;
+    for (int j = tid; j < nb; j += kST) mrow[j] = j < n ? 1 : 0;
     return;
   }
-  // radix select of the k-th largest value (scores are >= 0, so their bit
-  // patterns order like the values)
+  // radix select of the k-th largest value (probabilities are >= 0, so their
+  // bit patterns order like the values)
   uint32_t prefix = 0, pmask = 0;
   int kk = k;
   const int lane = tid & 63, wave = tid >> 6;
@@ -341,7 +342,155 @@ __global__ __launch_bounds__(kST) void gate_softmax_mask_kernel(GateArgs a, Topk
     if (u == prefix) { keep = before < kk ? 1 : 0; ++before; }
     mrow[j] = keep;
   }
-  for (int j = n + tid; j < a.nb; j += kST) mrow[j] = 0;
+  for (int j = n + tid; j < nb; j += kST) mrow[j] = 0;
+}
+
+// Row i of head z: softmax over the causal logits j <= i (in place in the
+// scores buffer) and the mask row.
+__global__ __launch_bounds__(kST) void gate_softmax_mask_kernel(GateArgs a, TopkTable tk) {
+  extern __shared__ float row[];             // nb floats
+  const int i = blockIdx.x;
+  const int z = blockIdx.y;                  // b * Hq + h
+  const int n = i + 1;                       // causal entries of this row
+  float* srow = a.scores + (static_cast<size_t>(z) * a.nb + i) * a.nb;
+  for (int j = threadIdx.x; j < n; j += kST) row[j] = srow[j];
+  __syncthreads();
+  softmax_mask_row(row, srow, a.mask + (static_cast<size_t>(z) * a.nb + i) * a.nb, n, a.nb, a.mode, a.threshold,
+                   tk.k[z % a.Hq]);
+}
+
+// ---------------------------------------------------------------------------
+// Decode-stage gate ("SeerAttention: Self-distilled Attention Gating for
+// Efficient Long-context Prefilling", responses on decoding): no query
+// pooling or projection; the compressed K cache holds the keys
+// [max | min | avg]-pooled per block and projected by W_k (3D -> D).
+// ---------------------------------------------------------------------------
+// Compressed cache of blocks [block_begin, nb): one workgroup per (block,
+// batch, W_k index, 32 output columns) pools the block's (up to 64) key rows
+// of the KV head that W_k index reads, and projects the pool through its 32
+// columns of W_k (3D -> D), the 3D-long sums split into 8 row ranges with
+// eight independent accumulators each so many loads are in flight.
+constexpr int kKcompCols = 32;
+template <int D>
+__global__ __launch_bounds__(256) void decode_kcomp_kernel(DecodeGateArgs a) {
+  constexpr int NV = D / 8;                  // pooling: groups of 8 dims (16-byte loads)
+  constexpr int P = 256 / NV;                // pooling: token parts
+  constexpr int TPT = kBlock / P;            // pooling: tokens per thread
+  constexpr int RP = 256 / kKcompCols;       // row ranges of the projection
+  constexpr int RR = 3 * D / RP;             // rows per range
+  __shared__ float red[3][P][D];
+  __shared__ float kp[3 * D];
+  __shared__ float part_s[RP][kKcompCols];
+  const int j = a.block_begin + blockIdx.x;
+  const int hwk = a.wk_per_kv ? a.Hkv : a.Hq;
+  const int b = blockIdx.y / hwk, w = blockIdx.y - b * hwk;
+  const int g = a.wk_per_kv ? w : w / a.group;
+  const int n0 = blockIdx.z * kKcompCols;
+  const int tid = threadIdx.x;
+  {
+    const int dg = tid % NV, part = tid / NV;
+    const int t0 = j * kBlock, n_tok = min(kBlock, a.S - t0);
+    const uint16_t* kr = a.k + ((static_cast<size_t>(b) * a.Hkv + g) * a.S + t0) * D + dg * 8;
+    uint4 raw[TPT];
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {            // all loads issued before use
+      const int u = part + P * i;
+      raw[i] = u < n_tok ? *reinterpret_cast<const uint4*>(kr + static_cast<size_t>(u) * D) : make_uint4(0, 0, 0, 0);
+    }
+    float mx[8], mn[8], sm[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { mx[e] = -INFINITY; mn[e] = INFINITY; sm[e] = 0.f; }
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      if (part + P * i >= n_tok) continue;
+      const uint32_t wv[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = __uint_as_float((e & 1) ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16));
+        mx[e] = fmaxf(mx[e], x);
+        mn[e] = fminf(mn[e], x);
+        sm[e] += x;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      red[0][part][dg * 8 + e] = mx[e];
+      red[1][part][dg * 8 + e] = mn[e];
+      red[2][part][dg * 8 + e] = sm[e];
+    }
+    __syncthreads();
+    if (tid < D) {
+      float x0 = -INFINITY, x1 = INFINITY, x2 = 0.f;
+      for (int p2 = 0; p2 < P; ++p2) {
+        x0 = fmaxf(x0, red[0][p2][tid]);
+        x1 = fminf(x1, red[1][p2][tid]);
+        x2 += red[2][p2][tid];
+      }
+      kp[tid] = x0;
+      kp[D + tid] = x1;
+      kp[2 * D + tid] = x2 / static_cast<float>(n_tok);
+    }
+    __syncthreads();
+  }
+  const int col = tid % kKcompCols, rp = tid / kKcompCols;
+  const float* wk = a.wk + static_cast<size_t>(w) * 3 * D * D + n0 + col;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int r0 = rp * RR;
+#pragma unroll
+  for (int r = 0; r < RR; r += 8)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(kp[r0 + r + e], wk[static_cast<size_t>(r0 + r + e) * D], acc[e]);
+  part_s[rp][col] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  __syncthreads();
+  if (tid < kKcompCols) {
+    float t = 0.f;
+#pragma unroll
+    for (int p2 = 0; p2 < RP; ++p2) t += part_s[p2][tid];
+    a.kcomp[((static_cast<size_t>(b) * hwk + w) * a.kcomp_blocks + j) * D + n0 + tid] = t;
+  }
+}
+
+// Decode gate logits: 8 lanes per block (16-byte loads, 3 shuffle steps),
+// 32 blocks per workgroup; workgroup (x, z) covers blocks 32x .. 32x+31 of
+// query head z.
+constexpr int kLogitBlocks = 32;
+__global__ __launch_bounds__(256) void decode_logits_kernel(DecodeGateArgs a) {
+  const int z = blockIdx.y;                  // b * Hq + h
+  const int b = z / a.Hq, h = z - b * a.Hq;
+  const int hwk = a.wk_per_kv ? a.Hkv : a.Hq;
+  const int w = a.wk_per_kv ? h / a.group : h;
+  const int sub = threadIdx.x & 7;           // lane within the block's 8
+  const int j = blockIdx.x * kLogitBlocks + (threadIdx.x >> 3);
+  const int dpl = a.D / 8;                   // dims per lane: 8 or 16
+  float acc = 0.f;
+  if (j < a.nb) {
+    const float4* kr = reinterpret_cast<const float4*>(
+        a.kcomp + ((static_cast<size_t>(b) * hwk + w) * a.kcomp_blocks + j) * a.D + sub * dpl);
+    const uint16_t* qr = a.q + static_cast<size_t>(z) * a.D + sub * dpl;
+    for (int i = 0; i < dpl / 4; ++i) {
+      const float4 v = kr[i];
+      acc = fmaf(v.x, bf16_to_f32(qr[4 * i]), acc);
+      acc = fmaf(v.y, bf16_to_f32(qr[4 * i + 1]), acc);
+      acc = fmaf(v.z, bf16_to_f32(qr[4 * i + 2]), acc);
+      acc = fmaf(v.w, bf16_to_f32(qr[4 * i + 3]), acc);
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (sub == 0 && j < a.nb) a.scores[static_cast<size_t>(z) * a.nb + j] = acc * a.scale;
+}
+
+// One workgroup per (batch, query head): softmax over every block, in place,
+// and the mask.
+__global__ __launch_bounds__(kST) void decode_gate_kernel(DecodeGateArgs a, TopkTable tk) {
+  extern __shared__ float row[];             // nb floats
+  const int z = blockIdx.x;                  // b * Hq + h
+  float* srow = a.scores + static_cast<size_t>(z) * a.nb;
+  for (int j = threadIdx.x; j < a.nb; j += kST) row[j] = srow[j];
+  __syncthreads();
+  softmax_mask_row(row, srow, a.mask + static_cast<size_t>(z) * a.nb, a.nb, a.nb, a.mode, a.threshold,
+                   tk.k[z % a.Hq]);
 }
 
 // ---------------------------------------------------------------------------
@@ -525,6 +674,23 @@ hipError_t launch_gate(const GateArgs& a, const TopkTable& tk, hipStream_t st) {
   if (e != hipSuccess) return e;
   dim3 gs(a.nb, a.B * a.Hq);
   hipLaunchKernelGGL(gate_softmax_mask_kernel, gs, dim3(kST), static_cast<size_t>(a.nb) * sizeof(float), st, a, tk);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_kcomp(const DecodeGateArgs& a, hipStream_t st) {
+  dim3 g(a.nb - a.block_begin, a.B * (a.wk_per_kv ? a.Hkv : a.Hq), a.D / kKcompCols);
+  if (a.D == 64) hipLaunchKernelGGL(decode_kcomp_kernel<64>, g, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(decode_kcomp_kernel<128>, g, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_gate(const DecodeGateArgs& a, const TopkTable& tk, hipStream_t st) {
+  hipLaunchKernelGGL(decode_logits_kernel, dim3((a.nb + kLogitBlocks - 1) / kLogitBlocks, a.B * a.Hq), dim3(256), 0,
+                     st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_gate_kernel, dim3(a.B * a.Hq), dim3(kST), static_cast<size_t>(a.nb) * sizeof(float), st,
+                     a, tk);
   return hipGetLastError();
 }
 

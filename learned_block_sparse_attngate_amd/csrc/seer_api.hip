@@ -163,6 +163,33 @@ DistillLayout distill_layout(const seer_shape* s, int dg, int wk_per_kv) {
   return L;
 }
 
+seer_status fill_topk(const seer_shape* shape, seer_mask_mode mode, int32_t topk_k, const int32_t* topk_per_head,
+                      seer::TopkTable* tk) {
+  if (mode != SEER_MASK_TOPK) return SEER_OK;
+  if (shape->heads_q > seer::kMaxTopkHeads)
+    return fail(SEER_ERR_UNSUPPORTED, "top-k supports at most %d query heads", seer::kMaxTopkHeads);
+  for (int h = 0; h < shape->heads_q; ++h) {
+    const int kv = topk_per_head ? topk_per_head[h] : topk_k;
+    if (kv < 1) return fail(SEER_ERR_INVALID_ARG, "top-k value %d (head %d) must be >= 1", kv, h);
+    tk->k[h] = kv;
+  }
+  return SEER_OK;
+}
+
+seer::DecodeGateArgs decode_gate_args(const seer_shape* s, int wk_per_kv_head) {
+  seer::DecodeGateArgs a{};
+  a.B = s->batch;
+  a.Hq = s->heads_q;
+  a.Hkv = s->heads_kv;
+  a.S = s->seq_len;
+  a.D = s->head_dim;
+  a.nb = static_cast<int>(nblocks(s));
+  a.group = s->heads_kv > 0 ? s->heads_q / s->heads_kv : 1;
+  a.wk_per_kv = wk_per_kv_head != 0;
+  a.scale = static_cast<float>(1.0 / sqrt(static_cast<double>(s->head_dim)));
+  return a;
+}
+
 seer_status check_rope(float rope_theta) {
   if (!isfinite(rope_theta) || rope_theta < 0.f)
     return fail(SEER_ERR_INVALID_ARG, "rope_theta must be 0 (no RoPE) or a finite positive base (got %g)",
@@ -213,15 +240,7 @@ seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_
     return fail(SEER_ERR_INVALID_ARG, "threshold must be finite");
   if ((st = check_rope(rope_theta)) != SEER_OK) return st;
   seer::TopkTable tk{};
-  if (mode == SEER_MASK_TOPK) {
-    if (shape->heads_q > seer::kMaxTopkHeads)
-      return fail(SEER_ERR_UNSUPPORTED, "top-k supports at most %d query heads", seer::kMaxTopkHeads);
-    for (int h = 0; h < shape->heads_q; ++h) {
-      const int kv = topk_per_head ? topk_per_head[h] : topk_k;
-      if (kv < 1) return fail(SEER_ERR_INVALID_ARG, "top-k value %d (head %d) must be >= 1", kv, h);
-      tk.k[h] = kv;
-    }
-  }
+  if ((st = fill_topk(shape, mode, topk_k, topk_per_head, &tk)) != SEER_OK) return st;
   if (nblocks(shape) > kMaxNbGate)
     return fail(SEER_ERR_UNSUPPORTED, "the gate supports at most %d blocks per sequence", kMaxNbGate);
   if (empty) return ok();
@@ -264,6 +283,124 @@ seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_
   a.rope_base = rope_theta > 0.f ? static_cast<double>(rope_theta) / shape->block : 0.0;
   hipError_t e = seer::launch_gate(a, tk, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SEER_ERR_HIP, "gate launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+seer_status seer_decode_compress_k(const seer_shape* shape, int32_t wk_per_kv_head, const void* k_cache,
+                                   const float* w_k, int32_t block_begin, float* kcomp, int32_t kcomp_blocks,
+                                   void* hip_stream) {
+  bool empty = false;
+  seer_status st = check_shape(shape, &empty);
+  if (st != SEER_OK) return st;
+  const int nb = static_cast<int>(nblocks(shape));
+  if (block_begin < 0 || block_begin > nb)
+    return fail(SEER_ERR_INVALID_ARG, "block_begin %d outside [0, %d]", block_begin, nb);
+  if (kcomp_blocks < nb)
+    return fail(SEER_ERR_INVALID_ARG, "kcomp_blocks (%d) is smaller than the cache's %d blocks", kcomp_blocks, nb);
+  if (empty || block_begin == nb) return ok();
+  if (k_cache == nullptr || !aligned(k_cache, 16))
+    return fail(SEER_ERR_INVALID_ARG, "k_cache must be a non-NULL, 16-byte aligned device pointer");
+  if (w_k == nullptr || kcomp == nullptr || !aligned(kcomp, 16))
+    return fail(SEER_ERR_INVALID_ARG, "w_k and kcomp must be non-NULL (kcomp 16-byte aligned)");
+  if ((st = check_device()) != SEER_OK) return st;
+  seer::DecodeGateArgs a = decode_gate_args(shape, wk_per_kv_head);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.wk = w_k;
+  a.kcomp = kcomp;
+  a.kcomp_blocks = kcomp_blocks;
+  a.block_begin = block_begin;
+  hipError_t e = seer::launch_decode_kcomp(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SEER_ERR_HIP, "decode K compression launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+seer_status seer_decode_gate_fwd(const seer_shape* shape, int32_t wk_per_kv_head, const void* q, const float* kcomp,
+                                 int32_t kcomp_blocks, seer_mask_mode mode, float threshold, int32_t topk_k,
+                                 const int32_t* topk_per_head, float* scores, uint8_t* block_mask,
+                                 void* hip_stream) {
+  bool empty = false;
+  seer_status st = check_shape(shape, &empty);
+  if (st != SEER_OK) return st;
+  if (mode != SEER_MASK_THRESHOLD && mode != SEER_MASK_TOPK)
+    return fail(SEER_ERR_INVALID_ARG, "mask mode %d is not SEER_MASK_THRESHOLD/SEER_MASK_TOPK", mode);
+  if (mode == SEER_MASK_THRESHOLD && !isfinite(threshold))
+    return fail(SEER_ERR_INVALID_ARG, "threshold must be finite");
+  seer::TopkTable tk{};
+  if ((st = fill_topk(shape, mode, topk_k, topk_per_head, &tk)) != SEER_OK) return st;
+  const int nb = static_cast<int>(nblocks(shape));
+  if (nb > kMaxNbGate) return fail(SEER_ERR_UNSUPPORTED, "the gate supports at most %d blocks", kMaxNbGate);
+  if (kcomp_blocks < nb)
+    return fail(SEER_ERR_INVALID_ARG, "kcomp_blocks (%d) is smaller than the cache's %d blocks", kcomp_blocks, nb);
+  if (empty) return ok();
+  if (q == nullptr || kcomp == nullptr || block_mask == nullptr || scores == nullptr || !aligned(kcomp, 16))
+    return fail(SEER_ERR_INVALID_ARG, "q, kcomp (16-byte aligned), scores and block_mask must be non-NULL");
+  if (!aligned(scores, 4)) return fail(SEER_ERR_INVALID_ARG, "scores must be 4-byte aligned");
+  if ((st = check_device()) != SEER_OK) return st;
+  seer::DecodeGateArgs a = decode_gate_args(shape, wk_per_kv_head);
+  a.q = static_cast<const uint16_t*>(q);
+  a.kcomp = const_cast<float*>(kcomp);
+  a.kcomp_blocks = kcomp_blocks;
+  a.scores = scores;
+  a.mask = block_mask;
+  a.mode = mode == SEER_MASK_TOPK ? 1 : 0;
+  a.threshold = threshold;
+  hipError_t e = seer::launch_decode_gate(a, tk, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SEER_ERR_HIP, "decode gate launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t seer_decode_attn_workspace_size(const seer_shape* shape) {
+  bool empty = false;
+  if (check_shape(shape, &empty) != SEER_OK || empty) return 0;
+  int nsplit = 1, bps = 1;
+  seer::decode_split(shape->batch, shape->heads_kv, static_cast<int>(nblocks(shape)), &nsplit, &bps);
+  return static_cast<size_t>(shape->batch) * shape->heads_q * nsplit * (shape->head_dim + 2) * sizeof(float);
+}
+
+seer_status seer_decode_attn_fwd(const seer_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                                 const uint8_t* block_mask, void* out, seer_dtype out_dtype, float* lse, float* gt,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+  bool empty = false;
+  seer_status st = check_shape(shape, &empty);
+  if (st != SEER_OK) return st;
+  if (out_dtype != SEER_F32 && out_dtype != SEER_BF16)
+    return fail(SEER_ERR_INVALID_ARG, "out_dtype %d is not SEER_F32/SEER_BF16", out_dtype);
+  if (shape->heads_q > 0 && shape->heads_q / shape->heads_kv > seer::kDecodeMaxGroup)
+    return fail(SEER_ERR_UNSUPPORTED, "decode attention supports at most %d query heads per KV head",
+                seer::kDecodeMaxGroup);
+  if (gt != nullptr && block_mask != nullptr)
+    return fail(SEER_ERR_INVALID_ARG, "the 1D max-pooled map (gt) is produced only in dense mode (block_mask NULL)");
+  if (empty) return ok();
+  if ((st = check_qkv(q, k_cache, v_cache)) != SEER_OK) return st;
+  if ((st = check_out(out, out_dtype, lse)) != SEER_OK) return st;
+  if (gt != nullptr && !aligned(gt, 4)) return fail(SEER_ERR_INVALID_ARG, "gt must be 4-byte aligned");
+  const size_t need = seer_decode_attn_workspace_size(shape);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
+    return fail(SEER_ERR_WORKSPACE, "workspace must be %zu bytes, 16-byte aligned (got %zu at %p)", need,
+                workspace_bytes, workspace);
+  if ((st = check_device()) != SEER_OK) return st;
+  seer::DecodeAttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.mask = block_mask;
+  a.out = out;
+  a.lse = lse;
+  a.gt = gt;
+  a.part = static_cast<float*>(workspace);
+  a.B = shape->batch;
+  a.Hq = shape->heads_q;
+  a.Hkv = shape->heads_kv;
+  a.S = shape->seq_len;
+  a.D = shape->head_dim;
+  a.nb = static_cast<int>(nblocks(shape));
+  a.group = shape->heads_q / shape->heads_kv;
+  a.out_bf16 = out_dtype == SEER_BF16;
+  a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(shape->head_dim)));
+  seer::decode_split(a.B, a.Hkv, a.nb, &a.nsplit, &a.bps);
+  hipError_t e = seer::launch_decode_attn(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SEER_ERR_HIP, "decode attention launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

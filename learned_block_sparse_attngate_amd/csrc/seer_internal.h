@@ -73,6 +73,45 @@ struct TopkTable {
 };
 
 hipError_t launch_gate(const GateArgs& a, const TopkTable& tk, hipStream_t st);
+
+// Decode-stage gate: compressed K cache and per-token gate.
+struct DecodeGateArgs {
+  const uint16_t* q;   // bf16 [B,Hq,D], one query per head
+  const uint16_t* k;   // bf16 [B,Hkv,S,D] key cache
+  const float* wk;     // [Hwk,3D,D]
+  float* kcomp;        // [B,Hwk,kcomp_blocks,D] compressed (pooled, projected) keys
+  float* scores;       // [B,Hq,nb] or null
+  uint8_t* mask;       // [B,Hq,nb]
+  int B, Hq, Hkv, S, D, nb, group;
+  int wk_per_kv;       // 1: Hwk = Hkv, 0: Hwk = Hq
+  int kcomp_blocks;    // block capacity (row stride) of kcomp
+  int block_begin;     // first block to (re)compute in the compressed cache
+  float scale;         // 1/sqrt(D)
+  int mode;            // 0 threshold, 1 top-k
+  float threshold;
+};
+hipError_t launch_decode_kcomp(const DecodeGateArgs& a, hipStream_t st);
+hipError_t launch_decode_gate(const DecodeGateArgs& a, const TopkTable& tk, hipStream_t st);
+
+// Decode attention: one query per head against the key/value cache, reading
+// only the blocks some head of the KV group selects.
+constexpr int kDecodeMaxGroup = 8;
+struct DecodeAttnArgs {
+  const uint16_t* q;   // bf16 [B,Hq,D]
+  const uint16_t* k;   // bf16 [B,Hkv,S,D]
+  const uint16_t* v;   // bf16 [B,Hkv,S,D]
+  const uint8_t* mask; // [B,Hq,nb] or null (every block)
+  void* out;           // [B,Hq,D] fp32 or bf16
+  float* lse;          // [B,Hq] or null
+  float* gt;           // [B,Hq,nb] 1D max-pooled map or null (dense mode only)
+  float* part;         // [B*Hq][nsplit][D + 2] partial (acc, max, sum) per key split
+  int B, Hq, Hkv, S, D, nb, group;
+  int nsplit, bps;     // key splits and blocks per split
+  int out_bf16;
+  float scale_log2;    // log2(e) / sqrt(D)
+};
+hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t st);
+void decode_split(int B, int Hkv, int nb, int* nsplit, int* bps);
 hipError_t launch_gate_distill(const GateArgs& a, hipStream_t st);
 
 }  // namespace seer

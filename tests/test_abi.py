@@ -133,6 +133,36 @@ def test_distill_workspace_size():
     assert lib.seer_gate_distill_workspace_size(ctypes.byref(s), 32, 0) == want
 
 
+def test_decode_validation():
+    lib = _lib()
+    s = _shape(hq=4, hkv=2, s=1000)                 # 16 blocks
+    assert lib.seer_decode_compress_k(ctypes.byref(s), 0, FAKE, FAKE, -1, FAKE, 16, None) == B.SEER_ERR_INVALID_ARG
+    assert lib.seer_decode_compress_k(ctypes.byref(s), 0, FAKE, FAKE, 17, FAKE, 16, None) == B.SEER_ERR_INVALID_ARG
+    assert lib.seer_decode_compress_k(ctypes.byref(s), 0, FAKE, FAKE, 0, FAKE, 15, None) == B.SEER_ERR_INVALID_ARG
+    assert b"kcomp_blocks" in lib.seer_last_error()
+    assert lib.seer_decode_compress_k(ctypes.byref(s), 0, FAKE, FAKE, 16, FAKE, 16, None) == B.SEER_OK  # nothing to do
+    assert lib.seer_decode_gate_fwd(ctypes.byref(s), 0, FAKE, FAKE, 16, 7, 0.1, 1, None, None, FAKE,
+                                    None) == B.SEER_ERR_INVALID_ARG
+    assert lib.seer_decode_gate_fwd(ctypes.byref(s), 0, FAKE, FAKE, 16, B.SEER_MASK_TOPK, 0.1, 0, None, None, FAKE,
+                                    None) == B.SEER_ERR_INVALID_ARG
+    assert lib.seer_decode_gate_fwd(ctypes.byref(s), 0, FAKE, FAKE, 16, B.SEER_MASK_THRESHOLD, 0.1, 1, None, FAKE,
+                                    None, None) == B.SEER_ERR_INVALID_ARG
+    assert lib.seer_decode_gate_fwd(ctypes.byref(s), 0, FAKE, FAKE, 16, B.SEER_MASK_THRESHOLD, 0.1, 1, None, None,
+                                    FAKE, None) == B.SEER_ERR_INVALID_ARG          # scores hold the logits
+    big = _shape(hq=32, hkv=2, s=1000)              # 16 query heads per KV head
+    need = lib.seer_decode_attn_workspace_size(ctypes.byref(s))
+    assert need > 0
+    args = (FAKE, FAKE, FAKE, None, FAKE, B.SEER_F32, None, None, FAKE, need, None)
+    assert lib.seer_decode_attn_fwd(ctypes.byref(big), *args) == B.SEER_ERR_UNSUPPORTED
+    assert lib.seer_decode_attn_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, B.SEER_F32, None, FAKE, FAKE,
+                                    need, None) == B.SEER_ERR_INVALID_ARG          # gt with a mask
+    assert lib.seer_decode_attn_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, B.SEER_F32, None, None, FAKE,
+                                    need - 1, None) == B.SEER_ERR_WORKSPACE
+    # partials: one (D + 2)-float record per query head and key split
+    splits = need // (4 * 4 * (128 + 2))
+    assert need == 4 * 4 * splits * (128 + 2) and 1 <= splits <= 16
+
+
 def test_gate_validation():
     s = _shape()
     assert _gate(s, dg=100) == B.SEER_ERR_UNSUPPORTED
