@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--no-train", action="store_true",
                     help="skip timing the ground-truth kernel and the gate's distillation step")
     ap.add_argument("--no-decode", action="store_true", help="skip timing the decode stage")
+    ap.add_argument("--no-varlen", action="store_true", help="skip timing a packed varlen batch")
     ap.add_argument("--rope-theta", type=float, default=5e5,
                     help="RoPE base for the gate's block-level RoPE (0: none); Llama-3.1 uses 500000")
     ap.add_argument("--copy-gib", type=float, default=0.0,
@@ -160,6 +161,49 @@ def bench_decode(seer, torch, q, k, v, shape, stream, seed, reps: int = 50):
                          "frac": round(sparse_bytes / sparse_us / 1e3 / PEAK_HBM_GBS, 4),
                          "bytes_per_call": sparse_bytes},
             "dense_roofline_frac": round(dense_bytes / dense_us / 1e3 / PEAK_HBM_GBS, 4)}
+
+
+def bench_varlen(seer, torch, dev, stream, seed, reps: int = 5):
+    """A packed batch of 8 Llama-3.1-8B-shaped sequences of seeded lengths in
+    [4k, 32k] tokens (no padding), each with its own 90%-sparse seeded block
+    mask, through the varlen block-sparse attention; TFLOP/s on executed tiles."""
+    import synth
+    rng = np.random.Generator(np.random.PCG64(seed + 300))
+    lens = [int(x) for x in rng.integers(4096, 32769, size=8)]
+    cu = [0] + [int(x) for x in np.cumsum(lens)]
+    Hq, Hkv, D = 32, 8, 128
+    T = cu[-1]
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 301)
+    q = torch.randn((Hq, T, D), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((Hkv, T, D), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((Hkv, T, D), generator=g, device=dev).to(torch.bfloat16)
+    masks, tiles = [], 0
+    for i, n in enumerate(lens):
+        sh = synth.Shape(1, Hq, Hkv, n, D)
+        m = synth.gen_block_mask(sh, seed + 310 + i, 0.9).mask[0]
+        nb = sh.nb
+        tiles += int(np.count_nonzero(np.tril(np.ones((nb, nb), dtype=bool))[None] & m.astype(bool)))
+        masks.append(m.reshape(-1))
+    mask = torch.from_numpy(np.concatenate(masks)).to(dev)
+    out = torch.empty((Hq, T, D), dtype=torch.bfloat16, device=dev)
+
+    def run():
+        seer.seer_block_sparse_attn_varlen_fwd(q, k, v, cu, mask, out=out)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tflops = tiles * 4.0 * 64 * 64 * D / ms / 1e9
+    print(f"[bench] varlen: {len(lens)} sequences, {T} tokens, block-sparse attention {ms:.3f} ms "
+          f"({tflops:.1f} TFLOP/s on executed tiles)", file=sys.stderr, flush=True)
+    return {"workload": f"packed batch of 8 sequences, lengths {lens}, 90% sparse masks", "tokens": T,
+            "sparse_attention_ms": round(ms, 4), "executed_tiles": tiles, "tflops": round(tflops, 2)}
 
 
 def topk_for_sparsity(nb: int, s: float) -> int:
@@ -344,6 +388,10 @@ def main():
     if not args.no_decode:
         decode = bench_decode(seer, torch, q, k, v, shape, stream, w["seed"])
 
+    varlen = None
+    if not args.no_varlen:
+        varlen = bench_varlen(seer, torch, dev, stream, w["seed"])
+
     ms_step = float(np.mean(step_ms))
     attn_avg = float(np.mean(attn_ms))
     gate_avg = float(np.mean(gate_ms))
@@ -381,6 +429,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(args.workload)},
         "decode": decode,
+        "varlen": varlen,
         "peak_computed": computed_peak(),
         "wall_s_timed": round(wall, 3),
     }

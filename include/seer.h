@@ -244,6 +244,51 @@ seer_status seer_decode_attn_fwd(const seer_shape* shape, const void* q, const v
                                  size_t workspace_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * Varlen (packed) prefill batches ([R], on batching: variable-length inputs
+ * are packed along the sequence dimension, hiding the batch in the sequence
+ * length).
+ *
+ * num_seqs sequences are packed without padding: sequence i is tokens
+ * cu_seqlens[i] .. cu_seqlens[i+1]-1 of T = cu_seqlens[num_seqs] tokens.
+ * Tensors are head-major over the packed tokens: q [Hq,T,D], k and v
+ * [Hkv,T,D] bf16; out [Hq,T,D]; lse [Hq,T]. Each sequence keeps its own
+ * 64-token blocks (the gate never pools across sequences, attention never
+ * crosses them), so its block maps (scores, mask, gt) are [Hq,nb_i,nb_i],
+ * nb_i = ceil(len_i / 64), stored one after another: sequence i's map starts
+ * at element sum_{i'<i} Hq * nb_i'^2 (seer_varlen_map_elements() gives the
+ * total). Every call computes exactly what the batch-1 call computes on each
+ * sequence alone. The sequences run one after another on hip_stream and share
+ * the workspace, whose size is the largest any sequence needs. All sequences
+ * are validated before anything is enqueued. Empty sequences are allowed.
+ * ---------------------------------------------------------------------- */
+typedef struct seer_varlen {
+  int32_t num_seqs;
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t head_dim;
+  int32_t block;                /* must be 64 */
+  const int32_t* cu_seqlens;    /* HOST array of num_seqs + 1 non-decreasing offsets, cu_seqlens[0] = 0 */
+} seer_varlen;
+
+size_t seer_varlen_map_elements(const seer_varlen* vl);
+size_t seer_gate_varlen_workspace_size(const seer_varlen* vl, int32_t gate_dim, int32_t wk_per_kv_head,
+                                       int32_t want_scores);
+seer_status seer_gate_varlen_fwd(const seer_varlen* vl, int32_t gate_dim, int32_t wk_per_kv_head,
+                                 float rope_theta, const void* q, const void* k, const float* w_q,
+                                 const float* w_k, seer_mask_mode mode, float threshold, int32_t topk_k,
+                                 const int32_t* topk_per_head, float* scores, uint8_t* block_mask,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream);
+size_t seer_attn_varlen_workspace_size(const seer_varlen* vl);
+seer_status seer_block_sparse_attn_varlen_fwd(const seer_varlen* vl, const void* q, const void* k,
+                                              const void* v, const uint8_t* block_mask, void* out,
+                                              seer_dtype out_dtype, float* lse, void* workspace,
+                                              size_t workspace_bytes, void* hip_stream);
+size_t seer_gt_varlen_workspace_size(const seer_varlen* vl);
+seer_status seer_attn_maxpool_gt_varlen(const seer_varlen* vl, const void* q, const void* k, const void* v,
+                                        void* out, seer_dtype out_dtype, float* lse, float* gt,
+                                        void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics.
  * seer_status_string: static name of a status code.
  * seer_last_error: message of the last failing call on this thread ("" if

@@ -36,6 +36,9 @@ EXPORTED = (
     "seer_attn_workspace_size", "seer_block_sparse_attn_fwd",
     "seer_gt_workspace_size", "seer_attn_maxpool_gt",
     "seer_decode_compress_k", "seer_decode_gate_fwd", "seer_decode_attn_workspace_size", "seer_decode_attn_fwd",
+    "seer_varlen_map_elements", "seer_gate_varlen_workspace_size", "seer_gate_varlen_fwd",
+    "seer_attn_varlen_workspace_size", "seer_block_sparse_attn_varlen_fwd", "seer_gt_varlen_workspace_size",
+    "seer_attn_maxpool_gt_varlen",
     "seer_status_string", "seer_last_error", "seer_version",
 )
 
@@ -43,6 +46,11 @@ EXPORTED = (
 class SeerShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
                 ("seq_len", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32)]
+
+
+class SeerVarlen(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32), ("cu_seqlens", ctypes.POINTER(ctypes.c_int32))]
 
 
 class SeerError(RuntimeError):
@@ -90,6 +98,22 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.seer_decode_attn_workspace_size.restype = sz
     lib.seer_decode_attn_fwd.argtypes = [shp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, sz, vp]
     lib.seer_decode_attn_fwd.restype = ctypes.c_int
+    vlp = ctypes.POINTER(SeerVarlen)
+    lib.seer_varlen_map_elements.argtypes = [vlp]
+    lib.seer_varlen_map_elements.restype = sz
+    lib.seer_gate_varlen_workspace_size.argtypes = [vlp, i32, i32, i32]
+    lib.seer_gate_varlen_workspace_size.restype = sz
+    lib.seer_gate_varlen_fwd.argtypes = [vlp, i32, i32, f32, vp, vp, vp, vp, ctypes.c_int, f32, i32,
+                                         ctypes.POINTER(i32), vp, vp, vp, sz, vp]
+    lib.seer_gate_varlen_fwd.restype = ctypes.c_int
+    lib.seer_attn_varlen_workspace_size.argtypes = [vlp]
+    lib.seer_attn_varlen_workspace_size.restype = sz
+    lib.seer_block_sparse_attn_varlen_fwd.argtypes = [vlp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, sz, vp]
+    lib.seer_block_sparse_attn_varlen_fwd.restype = ctypes.c_int
+    lib.seer_gt_varlen_workspace_size.argtypes = [vlp]
+    lib.seer_gt_varlen_workspace_size.restype = sz
+    lib.seer_attn_maxpool_gt_varlen.argtypes = [vlp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, sz, vp]
+    lib.seer_attn_maxpool_gt_varlen.restype = ctypes.c_int
     lib.seer_status_string.argtypes = [ctypes.c_int]
     lib.seer_status_string.restype = ctypes.c_char_p
     lib.seer_last_error.argtypes = []
@@ -353,6 +377,123 @@ def seer_decode_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.seer_decode_attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_mask),
                                     _ptr(out), dt, _ptr(lse), _ptr(gt), _ptr(workspace), ws_bytes, _stream(dev)))
+    return out, lse, gt
+
+
+def make_varlen(cu_seqlens: Sequence[int], heads_q: int, heads_kv: int, head_dim: int, block: int = BLOCK):
+    """Varlen descriptor; the returned object keeps the host offsets alive."""
+    arr = (ctypes.c_int32 * len(cu_seqlens))(*[int(x) for x in cu_seqlens])
+    vl = SeerVarlen(len(cu_seqlens) - 1, heads_q, heads_kv, head_dim, block, arr)
+    vl._keep = arr
+    return vl
+
+
+def varlen_map_offsets(cu_seqlens: Sequence[int], heads_q: int):
+    """Element offset of each sequence's [Hq, nb_i, nb_i] block map, and the total."""
+    offs, n = [], 0
+    for a, b in zip(cu_seqlens[:-1], cu_seqlens[1:]):
+        offs.append(n)
+        nb = nblocks(b - a)
+        n += heads_q * nb * nb
+    return offs, n
+
+
+def seer_gate_varlen_fwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                         cu_seqlens: Sequence[int], *, mode: str = "threshold", threshold: float = 5e-4,
+                         topk: Union[int, Sequence[int], None] = None, wk_per_kv_head: bool = False,
+                         rope_theta: float = 0.0, want_scores: bool = True, scores: Optional[torch.Tensor] = None,
+                         block_mask: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Gate of a packed batch (q [Hq,T,D], k [Hkv,T,D]). Returns (block_mask, scores or None),
+    each sequence's [Hq, nb_i, nb_i] map concatenated (see varlen_map_offsets)."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16)
+    _need(w_q, "w_q", torch.float32)
+    _need(w_k, "w_k", torch.float32)
+    Hq, T, D = q.shape
+    Hkv = k.shape[0]
+    Dg = w_q.shape[-1]
+    if int(cu_seqlens[-1]) != T:
+        raise ValueError(f"cu_seqlens[-1] ({cu_seqlens[-1]}) must equal the packed length {T}")
+    vl = make_varlen(cu_seqlens, Hq, Hkv, D)
+    dev = q.device
+    n_map = lib.seer_varlen_map_elements(ctypes.byref(vl))
+    if block_mask is None:
+        block_mask = torch.empty(n_map, dtype=torch.uint8, device=dev)
+    if want_scores and scores is None:
+        scores = torch.empty(n_map, dtype=torch.float32, device=dev)
+    if not want_scores:
+        scores = None
+    m, k_uniform, per_head = _topk_args(mode, topk, Hq)
+    nbytes = lib.seer_gate_varlen_workspace_size(ctypes.byref(vl), Dg, int(wk_per_kv_head), int(scores is not None))
+    workspace = _workspace(nbytes, dev, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.seer_gate_varlen_fwd(ctypes.byref(vl), Dg, int(wk_per_kv_head), float(rope_theta), _ptr(q), _ptr(k),
+                                    _ptr(w_q), _ptr(w_k), m, float(threshold), int(k_uniform), per_head, _ptr(scores),
+                                    _ptr(block_mask), _ptr(workspace), ws_bytes, _stream(dev)))
+    return block_mask, scores
+
+
+def seer_block_sparse_attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Sequence[int],
+                                      block_mask: Optional[torch.Tensor] = None, *,
+                                      out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                                      lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                                      workspace: Optional[torch.Tensor] = None):
+    """Causal GQA block-sparse attention of a packed batch (block_mask None: dense).
+    Returns (out [Hq,T,D], lse [Hq,T] or None)."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16)
+    _need(v, "v", torch.bfloat16)
+    Hq, T, D = q.shape
+    Hkv = k.shape[0]
+    if int(cu_seqlens[-1]) != T:
+        raise ValueError(f"cu_seqlens[-1] ({cu_seqlens[-1]}) must equal the packed length {T}")
+    vl = make_varlen(cu_seqlens, Hq, Hkv, D)
+    dev = q.device
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8)
+        if block_mask.numel() < lib.seer_varlen_map_elements(ctypes.byref(vl)):
+            raise ValueError("block_mask is smaller than the concatenated per-sequence maps")
+    if out is None:
+        out = torch.empty((Hq, T, D), dtype=out_dtype, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    dt = SEER_BF16 if out.dtype == torch.bfloat16 else SEER_F32
+    ws_need = lib.seer_attn_varlen_workspace_size(ctypes.byref(vl)) if block_mask is not None else 0
+    workspace = _workspace(ws_need, dev, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.seer_block_sparse_attn_varlen_fwd(ctypes.byref(vl), _ptr(q), _ptr(k), _ptr(v), _ptr(block_mask),
+                                                 _ptr(out), dt, _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev)))
+    return out, lse
+
+
+def seer_attn_maxpool_gt_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Sequence[int], *,
+                                out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                                lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                                gt: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Dense attention of a packed batch plus each sequence's 2D-maxpooled map. Returns (out, lse or None, gt)."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16)
+    _need(v, "v", torch.bfloat16)
+    Hq, T, D = q.shape
+    Hkv = k.shape[0]
+    if int(cu_seqlens[-1]) != T:
+        raise ValueError(f"cu_seqlens[-1] ({cu_seqlens[-1]}) must equal the packed length {T}")
+    vl = make_varlen(cu_seqlens, Hq, Hkv, D)
+    dev = q.device
+    if out is None:
+        out = torch.empty((Hq, T, D), dtype=out_dtype, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    if gt is None:
+        gt = torch.empty(lib.seer_varlen_map_elements(ctypes.byref(vl)), dtype=torch.float32, device=dev)
+    dt = SEER_BF16 if out.dtype == torch.bfloat16 else SEER_F32
+    workspace = _workspace(lib.seer_gt_varlen_workspace_size(ctypes.byref(vl)), dev, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.seer_attn_maxpool_gt_varlen(ctypes.byref(vl), _ptr(q), _ptr(k), _ptr(v), _ptr(out), dt, _ptr(lse),
+                                           _ptr(gt), _ptr(workspace), ws_bytes, _stream(dev)))
     return out, lse, gt
 
 

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   const int b = bh / p.Hq;
   const int h = bh - b * p.Hq;
   const int g = h / p.group;
-  const size_t kv_off = (static_cast<size_t>(b) * p.Hkv + g) * p.S * D;
+  const size_t kv_off = (static_cast<size_t>(b) * p.Hkv + g) * p.hs * D;
   const uint16_t* __restrict__ Kg = p.k + kv_off;
   const uint16_t* __restrict__ Vg = p.v + kv_off;
 
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   const bool t_ok = t < p.S;
   uint4 qreg[KS];
   {
-    const uint16_t* qrow = p.q + (static_cast<size_t>(bh) * p.S + (t_ok ? t : 0)) * D + 8 * hl;
+    const uint16_t* qrow = p.q + (static_cast<size_t>(bh) * p.hs + (t_ok ? t : 0)) * D + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qreg[ks] = t_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * ks) : make_uint4(0, 0, 0, 0);
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
     }
   }
   if (t_ok) {
-    const size_t obase = (static_cast<size_t>(bh) * p.S + t) * D;
+    const size_t obase = (static_cast<size_t>(bh) * p.hs + t) * D;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -548,7 +548,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
         }
       }
     }
-    if (p.lse != nullptr && hl == 0) p.lse[static_cast<size_t>(bh) * p.S + t] = lse2 * kLn2;
+    if (p.lse != nullptr && hl == 0) p.lse[static_cast<size_t>(bh) * p.hs + t] = lse2 * kLn2;
   }
 
   if constexpr (MODE == kDenseGt) {
@@ -620,7 +620,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs p) {
   const int t = qb * kBlock + q;
   if (t >= p.S) return;
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const size_t obase = (static_cast<size_t>(bh) * p.S + t) * D + d0;
+  const size_t obase = (static_cast<size_t>(bh) * p.hs + t) * D + d0;
   if (p.out_bf16) {
     uint16_t* o = static_cast<uint16_t*>(p.out) + obase;
 #pragma unroll
@@ -635,7 +635,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs p) {
           make_float4(acc[4 * i] * inv, acc[4 * i + 1] * inv, acc[4 * i + 2] * inv, acc[4 * i + 3] * inv);
   }
   if (p.lse != nullptr && d0 == 0)
-    p.lse[static_cast<size_t>(bh) * p.S + t] = wsum > 0.f ? (lmax + __log2f(wsum)) * kLn2 : -INFINITY;
+    p.lse[static_cast<size_t>(bh) * p.hs + t] = wsum > 0.f ? (lmax + __log2f(wsum)) * kLn2 : -INFINITY;
 }
 
 template <int D>

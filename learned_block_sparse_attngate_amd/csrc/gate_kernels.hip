@@ -54,8 +54,8 @@ __global__ __launch_bounds__(kPoolThreads) void gate_pool_kernel(GateArgs a) {
   const int b = blockIdx.y / H;
   const int hx = blockIdx.y - b * H;
   const bool isq = hx < a.Hq;
-  const uint16_t* src = isq ? a.q + (static_cast<size_t>(b) * a.Hq + hx) * a.S * D
-                            : a.k + (static_cast<size_t>(b) * a.Hkv + (hx - a.Hq)) * a.S * D;
+  const uint16_t* src = isq ? a.q + (static_cast<size_t>(b) * a.Hq + hx) * a.hs * D
+                            : a.k + (static_cast<size_t>(b) * a.Hkv + (hx - a.Hq)) * a.hs * D;
   const int t0 = i * kBlock;
   const int n = min(kBlock, a.S - t0);
   const int tid = threadIdx.x;

@@ -106,6 +106,7 @@ seer::AttnArgs attn_args(const seer_shape* s, const void* q, const void* k, cons
   a.D = s->head_dim;
   a.nb = static_cast<int>(nblocks(s));
   a.group = s->heads_q / s->heads_kv;
+  a.hs = s->seq_len;
   a.ntri = static_cast<long long>(a.nb) * (a.nb + 1) / 2;
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(s->head_dim)));
   a.sched = attn_sched(mode);
@@ -225,10 +226,13 @@ size_t seer_gate_workspace_size(const seer_shape* shape, int32_t gate_dim, int32
   return gate_layout(shape, gate_dim, wk_per_kv_head != 0, want_scores != 0).total;
 }
 
-seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_per_kv_head, float rope_theta,
-                          const void* q, const void* k, const float* w_q, const float* w_k, seer_mask_mode mode,
-                          float threshold, int32_t topk_k, const int32_t* topk_per_head, float* scores,
-                          uint8_t* block_mask, void* workspace, size_t workspace_bytes, void* hip_stream) {
+// hs: tokens between consecutive heads' rows of q and k (seq_len, or the packed
+// length of a varlen batch); launch = false only validates.
+static seer_status gate_impl(const seer_shape* shape, long long hs, int32_t gate_dim, int32_t wk_per_kv_head,
+                             float rope_theta, const void* q, const void* k, const float* w_q, const float* w_k,
+                             seer_mask_mode mode, float threshold, int32_t topk_k, const int32_t* topk_per_head,
+                             float* scores, uint8_t* block_mask, void* workspace, size_t workspace_bytes,
+                             void* hip_stream, bool launch) {
   bool empty = false;
   seer_status st = check_shape(shape, &empty);
   if (st != SEER_OK) return st;
@@ -254,7 +258,7 @@ seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_
     return fail(SEER_ERR_WORKSPACE, "workspace must be %zu bytes, 256-byte aligned (got %zu at %p)", L.total,
                 workspace_bytes, workspace);
   st = check_device();
-  if (st != SEER_OK) return st;
+  if (st != SEER_OK || !launch) return st;
 
   char* ws = static_cast<char*>(workspace);
   seer::GateArgs a{};
@@ -272,6 +276,7 @@ seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_
   a.Hq = shape->heads_q;
   a.Hkv = shape->heads_kv;
   a.S = shape->seq_len;
+  a.hs = hs;
   a.D = shape->head_dim;
   a.nb = static_cast<int>(nblocks(shape));
   a.Dg = gate_dim;
@@ -284,6 +289,14 @@ seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_
   hipError_t e = seer::launch_gate(a, tk, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SEER_ERR_HIP, "gate launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+seer_status seer_gate_fwd(const seer_shape* shape, int32_t gate_dim, int32_t wk_per_kv_head, float rope_theta,
+                          const void* q, const void* k, const float* w_q, const float* w_k, seer_mask_mode mode,
+                          float threshold, int32_t topk_k, const int32_t* topk_per_head, float* scores,
+                          uint8_t* block_mask, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return gate_impl(shape, shape ? shape->seq_len : 0, gate_dim, wk_per_kv_head, rope_theta, q, k, w_q, w_k, mode,
+                   threshold, topk_k, topk_per_head, scores, block_mask, workspace, workspace_bytes, hip_stream, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -460,6 +473,7 @@ seer_status seer_gate_distill_bwd(const seer_shape* shape, int32_t gate_dim, int
   a.Hq = shape->heads_q;
   a.Hkv = shape->heads_kv;
   a.S = shape->seq_len;
+  a.hs = shape->seq_len;
   a.D = shape->head_dim;
   a.nb = static_cast<int>(nblocks(shape));
   a.Dg = gate_dim;
@@ -481,9 +495,9 @@ size_t seer_attn_workspace_size(const seer_shape* shape) {
                                       seer::sparse_chunk_blocks(static_cast<int>(nblocks(shape))));
 }
 
-seer_status seer_block_sparse_attn_fwd(const seer_shape* shape, const void* q, const void* k, const void* v,
-                                       const uint8_t* block_mask, void* out, seer_dtype out_dtype, float* lse,
-                                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+static seer_status attn_impl(const seer_shape* shape, long long hs, const void* q, const void* k, const void* v,
+                             const uint8_t* block_mask, void* out, seer_dtype out_dtype, float* lse,
+                             void* workspace, size_t workspace_bytes, void* hip_stream, bool launch) {
   bool empty = false;
   seer_status st = check_shape(shape, &empty);
   if (st != SEER_OK) return st;
@@ -510,7 +524,8 @@ seer_status seer_block_sparse_attn_fwd(const seer_shape* shape, const void* q, c
       a.part_l = a.part_o + static_cast<size_t>(items) * 64 * a.D;
     }
   }
-  if ((st = check_device()) != SEER_OK) return st;
+  if ((st = check_device()) != SEER_OK || !launch) return st;
+  a.hs = hs;
   a.mask = block_mask;
   a.out = out;
   a.lse = lse;
@@ -518,6 +533,13 @@ seer_status seer_block_sparse_attn_fwd(const seer_shape* shape, const void* q, c
   hipError_t e = seer::launch_attn(a, block_mask ? 0 : 1, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SEER_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+seer_status seer_block_sparse_attn_fwd(const seer_shape* shape, const void* q, const void* k, const void* v,
+                                       const uint8_t* block_mask, void* out, seer_dtype out_dtype, float* lse,
+                                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return attn_impl(shape, shape ? shape->seq_len : 0, q, k, v, block_mask, out, out_dtype, lse, workspace,
+                   workspace_bytes, hip_stream, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -528,9 +550,9 @@ size_t seer_gt_workspace_size(const seer_shape* shape) {
   return align_up(static_cast<size_t>(shape->batch) * shape->heads_q * (nb * (nb + 1) / 2) * kBlock * sizeof(float));
 }
 
-seer_status seer_attn_maxpool_gt(const seer_shape* shape, const void* q, const void* k, const void* v, void* out,
-                                 seer_dtype out_dtype, float* lse, float* gt, void* workspace,
-                                 size_t workspace_bytes, void* hip_stream) {
+static seer_status gt_impl(const seer_shape* shape, long long hs, const void* q, const void* k, const void* v,
+                           void* out, seer_dtype out_dtype, float* lse, float* gt, void* workspace,
+                           size_t workspace_bytes, void* hip_stream, bool launch) {
   bool empty = false;
   seer_status st = check_shape(shape, &empty);
   if (st != SEER_OK) return st;
@@ -544,8 +566,9 @@ seer_status seer_attn_maxpool_gt(const seer_shape* shape, const void* q, const v
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
     return fail(SEER_ERR_WORKSPACE, "workspace must be %zu bytes, 16-byte aligned (got %zu at %p)", need,
                 workspace_bytes, workspace);
-  if ((st = check_device()) != SEER_OK) return st;
+  if ((st = check_device()) != SEER_OK || !launch) return st;
   seer::AttnArgs a = attn_args(shape, q, k, v, 2);
+  a.hs = hs;
   a.out = out;
   a.lse = lse;
   a.out_bf16 = out_dtype == SEER_BF16;
@@ -555,5 +578,173 @@ seer_status seer_attn_maxpool_gt(const seer_shape* shape, const void* q, const v
   if (e != hipSuccess) return fail(SEER_ERR_HIP, "ground-truth attention launch failed: %s", hipGetErrorString(e));
   return ok();
 }
+
+seer_status seer_attn_maxpool_gt(const seer_shape* shape, const void* q, const void* k, const void* v, void* out,
+                                 seer_dtype out_dtype, float* lse, float* gt, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream) {
+  return gt_impl(shape, shape ? shape->seq_len : 0, q, k, v, out, out_dtype, lse, gt, workspace, workspace_bytes,
+                 hip_stream, true);
+}
+
+// ---------------------------------------------------------------------------
+// Varlen (packed) batches: each sequence is a batch-1 problem at its token
+// offset, with the packed length as the head stride; sequences run one after
+// another on the stream and share the workspace. Every sequence is validated
+// before anything is enqueued.
+static seer_status check_varlen(const seer_varlen* vl, long long* total) {
+  if (vl == nullptr) return fail(SEER_ERR_INVALID_ARG, "varlen descriptor is NULL");
+  if (vl->num_seqs < 0) return fail(SEER_ERR_SHAPE, "num_seqs %d is negative", vl->num_seqs);
+  if (vl->num_seqs > 0 && vl->cu_seqlens == nullptr) return fail(SEER_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if (vl->num_seqs > 0 && vl->cu_seqlens[0] != 0) return fail(SEER_ERR_SHAPE, "cu_seqlens[0] must be 0");
+  for (int i = 0; i < vl->num_seqs; ++i)
+    if (vl->cu_seqlens[i + 1] < vl->cu_seqlens[i])
+      return fail(SEER_ERR_SHAPE, "cu_seqlens must be non-decreasing (entry %d)", i + 1);
+  *total = vl->num_seqs > 0 ? vl->cu_seqlens[vl->num_seqs] : 0;
+  return SEER_OK;
+}
+
+static seer_shape varlen_shape(const seer_varlen* vl, int i) {
+  seer_shape s{};
+  s.batch = 1;
+  s.heads_q = vl->heads_q;
+  s.heads_kv = vl->heads_kv;
+  s.seq_len = vl->cu_seqlens[i + 1] - vl->cu_seqlens[i];
+  s.head_dim = vl->head_dim;
+  s.block = vl->block;
+  return s;
+}
+
+size_t seer_varlen_map_elements(const seer_varlen* vl) {
+  long long total = 0;
+  if (check_varlen(vl, &total) != SEER_OK) return 0;
+  size_t n = 0;
+  for (int i = 0; i < vl->num_seqs; ++i) {
+    const size_t nb = (static_cast<size_t>(vl->cu_seqlens[i + 1] - vl->cu_seqlens[i]) + kBlock - 1) / kBlock;
+    n += static_cast<size_t>(vl->heads_q > 0 ? vl->heads_q : 0) * nb * nb;
+  }
+  return n;
+}
+
+size_t seer_gate_varlen_workspace_size(const seer_varlen* vl, int32_t gate_dim, int32_t wk_per_kv_head,
+                                       int32_t want_scores) {
+  long long total = 0;
+  if (check_varlen(vl, &total) != SEER_OK) return 0;
+  size_t need = 0;
+  for (int i = 0; i < vl->num_seqs; ++i) {
+    const seer_shape s = varlen_shape(vl, i);
+    const size_t n = seer_gate_workspace_size(&s, gate_dim, wk_per_kv_head, want_scores);
+    need = n > need ? n : need;
+  }
+  return need;
+}
+
+size_t seer_attn_varlen_workspace_size(const seer_varlen* vl) {
+  long long total = 0;
+  if (check_varlen(vl, &total) != SEER_OK) return 0;
+  size_t need = 0;
+  for (int i = 0; i < vl->num_seqs; ++i) {
+    const seer_shape s = varlen_shape(vl, i);
+    const size_t n = seer_attn_workspace_size(&s);
+    need = n > need ? n : need;
+  }
+  return need;
+}
+
+size_t seer_gt_varlen_workspace_size(const seer_varlen* vl) {
+  long long total = 0;
+  if (check_varlen(vl, &total) != SEER_OK) return 0;
+  size_t need = 0;
+  for (int i = 0; i < vl->num_seqs; ++i) {
+    const seer_shape s = varlen_shape(vl, i);
+    const size_t n = seer_gt_workspace_size(&s);
+    need = n > need ? n : need;
+  }
+  return need;
+}
+
+seer_status seer_gate_varlen_fwd(const seer_varlen* vl, int32_t gate_dim, int32_t wk_per_kv_head, float rope_theta,
+                                 const void* q, const void* k, const float* w_q, const float* w_k,
+                                 seer_mask_mode mode, float threshold, int32_t topk_k,
+                                 const int32_t* topk_per_head, float* scores, uint8_t* block_mask, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream) {
+  long long total = 0;
+  seer_status st = check_varlen(vl, &total);
+  if (st != SEER_OK) return st;
+  for (int pass = 0; pass < 2; ++pass) {
+    size_t moff = 0;
+    for (int i = 0; i < vl->num_seqs; ++i) {
+      const seer_shape s = varlen_shape(vl, i);
+      const size_t t0 = static_cast<size_t>(vl->cu_seqlens[i]) * vl->head_dim;
+      const size_t nb = nblocks(&s);
+      if (s.seq_len > 0) {
+        st = gate_impl(&s, total, gate_dim, wk_per_kv_head, rope_theta,
+                       q ? static_cast<const uint16_t*>(q) + t0 : nullptr,
+                       k ? static_cast<const uint16_t*>(k) + t0 : nullptr, w_q, w_k, mode, threshold, topk_k,
+                       topk_per_head, scores ? scores + moff : nullptr, block_mask ? block_mask + moff : nullptr,
+                       workspace, workspace_bytes, hip_stream, pass == 1);
+        if (st != SEER_OK) return st;
+      }
+      moff += static_cast<size_t>(vl->heads_q) * nb * nb;
+    }
+  }
+  return ok();
+}
+
+seer_status seer_block_sparse_attn_varlen_fwd(const seer_varlen* vl, const void* q, const void* k, const void* v,
+                                              const uint8_t* block_mask, void* out, seer_dtype out_dtype, float* lse,
+                                              void* workspace, size_t workspace_bytes, void* hip_stream) {
+  long long total = 0;
+  seer_status st = check_varlen(vl, &total);
+  if (st != SEER_OK) return st;
+  const size_t esize = out_dtype == SEER_BF16 ? 2 : 4;
+  for (int pass = 0; pass < 2; ++pass) {
+    size_t moff = 0;
+    for (int i = 0; i < vl->num_seqs; ++i) {
+      const seer_shape s = varlen_shape(vl, i);
+      const size_t tok = static_cast<size_t>(vl->cu_seqlens[i]);
+      const size_t t0 = tok * vl->head_dim;
+      const size_t nb = nblocks(&s);
+      if (s.seq_len > 0) {
+        st = attn_impl(&s, total, q ? static_cast<const uint16_t*>(q) + t0 : nullptr,
+                       k ? static_cast<const uint16_t*>(k) + t0 : nullptr,
+                       v ? static_cast<const uint16_t*>(v) + t0 : nullptr, block_mask ? block_mask + moff : nullptr,
+                       out ? static_cast<char*>(out) + t0 * esize : nullptr, out_dtype, lse ? lse + tok : nullptr,
+                       workspace, workspace_bytes, hip_stream, pass == 1);
+        if (st != SEER_OK) return st;
+      }
+      moff += static_cast<size_t>(vl->heads_q) * nb * nb;
+    }
+  }
+  return ok();
+}
+
+seer_status seer_attn_maxpool_gt_varlen(const seer_varlen* vl, const void* q, const void* k, const void* v,
+                                        void* out, seer_dtype out_dtype, float* lse, float* gt, void* workspace,
+                                        size_t workspace_bytes, void* hip_stream) {
+  long long total = 0;
+  seer_status st = check_varlen(vl, &total);
+  if (st != SEER_OK) return st;
+  const size_t esize = out_dtype == SEER_BF16 ? 2 : 4;
+  for (int pass = 0; pass < 2; ++pass) {
+    size_t moff = 0;
+    for (int i = 0; i < vl->num_seqs; ++i) {
+      const seer_shape s = varlen_shape(vl, i);
+      const size_t tok = static_cast<size_t>(vl->cu_seqlens[i]);
+      const size_t t0 = tok * vl->head_dim;
+      const size_t nb = nblocks(&s);
+      if (s.seq_len > 0) {
+        st = gt_impl(&s, total, q ? static_cast<const uint16_t*>(q) + t0 : nullptr,
+                     k ? static_cast<const uint16_t*>(k) + t0 : nullptr,
+                     v ? static_cast<const uint16_t*>(v) + t0 : nullptr,
+                     out ? static_cast<char*>(out) + t0 * esize : nullptr, out_dtype, lse ? lse + tok : nullptr,
+                     gt ? gt + moff : nullptr, workspace, workspace_bytes, hip_stream, pass == 1);
+        if (st != SEER_OK) return st;
+      }
+      moff += static_cast<size_t>(vl->heads_q) * nb * nb;
+    }
+  }
+  return ok();
+}
+
 
 }  // extern "C"

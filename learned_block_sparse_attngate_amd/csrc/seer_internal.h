@@ -18,6 +18,7 @@ struct AttnArgs {
   float* rmax;         // ground-truth scratch [B*Hq][nb(nb+1)/2][64] fp32 (log2 units)
   float* gt;           // fp32 [B,Hq,nb,nb]
   int B, Hq, Hkv, S, D, nb, group;
+  long long hs;        // tokens between consecutive heads' rows of q/k/v/out/lse (S; the packed length for varlen)
   long long ntri;      // nb(nb+1)/2
   float scale_log2;    // log2(e) / sqrt(D)
   int out_bf16;
@@ -52,6 +53,7 @@ struct GateArgs {
   float* scores;       // [B,Hq,nb,nb] (caller's output or workspace)
   uint8_t* mask;       // [B,Hq,nb,nb]
   int B, Hq, Hkv, S, D, nb, Dg, group;
+  long long hs;        // tokens between consecutive heads' rows of q/k (S; the packed length for varlen)
   int wk_per_kv;       // 1: Hwk = Hkv, 0: Hwk = Hq
   float scale;         // 1/sqrt(D)
   int mode;            // 0 threshold, 1 top-k

@@ -163,6 +163,33 @@ def test_decode_validation():
     assert need == 4 * 4 * splits * (128 + 2) and 1 <= splits <= 16
 
 
+def test_varlen_validation_and_sizes():
+    lib = _lib()
+    V = B.make_varlen
+    assert lib.seer_varlen_map_elements(ctypes.byref(V([0, 100, 300, 300, 1000], 4, 2, 128))) == 4 * (4 + 16 + 0 + 121)
+    bad = [V([1, 100], 4, 2, 128), V([0, 100, 50], 4, 2, 128)]
+    for vl in bad:
+        assert lib.seer_block_sparse_attn_varlen_fwd(ctypes.byref(vl), FAKE, FAKE, FAKE, None, FAKE, B.SEER_F32,
+                                                     None, None, 0, None) == B.SEER_ERR_SHAPE
+    assert lib.seer_block_sparse_attn_varlen_fwd(None, FAKE, FAKE, FAKE, None, FAKE, B.SEER_F32, None, None, 0,
+                                                 None) == B.SEER_ERR_INVALID_ARG
+    # the workspace is the largest one sequence needs
+    vl = V([0, 64 * 1100, 64 * 1100 + 500], 4, 2, 128)
+    one = lib.seer_attn_workspace_size(ctypes.byref(_shape(b=1, hq=4, hkv=2, s=64 * 1100, d=128)))
+    assert one > 0 and lib.seer_attn_varlen_workspace_size(ctypes.byref(vl)) == one
+    assert lib.seer_block_sparse_attn_varlen_fwd(ctypes.byref(vl), FAKE, FAKE, FAKE, FAKE, FAKE, B.SEER_F32, None,
+                                                 FAKE, one - 1, None) == B.SEER_ERR_WORKSPACE
+    g1 = lib.seer_gt_workspace_size(ctypes.byref(_shape(b=1, hq=4, hkv=2, s=64 * 1100, d=128)))
+    assert lib.seer_gt_varlen_workspace_size(ctypes.byref(vl)) == g1
+    # nothing is enqueued when a later sequence is invalid: a bad head_dim fails before any launch
+    assert lib.seer_gate_varlen_fwd(ctypes.byref(V([0, 64, 128], 4, 2, 96)), 128, 0, 0.0, FAKE, FAKE, FAKE, FAKE,
+                                    B.SEER_MASK_THRESHOLD, 0.1, 1, None, None, FAKE, FAKE, 1 << 40,
+                                    None) == B.SEER_ERR_UNSUPPORTED
+    # an all-empty batch is a no-op
+    assert lib.seer_block_sparse_attn_varlen_fwd(ctypes.byref(V([0, 0, 0], 4, 2, 128)), None, None, None, None,
+                                                 None, B.SEER_F32, None, None, 0, None) == B.SEER_OK
+
+
 def test_gate_validation():
     s = _shape()
     assert _gate(s, dg=100) == B.SEER_ERR_UNSUPPORTED

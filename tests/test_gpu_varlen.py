@@ -1,0 +1,146 @@
+"""GPU parity of varlen (packed, unpadded) prefill batches: gate, block-sparse
+and dense attention and the 2D-maxpooled map, each sequence against the fp64
+oracle on that sequence alone, and bitwise against the batch-1 calls."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import Shape
+from gpu_util import MASK_BAND, check_close, check_lse, dev_bf16, dev_f32, dev_u8, host, say
+
+pytestmark = pytest.mark.gpu
+
+HQ, HKV = 4, 2
+
+
+def _seer():
+    import learned_block_sparse_attngate_amd as seer
+    seer.load_library()
+    return seer
+
+
+def _pack(lens, D, seed):
+    """Per-sequence bf16 q, k, v ([1, H, len, D]) and their packed [H, T, D] forms."""
+    seqs = []
+    for i, n in enumerate(lens):
+        if n == 0:
+            seqs.append(None)
+            continue
+        q, k, v = synth.gen_qkv(Shape(1, HQ, HKV, n, D), seed + i)
+        seqs.append((q, k, v))
+    def cat(idx, H):
+        parts = [s[idx][0] for s in seqs if s is not None]
+        return np.ascontiguousarray(np.concatenate(parts, axis=1)) if parts else np.zeros((H, 0, D), np.uint16)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(int).tolist()
+    return seqs, cat(0, HQ), cat(1, HKV), cat(2, HKV), cu
+
+
+def _masks(lens, seed, p):
+    rng = np.random.default_rng(seed)
+    out = []
+    for n in lens:
+        nb = synth.Shape(1, HQ, HKV, max(n, 1), 64).nb if n else 0
+        m = (rng.random((HQ, nb, nb)) < p).astype(np.uint8)
+        if nb:
+            m[:, np.arange(nb), np.arange(nb)] = 1
+        out.append(m)
+    return out
+
+
+LENS = [1, 130, 0, 1000, 64 * 20 - 5, 64]
+
+
+@pytest.mark.parametrize("D,dt", [(128, torch.float32), (64, torch.bfloat16)], ids=["d128_f32", "d64_bf16"])
+def test_varlen_sparse_and_dense_attention(D, dt):
+    seer = _seer()
+    seqs, qp, kp, vp, cu = _pack(LENS, D, 100 + D)
+    say(f"[varlen attn D={D}] lens={LENS}")
+    masks = _masks(LENS, 7, 0.4)
+    flat = np.concatenate([m.reshape(-1) for m in masks])
+    dq, dk, dv = dev_bf16(qp), dev_bf16(kp), dev_bf16(vp)
+    out, lse = seer.seer_block_sparse_attn_varlen_fwd(dq, dk, dv, cu, dev_u8(flat), out_dtype=dt, want_lse=True)
+    outd, lsed = seer.seer_block_sparse_attn_varlen_fwd(dq, dk, dv, cu, None, out_dtype=dt, want_lse=True)
+    torch.cuda.synchronize()
+    o_h, l_h, od_h, ld_h = host(out), host(lse), host(outd), host(lsed)
+    for i, n in enumerate(LENS):
+        if n == 0:
+            continue
+        q, k, v = seqs[i]
+        a, b = cu[i], cu[i + 1]
+        o_ref, l_ref = oracle.attention(q, k, v, masks[i][None])
+        check_close(o_h[:, a:b][None], o_ref, f"seq {i} sparse O")
+        check_lse(l_h[:, a:b][None], l_ref, f"seq {i} sparse LSE")
+        od_ref, ld_ref = oracle.attention(q, k, v, None)
+        check_close(od_h[:, a:b][None], od_ref, f"seq {i} dense O")
+        # the batch-1 call on the sequence alone gives the same bits
+        o1, l1 = seer.seer_block_sparse_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_u8(masks[i][None]),
+                                                 out_dtype=dt, want_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], out[:, a:b]) and torch.equal(l1[0], lse[:, a:b])
+
+
+def test_varlen_long_sequence_key_chunks():
+    """A sequence above 1024 blocks (key-chunked, with a workspace) packed with a short one."""
+    seer = _seer()
+    lens = [64 * 1100 - 30, 3000]
+    seqs, qp, kp, vp, cu = _pack(lens, 64, 300)
+    say(f"[varlen long] lens={lens}")
+    masks = [synth.gen_block_mask(Shape(1, HQ, HKV, n, 64), 301 + i, 0.9).mask[0] for i, n in enumerate(lens)]
+    flat = np.concatenate([m.reshape(-1) for m in masks])
+    out, lse = seer.seer_block_sparse_attn_varlen_fwd(dev_bf16(qp), dev_bf16(kp), dev_bf16(vp), cu, dev_u8(flat),
+                                                      out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    q, k, v = seqs[0]
+    nb = (lens[0] + 63) // 64
+    rows = [(0, h, i) for h in range(HQ) for i in (0, 511, 512, 1023, 1024, nb - 1)]
+    o_ref, l_ref = oracle.attention_rows(q, k, v, masks[0][None], rows)
+    o_h, l_h = host(out), host(lse)
+    got = np.concatenate([o_h[h, 64 * i:64 * i + 64][: len(o_ref[n])] for n, (_, h, i) in enumerate(rows)])
+    got_l = np.concatenate([l_h[h, 64 * i:64 * i + 64][: len(l_ref[n])] for n, (_, h, i) in enumerate(rows)])
+    check_close(got, np.concatenate(o_ref), "long seq O (sampled)")
+    check_lse(got_l, np.concatenate(l_ref), "long seq LSE (sampled)")
+    q2, k2, v2 = seqs[1]
+    o2, _ = oracle.attention(q2, k2, v2, masks[1][None])
+    check_close(o_h[:, cu[1]:cu[2]][None], o2, "short seq O")
+
+
+def test_varlen_gate_and_gt():
+    seer = _seer()
+    lens = [640, 0, 64 * 30 - 7, 65]
+    D, dg = 128, 128
+    seqs, qp, kp, vp, cu = _pack(lens, D, 400)
+    wq, wk = synth.gen_gate_weights(HQ, D, dg, 401, var=4.0 / dg)
+    offs, n_map = seer.varlen_map_offsets(cu, HQ)
+    mask, scores = seer.seer_gate_varlen_fwd(dev_bf16(qp), dev_bf16(kp), dev_f32(wq), dev_f32(wk), cu,
+                                             mode="topk", topk=3, rope_theta=5e5)
+    _, _, gt = seer.seer_attn_maxpool_gt_varlen(dev_bf16(qp), dev_bf16(kp), dev_bf16(vp), cu, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    m_h, s_h, g_h = mask.cpu().numpy(), host(scores), host(gt)
+    assert m_h.size == n_map
+    for i, n in enumerate(lens):
+        if n == 0:
+            continue
+        q, k, v = seqs[i]
+        nb = (n + 63) // 64
+        sl = slice(offs[i], offs[i] + HQ * nb * nb)
+        sc_ref = oracle.gate_scores(q, k, wq, wk, rope_theta=5e5)[0]
+        s_i = s_h[sl].reshape(HQ, nb, nb)
+        assert np.abs(s_i - sc_ref).max() < 1e-5
+        want = oracle.topk_mask(sc_ref[None], 3)[0]
+        got = m_h[sl].reshape(HQ, nb, nb)
+        bad = 0
+        for h in range(HQ):
+            for r in range(nb):
+                kk = min(3, r + 1)
+                assert int(got[h, r].sum()) == kk
+                row = sc_ref[h, r, :r + 1]
+                kth = np.sort(row)[::-1][kk - 1]
+                bad += int(((got[h, r, :r + 1] != want[h, r, :r + 1]) & (np.abs(row - kth) > MASK_BAND)).sum())
+        say(f"  seq {i}: gate top-3 mismatches outside the band {bad}")
+        assert bad == 0
+        gt_ref = oracle.maxpool_gt(q, k)[0]
+        err = np.abs(g_h[sl].reshape(HQ, nb, nb) - gt_ref).max()
+        say(f"  seq {i}: gt max-abs {err:.3e}")
+        assert err <= 1e-4
