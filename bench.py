@@ -424,7 +424,7 @@ def main():
             "target_0.8/(1-s)": round(0.8 / (1.0 - s_real), 3),
             "ideal_1/(1-s)": round(1.0 / (1.0 - s_real), 3)},
         "dense_tflops": None if dense_ms is None else round(dense_flop / dense_ms / 1e9, 2),
-        "roofline": {"kernel": "seer_block_sparse_attn_fwd = attn_fwd_kernel<128, sparse> + attn_combine_kernel<128>",
+        "roofline": {"kernel": "seer_block_sparse_attn_fwd (one call: main block-sparse kernel + merge of partial outputs)",
                      "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(args.workload)},

@@ -160,12 +160,16 @@ seer_status seer_gate_distill_bwd(const seer_shape* shape, int32_t gate_dim, int
  * workspace    device scratch of at least seer_attn_workspace_size() bytes,
  *              16-byte aligned, used only when block_mask is non-NULL. Rows
  *              of more than 1024 blocks (seq_len > 65536) are processed in
- *              key chunks of 512 blocks, so that the GPU works on one chunk
- *              of K/V at a time, and leave per-chunk fp32 partial outputs
- *              there that a second kernel merges (64 * (head_dim + 1) * 4
- *              bytes per row and chunk). The size is 0, and workspace may be
- *              NULL, when seq_len <= 65536. The active-block list of each row
- *              is compacted on chip.
+ *              key chunks and leave per-chunk partial outputs there that a
+ *              second kernel merges. Rows of at least 1280 blocks with at
+ *              least 64 (batch, KV head, 128-block chunk) pairs use chunks of
+ *              128 blocks, each owned by one XCD: 64 * (2 * head_dim + 4)
+ *              bytes per row and chunk (bf16 output, fp32 log-sum-exp) plus
+ *              256 bytes of item counters that every call resets. Other long
+ *              rows use chunks of 512 blocks: 64 * (head_dim + 1) * 4 bytes
+ *              per row and chunk. The size is 0, and workspace may be NULL,
+ *              when seq_len <= 65536. The active blocks of each row are
+ *              compacted on chip.
  * ---------------------------------------------------------------------- */
 size_t seer_attn_workspace_size(const seer_shape* shape);
 seer_status seer_block_sparse_attn_fwd(const seer_shape* shape, const void* q, const void* k,

@@ -49,6 +49,7 @@
 #include <stdlib.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "seer_device.h"
 #include "seer_internal.h"
@@ -66,6 +67,16 @@ constexpr int kXcds = 8;                 // workgroups are dealt round-robin to 
 constexpr int kSweepPhases = 128;        // resident workgroups per XCD (32 CUs x 4)
 
 enum Mode { kSparse = 0, kDense = 1, kDenseGt = 2 };
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>)
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -108,6 +119,195 @@ __device__ __forceinline__ uint32_t lds_read_u32(uint32_t addr) {
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)p));
+}
+
+// K operands of one tile for S^T = K Q^T: kr[2 ks + mt] holds keys 32 mt + l32,
+// dims 16 ks + 8 hl .. +7. Waits for its own LDS reads before returning.
+template <int D>
+__device__ __forceinline__ void read_k_tile(const uint32_t (&kaddr)[D / 16], u32x4_t (&kr)[D / 8]) {
+  if constexpr (D == 128) {
+    asm volatile(
+        "ds_read_b128 %0, %16\n ds_read_b128 %1, %16 offset:8192\n"
+        "ds_read_b128 %2, %17\n ds_read_b128 %3, %17 offset:8192\n"
+        "ds_read_b128 %4, %18\n ds_read_b128 %5, %18 offset:8192\n"
+        "ds_read_b128 %6, %19\n ds_read_b128 %7, %19 offset:8192\n"
+        "ds_read_b128 %8, %20\n ds_read_b128 %9, %20 offset:8192\n"
+        "ds_read_b128 %10, %21\n ds_read_b128 %11, %21 offset:8192\n"
+        "ds_read_b128 %12, %22\n ds_read_b128 %13, %22 offset:8192\n"
+        "ds_read_b128 %14, %23\n ds_read_b128 %15, %23 offset:8192\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(kr[4]), "=&v"(kr[5]), "=&v"(kr[6]),
+          "=&v"(kr[7]), "=&v"(kr[8]), "=&v"(kr[9]), "=&v"(kr[10]), "=&v"(kr[11]), "=&v"(kr[12]), "=&v"(kr[13]),
+          "=&v"(kr[14]), "=&v"(kr[15])
+        : "v"(kaddr[0]), "v"(kaddr[1]), "v"(kaddr[2]), "v"(kaddr[3]), "v"(kaddr[4]), "v"(kaddr[5]),
+          "v"(kaddr[6]), "v"(kaddr[7])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %8\n ds_read_b128 %1, %8 offset:4096\n"
+        "ds_read_b128 %2, %9\n ds_read_b128 %3, %9 offset:4096\n"
+        "ds_read_b128 %4, %10\n ds_read_b128 %5, %10 offset:4096\n"
+        "ds_read_b128 %6, %11\n ds_read_b128 %7, %11 offset:4096\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(kr[4]), "=&v"(kr[5]), "=&v"(kr[6]),
+          "=&v"(kr[7])
+        : "v"(kaddr[0]), "v"(kaddr[1]), "v"(kaddr[2]), "v"(kaddr[3])
+        : "memory");
+  }
+}
+
+// V^T operands of one tile for O^T = V^T P^T through transposing reads:
+// vr[(ks MT + mt) 2 + u] holds dims 32 mt + .., keys 16 ks + 8 u + ..
+template <int D>
+__device__ __forceinline__ void read_v_tile(const uint32_t (&vaddr)[D / 32], u32x2_t (&vr)[D / 4]) {
+  if constexpr (D == 128) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %32\n ds_read_b64_tr_b16 %1, %32 offset:2048\n"
+        "ds_read_b64_tr_b16 %2, %33\n ds_read_b64_tr_b16 %3, %33 offset:2048\n"
+        "ds_read_b64_tr_b16 %4, %34\n ds_read_b64_tr_b16 %5, %34 offset:2048\n"
+        "ds_read_b64_tr_b16 %6, %35\n ds_read_b64_tr_b16 %7, %35 offset:2048\n"
+        "ds_read_b64_tr_b16 %8, %32 offset:4096\n ds_read_b64_tr_b16 %9, %32 offset:6144\n"
+        "ds_read_b64_tr_b16 %10, %33 offset:4096\n ds_read_b64_tr_b16 %11, %33 offset:6144\n"
+        "ds_read_b64_tr_b16 %12, %34 offset:4096\n ds_read_b64_tr_b16 %13, %34 offset:6144\n"
+        "ds_read_b64_tr_b16 %14, %35 offset:4096\n ds_read_b64_tr_b16 %15, %35 offset:6144\n"
+        "ds_read_b64_tr_b16 %16, %32 offset:8192\n ds_read_b64_tr_b16 %17, %32 offset:10240\n"
+        "ds_read_b64_tr_b16 %18, %33 offset:8192\n ds_read_b64_tr_b16 %19, %33 offset:10240\n"
+        "ds_read_b64_tr_b16 %20, %34 offset:8192\n ds_read_b64_tr_b16 %21, %34 offset:10240\n"
+        "ds_read_b64_tr_b16 %22, %35 offset:8192\n ds_read_b64_tr_b16 %23, %35 offset:10240\n"
+        "ds_read_b64_tr_b16 %24, %32 offset:12288\n ds_read_b64_tr_b16 %25, %32 offset:14336\n"
+        "ds_read_b64_tr_b16 %26, %33 offset:12288\n ds_read_b64_tr_b16 %27, %33 offset:14336\n"
+        "ds_read_b64_tr_b16 %28, %34 offset:12288\n ds_read_b64_tr_b16 %29, %34 offset:14336\n"
+        "ds_read_b64_tr_b16 %30, %35 offset:12288\n ds_read_b64_tr_b16 %31, %35 offset:14336\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]),
+          "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]), "=&v"(vr[12]), "=&v"(vr[13]),
+          "=&v"(vr[14]), "=&v"(vr[15]), "=&v"(vr[16]), "=&v"(vr[17]), "=&v"(vr[18]), "=&v"(vr[19]),
+          "=&v"(vr[20]), "=&v"(vr[21]), "=&v"(vr[22]), "=&v"(vr[23]), "=&v"(vr[24]), "=&v"(vr[25]),
+          "=&v"(vr[26]), "=&v"(vr[27]), "=&v"(vr[28]), "=&v"(vr[29]), "=&v"(vr[30]), "=&v"(vr[31])
+        : "v"(vaddr[0]), "v"(vaddr[1]), "v"(vaddr[2]), "v"(vaddr[3])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n ds_read_b64_tr_b16 %1, %16 offset:1024\n"
+        "ds_read_b64_tr_b16 %2, %17\n ds_read_b64_tr_b16 %3, %17 offset:1024\n"
+        "ds_read_b64_tr_b16 %4, %16 offset:2048\n ds_read_b64_tr_b16 %5, %16 offset:3072\n"
+        "ds_read_b64_tr_b16 %6, %17 offset:2048\n ds_read_b64_tr_b16 %7, %17 offset:3072\n"
+        "ds_read_b64_tr_b16 %8, %16 offset:4096\n ds_read_b64_tr_b16 %9, %16 offset:5120\n"
+        "ds_read_b64_tr_b16 %10, %17 offset:4096\n ds_read_b64_tr_b16 %11, %17 offset:5120\n"
+        "ds_read_b64_tr_b16 %12, %16 offset:6144\n ds_read_b64_tr_b16 %13, %16 offset:7168\n"
+        "ds_read_b64_tr_b16 %14, %17 offset:6144\n ds_read_b64_tr_b16 %15, %17 offset:7168\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]),
+          "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]), "=&v"(vr[12]), "=&v"(vr[13]),
+          "=&v"(vr[14]), "=&v"(vr[15])
+        : "v"(vaddr[0]), "v"(vaddr[1])
+        : "memory");
+  }
+}
+
+// S^T = K Q^T for one tile (32 keys x 32 queries per m-tile, two m-tiles),
+// element causality on the diagonal tile, and the row maximum of the tile in
+// log2 units (c = log2(e) / sqrt(D)).
+template <int D, bool kDiag>
+__device__ __forceinline__ float tile_scores(const u32x4_t (&kr)[D / 8], const uint4 (&qreg)[D / 16],
+                                             f32x16_t (&sacc)[2], int q_local, int hl, float c) {
+  sacc[0] = f32x16_t{};
+  sacc[1] = f32x16_t{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      sacc[mt] = mfma_32x32x16(__builtin_bit_cast(uint4, kr[2 * ks + mt]), qreg[ks], sacc[mt]);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if constexpr (kDiag) {
+        const int key = 32 * mt + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (key > q_local) sacc[mt][r] = -INFINITY;
+      }
+      mx = fmaxf(mx, sacc[mt][r]);
+    }
+  }
+  return pair_max(mx) * c;
+}
+
+// Online-softmax update with one tile: lazy rescale (the running max m moves
+// only when a lane's tile max exceeds it by more than the slack), P = exp2(s c
+// - m) packed to bf16 in the B-operand layout, and O^T += V^T P^T.
+// As tile_scores with the diagonal decided at run time (one inlined copy in a
+// loop). The causality compares take the query row through an empty asm so
+// that they are not hoisted out of the loop as 32 loop-invariant scalar masks.
+template <int D>
+__device__ __forceinline__ float tile_scores_rt(const u32x4_t (&kr)[D / 8], const uint4 (&qreg)[D / 16],
+                                                f32x16_t (&sacc)[2], int q_local, int hl, float c, bool diag) {
+  sacc[0] = f32x16_t{};
+  sacc[1] = f32x16_t{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      sacc[mt] = mfma_32x32x16(__builtin_bit_cast(uint4, kr[2 * ks + mt]), qreg[ks], sacc[mt]);
+  if (diag) {
+    int ql = q_local - 4 * hl;
+    asm volatile("" : "+v"(ql));
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * mt + 8 * (r >> 2) + (r & 3);
+        if (key > ql) sacc[mt][r] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
+  return pair_max(mx) * c;
+}
+
+template <int D>
+__device__ __forceinline__ void tile_update(const f32x16_t (&sacc)[2], const u32x2_t (&vr)[D / 4], float mx,
+                                            float c, float& m, float& lsum, f32x16_t (&oacc)[D / 32]) {
+  constexpr int MT = D / 32;
+  // lazy rescale: move the running max only when it grows by > slack
+  const bool upd = mx > m + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(upd)) {
+    const float mn = upd ? mx : m;
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);   // m = -inf on the first tile: alpha = 0
+    lsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) oacc[i] *= alpha;
+    m = mn;
+  }
+  // P = exp2(s*c - m), packed to bf16 in the B-operand layout of O^T = V^T P^T
+  uint4 pb[4];
+  float ls = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float e[8];
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8) {
+        e[s8] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][8 * hh + s8], c, -m));
+        ls += e[s8];
+      }
+      pb[2 * mt + hh] = make_uint4(pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
+                                   pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7]));
+    }
+  }
+  lsum += ls;
+  // ---- O^T += V^T P^T (32 dims x 32 queries per m-tile, 4 k-steps of 16 keys)
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x2_t lo = vr[(ks * MT + mt) * 2], hi = vr[(ks * MT + mt) * 2 + 1];
+      oacc[mt] = mfma_32x32x16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[ks], oacc[mt]);
+    }
 }
 
 template <int D, int MODE>
@@ -275,60 +475,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
     wait_vmcnt(first ? NDMA : NDMA + stores_pending);
     wg_barrier();
     u32x4_t kr[2 * KS];                           // kr[2 ks + mt]: keys 32 mt + l32, dims 16 ks + 8 hl ..
-    if constexpr (D == 128) {
-      asm volatile(
-          "ds_read_b128 %0, %16\n ds_read_b128 %1, %16 offset:8192\n"
-          "ds_read_b128 %2, %17\n ds_read_b128 %3, %17 offset:8192\n"
-          "ds_read_b128 %4, %18\n ds_read_b128 %5, %18 offset:8192\n"
-          "ds_read_b128 %6, %19\n ds_read_b128 %7, %19 offset:8192\n"
-          "ds_read_b128 %8, %20\n ds_read_b128 %9, %20 offset:8192\n"
-          "ds_read_b128 %10, %21\n ds_read_b128 %11, %21 offset:8192\n"
-          "ds_read_b128 %12, %22\n ds_read_b128 %13, %22 offset:8192\n"
-          "ds_read_b128 %14, %23\n ds_read_b128 %15, %23 offset:8192\n"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(kr[4]), "=&v"(kr[5]), "=&v"(kr[6]),
-            "=&v"(kr[7]), "=&v"(kr[8]), "=&v"(kr[9]), "=&v"(kr[10]), "=&v"(kr[11]), "=&v"(kr[12]), "=&v"(kr[13]),
-            "=&v"(kr[14]), "=&v"(kr[15])
-          : "v"(kaddr[0]), "v"(kaddr[1]), "v"(kaddr[2]), "v"(kaddr[3]), "v"(kaddr[4]), "v"(kaddr[5]),
-            "v"(kaddr[6]), "v"(kaddr[7])
-          : "memory");
-    } else {
-      asm volatile(
-          "ds_read_b128 %0, %8\n ds_read_b128 %1, %8 offset:4096\n"
-          "ds_read_b128 %2, %9\n ds_read_b128 %3, %9 offset:4096\n"
-          "ds_read_b128 %4, %10\n ds_read_b128 %5, %10 offset:4096\n"
-          "ds_read_b128 %6, %11\n ds_read_b128 %7, %11 offset:4096\n"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(kr[4]), "=&v"(kr[5]), "=&v"(kr[6]),
-            "=&v"(kr[7])
-          : "v"(kaddr[0]), "v"(kaddr[1]), "v"(kaddr[2]), "v"(kaddr[3])
-          : "memory");
-    }
+    read_k_tile<D>(kaddr, kr);
     wg_barrier();                                  // both waves hold K: refill the K buffer
     if (next >= 0) issue_k(next);
 
-    // ---- S^T = K Q^T (32 keys x 32 queries per m-tile, two m-tiles)
-    f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        sacc[mt] = mfma_32x32x16(__builtin_bit_cast(uint4, kr[2 * ks + mt]), qreg[ks], sacc[mt]);
-
-    // element causality on the diagonal tile; row max
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if constexpr (kDiag) {
-          const int key = 32 * mt + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key > q_local) sacc[mt][r] = -INFINITY;
-        }
-        mx = fmaxf(mx, sacc[mt][r]);
-      }
-    }
-    mx = pair_max(mx) * c;                         // row max of this tile, log2 units
+    f32x16_t sacc[2];
+    float mx = tile_scores<D, kDiag>(kr, qreg, sacc, q_local, hl, c);
     int stores_now = 0;
     if constexpr (MODE == kDenseGt) {
       if (hl == 0) p.rmax[((static_cast<size_t>(bh) * p.ntri + ntri_off + kb) << 6) + q_local] = mx;
@@ -339,89 +491,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
     wait_vmcnt((next >= 0 ? NDMA : 0) + stores_now);
     wg_barrier();
     u32x2_t vr[8 * MT];                            // vr[(ks MT + mt) 2 + u]: dims 32 mt + .., keys 16 ks + 8 u + ..
-    if constexpr (D == 128) {
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %32\n ds_read_b64_tr_b16 %1, %32 offset:2048\n"
-          "ds_read_b64_tr_b16 %2, %33\n ds_read_b64_tr_b16 %3, %33 offset:2048\n"
-          "ds_read_b64_tr_b16 %4, %34\n ds_read_b64_tr_b16 %5, %34 offset:2048\n"
-          "ds_read_b64_tr_b16 %6, %35\n ds_read_b64_tr_b16 %7, %35 offset:2048\n"
-          "ds_read_b64_tr_b16 %8, %32 offset:4096\n ds_read_b64_tr_b16 %9, %32 offset:6144\n"
-          "ds_read_b64_tr_b16 %10, %33 offset:4096\n ds_read_b64_tr_b16 %11, %33 offset:6144\n"
-          "ds_read_b64_tr_b16 %12, %34 offset:4096\n ds_read_b64_tr_b16 %13, %34 offset:6144\n"
-          "ds_read_b64_tr_b16 %14, %35 offset:4096\n ds_read_b64_tr_b16 %15, %35 offset:6144\n"
-          "ds_read_b64_tr_b16 %16, %32 offset:8192\n ds_read_b64_tr_b16 %17, %32 offset:10240\n"
-          "ds_read_b64_tr_b16 %18, %33 offset:8192\n ds_read_b64_tr_b16 %19, %33 offset:10240\n"
-          "ds_read_b64_tr_b16 %20, %34 offset:8192\n ds_read_b64_tr_b16 %21, %34 offset:10240\n"
-          "ds_read_b64_tr_b16 %22, %35 offset:8192\n ds_read_b64_tr_b16 %23, %35 offset:10240\n"
-          "ds_read_b64_tr_b16 %24, %32 offset:12288\n ds_read_b64_tr_b16 %25, %32 offset:14336\n"
-          "ds_read_b64_tr_b16 %26, %33 offset:12288\n ds_read_b64_tr_b16 %27, %33 offset:14336\n"
-          "ds_read_b64_tr_b16 %28, %34 offset:12288\n ds_read_b64_tr_b16 %29, %34 offset:14336\n"
-          "ds_read_b64_tr_b16 %30, %35 offset:12288\n ds_read_b64_tr_b16 %31, %35 offset:14336\n"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]),
-            "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]), "=&v"(vr[12]), "=&v"(vr[13]),
-            "=&v"(vr[14]), "=&v"(vr[15]), "=&v"(vr[16]), "=&v"(vr[17]), "=&v"(vr[18]), "=&v"(vr[19]),
-            "=&v"(vr[20]), "=&v"(vr[21]), "=&v"(vr[22]), "=&v"(vr[23]), "=&v"(vr[24]), "=&v"(vr[25]),
-            "=&v"(vr[26]), "=&v"(vr[27]), "=&v"(vr[28]), "=&v"(vr[29]), "=&v"(vr[30]), "=&v"(vr[31])
-          : "v"(vaddr[0]), "v"(vaddr[1]), "v"(vaddr[2]), "v"(vaddr[3])
-          : "memory");
-    } else {
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %16\n ds_read_b64_tr_b16 %1, %16 offset:1024\n"
-          "ds_read_b64_tr_b16 %2, %17\n ds_read_b64_tr_b16 %3, %17 offset:1024\n"
-          "ds_read_b64_tr_b16 %4, %16 offset:2048\n ds_read_b64_tr_b16 %5, %16 offset:3072\n"
-          "ds_read_b64_tr_b16 %6, %17 offset:2048\n ds_read_b64_tr_b16 %7, %17 offset:3072\n"
-          "ds_read_b64_tr_b16 %8, %16 offset:4096\n ds_read_b64_tr_b16 %9, %16 offset:5120\n"
-          "ds_read_b64_tr_b16 %10, %17 offset:4096\n ds_read_b64_tr_b16 %11, %17 offset:5120\n"
-          "ds_read_b64_tr_b16 %12, %16 offset:6144\n ds_read_b64_tr_b16 %13, %16 offset:7168\n"
-          "ds_read_b64_tr_b16 %14, %17 offset:6144\n ds_read_b64_tr_b16 %15, %17 offset:7168\n"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]),
-            "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]), "=&v"(vr[12]), "=&v"(vr[13]),
-            "=&v"(vr[14]), "=&v"(vr[15])
-          : "v"(vaddr[0]), "v"(vaddr[1])
-          : "memory");
-    }
+    read_v_tile<D>(vaddr, vr);
     wg_barrier();                                  // both waves hold V: refill the V buffer
     if (next >= 0) issue_v(next);
     stores_pending = stores_now;
 
-    // lazy rescale: move the running max only when it grows by > slack
-    const bool upd = mx > m + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(upd)) {
-      const float mn = upd ? mx : m;
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);   // m = -inf on the first tile: alpha = 0
-      lsum *= alpha;
-#pragma unroll
-      for (int i = 0; i < MT; ++i) oacc[i] *= alpha;
-      m = mn;
-    }
-    // P = exp2(s*c - m), packed to bf16 in the B-operand layout of O^T = V^T P^T
-    uint4 pb[4];
-    float ls = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float e[8];
-#pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8) {
-          e[s8] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][8 * hh + s8], c, -m));
-          ls += e[s8];
-        }
-        pb[2 * mt + hh] = make_uint4(pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
-                                     pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7]));
-      }
-    }
-    lsum += ls;
-    // ---- O^T += V^T P^T (32 dims x 32 queries per m-tile, 4 k-steps of 16 keys)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const u32x2_t lo = vr[(ks * MT + mt) * 2], hi = vr[(ks * MT + mt) * 2 + 1];
-        oacc[mt] = mfma_32x32x16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[ks], oacc[mt]);
-      }
+    tile_update<D>(sacc, vr, mx, c, m, lsum, oacc);
   };
 
   // ---- main loop over active key blocks -----------------------------------
@@ -575,6 +650,462 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Block-sparse rows of many key blocks: XCD-owned key chunks, persistent
+// workgroups.
+//
+// The key range is cut into chunks of C blocks. A job is one chunk of one
+// (batch, KV group): the (row, chunk) items of every query head of the group
+// whose causal range reaches the chunk, head major, query block descending.
+// Jobs are dealt to the 8 XCDs in the order 0..7, 7..0, 0..7, ... (so each XCD
+// gets chunks c and n-1-c of the groups, which evens out the causal triangle)
+// and every XCD works through its own jobs one after another: the K/V of the
+// chunk its items read (C = 128 tiles of 32 KiB at D = 128, the size of the
+// XCD's 4 MiB L2) is fetched from HBM a few times per job instead of once per
+// reading row. The
+// grid is the resident capacity, kXcdSlots workgroups per XCD; workgroup w
+// runs on XCD w % 8 and takes the next item of that XCD's sequence from a
+// per-XCD counter, so the items resident on an XCD stay a contiguous window of
+// its sequence (a fixed stride per workgroup lets them drift over several
+// chunks). Nothing drains between items: item indices are fetched two items
+// ahead, the next item's mask flags one item ahead, and its Q rows and first
+// K/V tile are issued during the current item's last tile. An item of a row
+// that spans several chunks writes a bf16 partial output (normalized by its
+// own sum) and its log2-sum-exp; attn_xcd_combine_kernel merges them. Rows
+// inside the first chunk are one item and are written directly.
+constexpr int kXcdMaxChunk = 128;        // key blocks per chunk at most (two 64-bit flag words)
+constexpr int kXcdDefaultChunk = 128;    // 4 MiB of K/V at D = 128: one XCD's L2
+constexpr int kXcdMinBlocks = 1280;      // rows of 80k tokens and more
+constexpr int kXcdSlots = 128;           // resident workgroups per XCD: 32 CUs x 4
+
+// s_waitcnt vmcnt(n) for the counts the persistent kernel uses; anything else
+// waits for every operation in flight.
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 4: __builtin_amdgcn_s_waitcnt(0x0f74); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0f78); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0f7c); break;
+    case 16: __builtin_amdgcn_s_waitcnt(0x4f70); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0f70); break;
+  }
+}
+
+// Job at position t of XCD x's sequence, or -1 past its end. Positions 2i and
+// 2i+1 take jobs 16i + x and 16i + 15 - x; the first job past the end ends it.
+__device__ __forceinline__ int xcd_job(int x, int t, int njobs) {
+  const int base = 2 * kXcds * (t >> 1);
+  const int k = (t & 1) ? base + 2 * kXcds - 1 - x : base + x;
+  return k < njobs ? k : -1;
+}
+
+struct XcdItem {
+  int bh;      // batch * Hq + head; -1: past the end of the sequence
+  int qb;      // query block
+  int c;       // key chunk
+};
+
+// Walks one XCD's item sequence; queried with increasing item indices (the
+// host keeps every index within 32 bits).
+struct XcdCursor {
+  int t = 0;
+  int job = -1;
+  int begin = 0;           // sequence index of the job's first item
+  int count = 0;           // items in the job
+};
+
+__device__ __forceinline__ XcdItem xcd_item(const AttnArgs& p, int x, int j, XcdCursor& cur) {
+  while (true) {
+    if (cur.job < 0) {
+      cur.job = xcd_job(x, cur.t, p.njobs);
+      if (cur.job < 0) return XcdItem{-1, 0, 0};
+      cur.count = p.group * (p.nb - (cur.job % p.nchunk) * p.chunk);
+    }
+    if (j < cur.begin + cur.count) break;
+    cur.begin += cur.count;
+    ++cur.t;
+    cur.job = -1;
+  }
+  const int c = cur.job % p.nchunk, gi = cur.job / p.nchunk;
+  const int rows = p.nb - c * p.chunk;
+  const int mi = j - cur.begin;
+  const int hig = mi / rows;
+  const int bb = gi / p.Hkv, gg = gi - bb * p.Hkv;
+  return XcdItem{bb * p.Hq + gg * p.group + hig, p.nb - 1 - (mi - hig * rows), c};
+}
+
+// Partial-output slots before query block qb of one head: rows qb' >= C own
+// qb'/C + 1 slots each (one per key chunk they reach).
+__device__ __host__ __forceinline__ long long xcd_slot_base(long long qb, long long C) {
+  const long long k = qb / C;
+  return qb + C * k * (k - 1) / 2 + k * (qb - k * C) - C;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p) {
+  constexpr int CPR = D / 8;               // 16-byte chunks per K/V row
+  constexpr int KS = D / 16;               // MFMA k-steps for S^T (= Q loads per thread)
+  constexpr int MT = D / 32;               // MFMA m-tiles for O^T
+  constexpr int RPI = 64 / CPR;            // tile rows per copy instruction
+  constexpr int NDMA = 32 / RPI;           // copy instructions per wave per operand
+  constexpr int HALF = D / 2;              // output values per thread
+
+  __shared__ uint4 Ks[kBlock * CPR];
+  __shared__ uint4 Vs[kBlock * CPR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+  const int q_local = wave * 32 + l32;
+  const int x = static_cast<int>(blockIdx.x % kXcds);
+  int* const ctr = p.xcd_ctr + x;                  // next unclaimed item of this XCD's sequence
+
+  uint32_t kofs[4], vofs;
+  {
+    const int r0 = 32 * wave + lane / CPR;
+    const int pc = lane % CPR;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) kofs[v] = static_cast<uint32_t>(r0 * 2 * D + 16 * (pc ^ swz_k<D>(r0 + RPI * v)));
+    vofs = static_cast<uint32_t>(r0 * 2 * D + 16 * (pc ^ swz_v<D>(r0)));
+  }
+  // copies of tile kb of the K/V head that starts at kv (rows past the
+  // sequence read as zeros, as in attn_fwd_kernel). Copy instruction i moves
+  // RPI rows of 2D bytes = 1024 bytes further on in memory and in LDS, so its
+  // immediate offset (added to both addresses) carries i % 4 and one LDS base
+  // serves four instructions. The immediate field holds 12 bits (offsets past
+  // 4095 do not encode), so instructions 4..7 take a second base 4096 bytes on.
+  auto issue_k = [&](const uint16_t* kv, int kb) {
+    const int key0 = kb * kBlock;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kv + static_cast<size_t>(key0) * D), 0,
+                                                      (p.S - key0) * 2 * D, kBufferWord3);
+    char* dst = reinterpret_cast<char*>(Ks) + 32 * wave * D * 2;
+    static_for<NDMA>([&](auto I) {
+      constexpr int i = decltype(I)::value, hi = i / 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + 4096 * hi), 16,
+                                               (D == 128 ? kofs[i & 3] : kofs[0]) + 4096 * hi, 0, 1024 * (i % 4), 0);
+    });
+  };
+  auto issue_v = [&](const uint16_t* kv, int kb) {
+    const int key0 = kb * kBlock;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kv + static_cast<size_t>(key0) * D), 0,
+                                                      (p.S - key0) * 2 * D, kBufferWord3);
+    char* dst = reinterpret_cast<char*>(Vs) + 32 * wave * D * 2;
+    static_for<NDMA>([&](auto I) {
+      constexpr int i = decltype(I)::value, hi = i / 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + 4096 * hi), 16, vofs + 4096 * hi, 0,
+                                               1024 * (i % 4), 0);
+    });
+  };
+  uint32_t kaddr[KS], vaddr[MT];
+  {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kaddr[ks] = lds_addr(Ks) + l32 * 2 * D + 16 * ((2 * ks + hl) ^ swz_k<D>(l32));
+    const int G = lane >> 4, jj = (lane >> 2) & 3, a = lane & 3;
+    const int key = 4 * (G >> 1) + jj;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      vaddr[mt] = lds_addr(Vs) + key * 2 * D + 16 * ((4 * mt + 2 * (G & 1) + (a >> 1)) ^ swz_v<D>(key)) + 8 * (a & 1);
+  }
+
+  auto kv_head = [&](const XcdItem& it) -> size_t {
+    const int b = it.bh / p.Hq;
+    const int g = (it.bh - b * p.Hq) / p.group;
+    return (static_cast<size_t>(b) * p.Hkv + g) * p.hs * D;
+  };
+  // this lane's mask bytes of an item's chunk: keys c0 + lane and c0 + 64 +
+  // lane (0 past the causal end, the diagonal included)
+  auto load_flags = [&](const XcdItem& it, uint32_t& f0, uint32_t& f1) {
+    f0 = 0;
+    f1 = 0;
+    if (it.bh < 0) return;
+    const int c0 = it.c * p.chunk;
+    const int kend = min(it.qb + 1, c0 + p.chunk);
+    const uint8_t* mrow = p.mask + (static_cast<size_t>(it.bh) * p.nb + it.qb) * p.nb;
+    if (c0 + lane < kend) f0 = mrow[c0 + lane];
+    if (c0 + 64 + lane < kend) f1 = mrow[c0 + 64 + lane];
+  };
+  // Q rows of an item (rows past the sequence repeat the last one: their
+  // outputs are never stored)
+  auto load_q = [&](const XcdItem& it, uint4 (&qr)[KS]) {
+    const int t = min(it.qb * kBlock + q_local, p.S - 1);
+    const uint16_t* qrow = p.q + (static_cast<size_t>(it.bh) * p.hs + t) * D + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qr[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks);
+  };
+  // first tile of an item: the diagonal if it is active, else the lowest active block
+  auto first_tile = [&](const XcdItem& it, uint64_t f0, uint64_t f1) -> int {
+    const int c0 = it.c * p.chunk;
+    const int d = it.qb - c0;
+    if (d < p.chunk && ((d < 64 ? (f0 >> d) : (f1 >> (d - 64))) & 1)) return it.qb;
+    if (f0) return c0 + static_cast<int>(__builtin_ctzll(f0));
+    if (f1) return c0 + 64 + static_cast<int>(__builtin_ctzll(f1));
+    return -1;
+  };
+
+  // next active block of the item (ascending), -1 when none is left
+  auto pop_flag = [](uint64_t& f0, uint64_t& f1, int c0) -> int {
+    if (f0) {
+      const int b = static_cast<int>(__builtin_ctzll(f0));
+      f0 &= f0 - 1;
+      return c0 + b;
+    }
+    if (f1) {
+      const int b = static_cast<int>(__builtin_ctzll(f1));
+      f1 &= f1 - 1;
+      return c0 + 64 + b;
+    }
+    return -1;
+  };
+
+  // the first three items in one claim; afterwards one claim per item, two
+  // items ahead (wave 0 lane 0 claims, LDS hands the index to both waves)
+  __shared__ int claim;
+  if (tid == 0) claim = atomicAdd(ctr, 3);
+  __syncthreads();
+  const int j0 = claim;
+  XcdCursor cur;
+  XcdItem it = xcd_item(p, x, j0, cur);            // this item
+  if (it.bh < 0) return;
+  XcdItem it1 = xcd_item(p, x, j0 + 1, cur);       // the next one
+  int j2 = j0 + 2;                                 // the one after
+  int pend = 0;                                    // wave 0 lane 0: claim in flight (the item after j2)
+  bool claimed = false;
+
+  const float c = p.scale_log2;
+  uint4 qreg[KS];
+  float m = -INFINITY, lsum = 0.f;
+  f32x16_t oacc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) oacc[i] = f32x16_t{};
+
+  // One tile; its copies were issued before. `tile0`: the item's first tile,
+  // whose copies (and everything else issued earlier) have landed. `nkv`:
+  // offset of the K/V head of the next tile `next` (-1: none). `qn`: load the
+  // next item's Q rows into qreg once this tile's scores are computed.
+  auto compute = [&](bool diag, bool tile0, size_t nkv, int next, bool qn) {
+    if (!tile0) wait_vm(NDMA);                     // this tile's K landed (its V may be in flight)
+    wg_barrier();
+    u32x4_t kr[2 * KS];
+    read_k_tile<D>(kaddr, kr);
+    wg_barrier();                                  // both waves hold K: refill the K buffer
+    if (next >= 0) issue_k(p.k + nkv, next);
+    f32x16_t sacc[2];
+    const float mx = tile_scores_rt<D>(kr, qreg, sacc, q_local, hl, c, diag);
+    if (qn) load_q(it1, qreg);                     // qreg is free once the scores are issued
+    if (!tile0) wait_vm((next >= 0 ? NDMA : 0) + (qn ? KS : 0));   // this tile's V landed
+    wg_barrier();
+    u32x2_t vr[8 * MT];
+    read_v_tile<D>(vaddr, vr);
+    wg_barrier();                                  // both waves hold V: refill the V buffer
+    if (next >= 0) issue_v(p.v + nkv, next);
+    tile_update<D>(sacc, vr, mx, c, m, lsum, oacc);
+  };
+
+  // ---- prologue: the first item is started cold ---------------------------
+  uint32_t fa0, fa1, fb0, fb1;                     // mask bytes: this item, the next one
+  load_flags(it, fa0, fa1);
+  load_flags(it1, fb0, fb1);
+  wait_vm(0);
+  uint64_t f0 = __builtin_amdgcn_ballot_w64(fa0 != 0), f1 = __builtin_amdgcn_ballot_w64(fa1 != 0);
+  bool warm = false;                               // the item's Q and first tile were issued during the previous one
+
+  while (true) {
+    // ---- item start ------------------------------------------------------
+    const int c0 = it.c * p.chunk;
+    const size_t kvo = kv_head(it);
+    int kb = first_tile(it, f0, f1);
+    if (kb >= 0) {
+      const int d = kb - c0;
+      if (d < 64) f0 &= ~(1ull << d);
+      else f1 &= ~(1ull << (d - 64));
+    }
+    if (!warm) {
+      load_q(it, qreg);
+      if (kb >= 0) {
+        issue_k(p.k + kvo, kb);
+        issue_v(p.v + kvo, kb);
+      }
+    }
+    wait_vm(0);                                    // everything issued so far has landed
+    const uint64_t g0 = __builtin_amdgcn_ballot_w64(fb0 != 0), g1 = __builtin_amdgcn_ballot_w64(fb1 != 0);
+    if (claimed) {                                 // the claim issued at the previous item's start
+      if (tid == 0) claim = pend;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      wg_barrier();
+      j2 = __builtin_amdgcn_readfirstlane(static_cast<int>(lds_read_u32(lds_addr(&claim))));
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      wg_barrier();                                // both waves hold it before the LDS word is reused
+    }
+    const XcdItem it2 = xcd_item(p, x, j2, cur);
+    load_flags(it2, fb0, fb1);                     // the item after next; read at the next item's start
+    claimed = it2.bh >= 0;
+    if (claimed && tid == 0) pend = atomicAdd(ctr, 1);
+    const int kb1 = it1.bh >= 0 ? first_tile(it1, g0, g1) : -1;
+    const size_t kvo1 = it1.bh >= 0 ? kv_head(it1) : 0;
+
+    // ---- tiles: the diagonal first, then ascending; the last one hands over
+    // to the next item (its first tile's copies and its Q rows)
+    warm = false;
+    if (kb >= 0) {
+      bool tile0 = true;
+      bool diag = kb == it.qb;
+      int next = pop_flag(f0, f1, c0);
+      while (next >= 0) {
+        compute(diag, tile0, kvo, next, false);
+        tile0 = false;
+        diag = false;
+        next = pop_flag(f0, f1, c0);
+      }
+      warm = it1.bh >= 0;
+      compute(diag, tile0, warm ? kvo1 : kvo, warm ? kb1 : -1, warm);
+    }
+
+    // ---- epilogue ----------------------------------------------------------
+    const float ltot = pair_sum(lsum);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const float lse2 = ltot > 0.f ? m + __log2f(ltot) : -INFINITY;
+    if (it.qb >= p.chunk) {
+      // normalized bf16 partial in register order (value 16 mt + r of the
+      // thread is oacc[mt][r]) and its log2-sum-exp
+      const long long slot = static_cast<long long>(it.bh) * p.slots_per_head +
+                             xcd_slot_base(it.qb, p.chunk) + it.c;
+      uint4* po = reinterpret_cast<uint4*>(p.part_o16 + (slot * kBlock * D) + static_cast<long long>(tid) * HALF);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          po[2 * mt + h2] = make_uint4(pack_bf16x2(oacc[mt][8 * h2 + 0] * inv, oacc[mt][8 * h2 + 1] * inv),
+                                       pack_bf16x2(oacc[mt][8 * h2 + 2] * inv, oacc[mt][8 * h2 + 3] * inv),
+                                       pack_bf16x2(oacc[mt][8 * h2 + 4] * inv, oacc[mt][8 * h2 + 5] * inv),
+                                       pack_bf16x2(oacc[mt][8 * h2 + 6] * inv, oacc[mt][8 * h2 + 7] * inv));
+      if (hl == 0) p.part_l[slot * kBlock + q_local] = lse2;
+    } else {
+      const int t = it.qb * kBlock + q_local;
+      if (t < p.S) {
+        const size_t obase = (static_cast<size_t>(it.bh) * p.hs + t) * D;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int dim = 32 * mt + 8 * r4 + 4 * hl;
+            const float o0 = oacc[mt][4 * r4 + 0] * inv, o1 = oacc[mt][4 * r4 + 1] * inv;
+            const float o2 = oacc[mt][4 * r4 + 2] * inv, o3 = oacc[mt][4 * r4 + 3] * inv;
+            if (p.out_bf16) {
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + obase + dim) =
+                  make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+            } else {
+              *reinterpret_cast<float4*>(static_cast<float*>(p.out) + obase + dim) = make_float4(o0, o1, o2, o3);
+            }
+          }
+        }
+        if (p.lse != nullptr && hl == 0) p.lse[static_cast<size_t>(it.bh) * p.hs + t] = lse2 * kLn2;
+      }
+    }
+    m = -INFINITY;
+    lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) oacc[i] = f32x16_t{};
+
+    if (it1.bh < 0) break;
+    it = it1;
+    it1 = it2;
+    f0 = g0;
+    f1 = g1;
+  }
+}
+
+// Per-XCD item counters of attn_sparse_xcd_kernel start at 0 on every call.
+__global__ void attn_xcd_counters_init(int* ctr) {
+  if (threadIdx.x < kXcds) ctr[threadIdx.x] = 0;
+}
+
+// Merge of the bf16 partials written by attn_sparse_xcd_kernel:
+// O = sum_c w_c O_c / sum_c w_c, w_c = 2^(L_c - max L), LSE = max L + log2(sum w).
+// One workgroup per row qb >= C, thread layout as in the writer. The slots are
+// read kXcdMergeBatch at a time, all loads of a batch issued before any is
+// used, so the merge runs at memory bandwidth rather than one latency per slot.
+constexpr int kXcdMergeBatch = 4;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_xcd_combine_kernel(AttnArgs p) {
+  constexpr int MT = D / 32;
+  constexpr int HALF = D / 2;
+  constexpr int NV = HALF / 8;                     // 16-byte loads per thread and slot
+  const int rows = p.nb - p.chunk;
+  const int bh = blockIdx.x / rows;
+  const int qb = p.chunk + static_cast<int>(blockIdx.x % rows);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int q_local = wave * 32 + l32;
+  const int n = qb / p.chunk + 1;
+  const long long slot0 = static_cast<long long>(bh) * p.slots_per_head + xcd_slot_base(qb, p.chunk);
+  const float* lse = p.part_l + slot0 * kBlock + q_local;
+  float lmax = -INFINITY;
+  for (int c0 = 0; c0 < n; c0 += 2 * kXcdMergeBatch) {
+    float l[2 * kXcdMergeBatch];
+#pragma unroll
+    for (int u = 0; u < 2 * kXcdMergeBatch; ++u) l[u] = c0 + u < n ? lse[(c0 + u) * kBlock] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2 * kXcdMergeBatch; ++u) lmax = fmaxf(lmax, l[u]);
+  }
+  float acc[HALF];
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) acc[i] = 0.f;
+  float wsum = 0.f;
+  if (lmax > -INFINITY) {
+    const uint4* src = reinterpret_cast<const uint4*>(p.part_o16 + slot0 * kBlock * D) + tid * NV;
+    for (int c0 = 0; c0 < n; c0 += kXcdMergeBatch) {
+      uint4 v[kXcdMergeBatch][NV];
+      float w[kXcdMergeBatch];
+#pragma unroll
+      for (int u = 0; u < kXcdMergeBatch; ++u) {
+        const bool ok = c0 + u < n;
+        const int cc = ok ? c0 + u : c0;           // a slot that exists; its weight is 0 below
+        w[u] = ok ? lse[cc * kBlock] : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[u][i] = src[static_cast<long long>(cc) * (kBlock * D / 8) + i];
+      }
+#pragma unroll
+      for (int u = 0; u < kXcdMergeBatch; ++u) {
+        const float wu = __builtin_amdgcn_exp2f(w[u] - lmax);
+        wsum += wu;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          const uint32_t wd[4] = {v[u][i].x, v[u][i].y, v[u][i].z, v[u][i].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[8 * i + 2 * e] = fmaf(wu, __uint_as_float(wd[e] << 16), acc[8 * i + 2 * e]);
+            acc[8 * i + 2 * e + 1] = fmaf(wu, __uint_as_float(wd[e] & 0xffff0000u), acc[8 * i + 2 * e + 1]);
+          }
+        }
+      }
+    }
+  }
+  const int t = qb * kBlock + q_local;
+  if (t >= p.S) return;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const size_t obase = (static_cast<size_t>(bh) * p.hs + t) * D;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int dim = 32 * mt + 8 * r4 + 4 * hl;
+      const float* a = acc + 16 * mt + 4 * r4;
+      if (p.out_bf16) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + obase + dim) =
+            make_uint2(pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv));
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + obase + dim) =
+            make_float4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);
+      }
+    }
+  }
+  if (p.lse != nullptr && hl == 0)
+    p.lse[static_cast<size_t>(bh) * p.hs + t] = wsum > 0.f ? (lmax + __log2f(wsum)) * kLn2 : -INFINITY;
+}
+
 // Merge the per-chunk partials of rows spanning several key chunks:
 // O = sum_c w_c O_c / sum_c w_c, w_c = 2^(L_c - max L), LSE = max L + log2(sum w).
 // One workgroup per such row; thread t handles query t/4, dims 32*(t%4) ...
@@ -641,6 +1172,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs p) {
 template <int D>
 hipError_t launch_d(const AttnArgs& a, int mode, hipStream_t st) {
   const dim3 block(kThreads);
+  if (mode == kSparse && a.xcd) {
+    hipLaunchKernelGGL(attn_xcd_counters_init, dim3(1), dim3(kWave), 0, st, a.xcd_ctr);
+    hipLaunchKernelGGL((attn_sparse_xcd_kernel<D>), dim3(kXcds * kXcdSlots), block, 0, st, a);
+    if (a.nb > a.chunk) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const dim3 cgrid(static_cast<unsigned>(a.B) * a.Hq * (a.nb - a.chunk));
+      hipLaunchKernelGGL((attn_xcd_combine_kernel<D>), cgrid, block, 0, st, a);
+    }
+    return hipGetLastError();
+  }
   if (mode == kSparse) {
     const dim3 grid(static_cast<unsigned>(static_cast<long long>(a.B) * a.Hkv * a.items_per_group));
     hipLaunchKernelGGL((attn_fwd_kernel<D, kSparse>), grid, block, 0, st, a);
@@ -660,11 +1202,12 @@ hipError_t launch_d(const AttnArgs& a, int mode, hipStream_t st) {
 
 }  // namespace
 
-// Key blocks per chunk of the block-sparse work items. Up to 1024 blocks
-// (64k tokens) a row is one item; longer rows are cut into chunks of 512
-// blocks, which the XCDs sweep together. SEER_ATTN_CHUNK overrides the chunk
-// (rounded to a multiple of 16, at most the on-chip list capacity).
-int sparse_chunk_blocks(int nb) {
+namespace {
+// Key blocks per chunk of the other block-sparse path. Up to 1024 blocks (64k
+// tokens) a row is one item; longer rows are cut into chunks of 512 blocks,
+// which the XCDs sweep together. SEER_ATTN_CHUNK overrides the chunk (rounded
+// to a multiple of 16, at most the on-chip list capacity).
+int sweep_chunk_blocks(int nb) {
   static const int forced = [] {
     const char* v = getenv("SEER_ATTN_CHUNK");
     if (v == nullptr) return 0;
@@ -676,27 +1219,54 @@ int sparse_chunk_blocks(int nb) {
   if (forced) return forced;
   return nb > 1024 ? 512 : kListCap;
 }
+}  // namespace
 
-// Circular sweep of each row's tiles (on by default; SEER_ATTN_ROTATE=0 turns
-// it off). It changes only the order in which a row's tiles are accumulated.
-int sparse_rotate(int nchunk) {
-  (void)nchunk;
-  static const int forced = [] {
+// The XCD-owned path takes rows of at least kXcdMinBlocks blocks when there
+// are at least 64 (batch, KV group, chunk) jobs to deal over the 8 XCDs (it
+// measured 1-3% faster than the other path from 80k tokens up, slower at 64k
+// and below, where fewer K/V re-reads miss the L2); otherwise the rows go to
+// attn_fwd_kernel (cut into chunks of 512 blocks above 1024 blocks, with the
+// circular sweep). SEER_ATTN_XCD=0 / 1 forces the choice (1: whenever rows
+// reach a second chunk), SEER_XCD_CHUNK sets its chunk (16..128) and
+// SEER_ATTN_ROTATE=0 turns the sweep off.
+SparsePlan sparse_plan(int B, int Hkv, int group, int nb, int D) {
+  static const int forced_xcd = [] {
+    const char* v = getenv("SEER_ATTN_XCD");
+    return v == nullptr ? -1 : (atoi(v) != 0);
+  }();
+  static const int forced_rotate = [] {
     const char* v = getenv("SEER_ATTN_ROTATE");
     return v == nullptr ? -1 : (atoi(v) != 0);
   }();
-  return forced >= 0 ? forced : 1;
-}
-
-long long sparse_items_per_group(int nb, int group, int chunk) {
-  const long long nc = (nb + chunk - 1) / chunk;
-  return static_cast<long long>(group) * (nc * nb - static_cast<long long>(chunk) * nc * (nc - 1) / 2);
-}
-
-size_t sparse_workspace_bytes(int B, int Hkv, int group, int nb, int D, int chunk) {
-  if (nb <= chunk) return 0;
-  const size_t items = static_cast<size_t>(B) * Hkv * sparse_items_per_group(nb, group, chunk);
-  return items * kBlock * (static_cast<size_t>(D) + 1) * sizeof(float);
+  static const int xcd_chunk = [] {
+    const char* v = getenv("SEER_XCD_CHUNK");
+    int x = v == nullptr ? kXcdDefaultChunk : atoi(v);
+    return x < 16 ? 16 : (x > kXcdMaxChunk ? kXcdMaxChunk : x);
+  }();
+  SparsePlan pl{};
+  const int C = xcd_chunk;
+  const long long nch = (nb + C - 1) / C;
+  const long long jobs = static_cast<long long>(B) * Hkv * nch;
+  pl.xcd = forced_xcd >= 0 ? (forced_xcd && nb > C) : (nb >= kXcdMinBlocks && jobs >= 64);
+  if (pl.xcd) {
+    pl.chunk = C;
+    pl.nchunk = static_cast<int>(nch);
+    pl.njobs = static_cast<int>(jobs);
+    pl.slots_per_head = xcd_slot_base(nb, C);
+    const size_t slots = static_cast<size_t>(B) * Hkv * group * pl.slots_per_head;
+    pl.workspace_bytes = slots * kBlock * (static_cast<size_t>(D) * sizeof(uint16_t) + sizeof(float)) + 256;
+    return pl;
+  }
+  pl.chunk = sweep_chunk_blocks(nb);
+  pl.nchunk = (nb + pl.chunk - 1) / pl.chunk;
+  pl.rotate = forced_rotate >= 0 ? forced_rotate : 1;
+  const long long nc = pl.nchunk;
+  pl.items_per_group = static_cast<long long>(group) * (nc * nb - static_cast<long long>(pl.chunk) * nc * (nc - 1) / 2);
+  if (nb > pl.chunk) {
+    const size_t items = static_cast<size_t>(B) * Hkv * pl.items_per_group;
+    pl.workspace_bytes = items * kBlock * (static_cast<size_t>(D) + 1) * sizeof(float);
+  }
+  return pl;
 }
 
 hipError_t launch_attn(const AttnArgs& a, int mode, hipStream_t st) {

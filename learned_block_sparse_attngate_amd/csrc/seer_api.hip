@@ -490,9 +490,9 @@ seer_status seer_gate_distill_bwd(const seer_shape* shape, int32_t gate_dim, int
 size_t seer_attn_workspace_size(const seer_shape* shape) {
   bool empty = false;
   if (check_shape(shape, &empty) != SEER_OK || empty) return 0;
-  return seer::sparse_workspace_bytes(shape->batch, shape->heads_kv, shape->heads_q / shape->heads_kv,
-                                      static_cast<int>(nblocks(shape)), shape->head_dim,
-                                      seer::sparse_chunk_blocks(static_cast<int>(nblocks(shape))));
+  return seer::sparse_plan(shape->batch, shape->heads_kv, shape->heads_q / shape->heads_kv,
+                           static_cast<int>(nblocks(shape)), shape->head_dim)
+      .workspace_bytes;
 }
 
 static seer_status attn_impl(const seer_shape* shape, long long hs, const void* q, const void* k, const void* v,
@@ -508,20 +508,31 @@ static seer_status attn_impl(const seer_shape* shape, long long hs, const void* 
   if ((st = check_out(out, out_dtype, lse)) != SEER_OK) return st;
   seer::AttnArgs a = attn_args(shape, q, k, v, block_mask ? 0 : 1);
   if (block_mask != nullptr) {
-    a.chunk = seer::sparse_chunk_blocks(a.nb);
-    a.nchunk = (a.nb + a.chunk - 1) / a.chunk;
-    a.rotate = seer::sparse_rotate(a.nchunk);
-    a.items_per_group = seer::sparse_items_per_group(a.nb, a.group, a.chunk);
+    const seer::SparsePlan pl = seer::sparse_plan(a.B, a.Hkv, a.group, a.nb, a.D);
+    a.xcd = pl.xcd;
+    a.chunk = pl.chunk;
+    a.nchunk = pl.nchunk;
+    a.rotate = pl.rotate;
+    a.items_per_group = pl.items_per_group;
+    a.njobs = pl.njobs;
+    a.slots_per_head = pl.slots_per_head;
     const long long items = static_cast<long long>(a.B) * a.Hkv * a.items_per_group;
     if (items > 0x7fffffffLL)
       return fail(SEER_ERR_SHAPE, "%lld block-sparse work items exceed the launch limit", items);
-    const size_t need = seer::sparse_workspace_bytes(a.B, a.Hkv, a.group, a.nb, a.D, a.chunk);
+    const size_t need = pl.workspace_bytes;
     if (need > 0) {
       if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
         return fail(SEER_ERR_WORKSPACE, "workspace must be %zu bytes, 16-byte aligned (got %zu at %p)", need,
                     workspace_bytes, workspace);
-      a.part_o = static_cast<float*>(workspace);
-      a.part_l = a.part_o + static_cast<size_t>(items) * 64 * a.D;
+      if (pl.xcd) {
+        const size_t slots = static_cast<size_t>(a.B) * a.Hq * pl.slots_per_head;
+        a.part_o16 = static_cast<uint16_t*>(workspace);
+        a.part_l = reinterpret_cast<float*>(a.part_o16 + slots * 64 * a.D);
+        a.xcd_ctr = reinterpret_cast<int*>(a.part_l + slots * 64);
+      } else {
+        a.part_o = static_cast<float*>(workspace);
+        a.part_l = a.part_o + static_cast<size_t>(items) * 64 * a.D;
+      }
     }
   }
   if ((st = check_device()) != SEER_OK || !launch) return st;

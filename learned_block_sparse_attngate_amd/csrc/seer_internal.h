@@ -28,18 +28,31 @@ struct AttnArgs {
   int nchunk;          // chunks per sequence = ceil(nb / C)
   long long items_per_group;  // work items per (batch, KV group)
   float* part_o;       // [items][64][D] fp32 normalized partial outputs (rows spanning > 1 chunk)
-  float* part_l;       // [items][64] fp32 partial log2-sum-exp
+  float* part_l;       // [items][64] fp32 partial log2-sum-exp ([slots][64] on the XCD-owned path)
   int rotate;          // block-sparse: walk each row's tiles in the XCD-phased circular order
+  // block-sparse, XCD-owned key chunks (persistent workgroups)
+  int xcd;             // 1: this path (chunk = 128 blocks)
+  int njobs;           // (batch, KV group, chunk) jobs
+  long long slots_per_head;   // partial-output slots per (batch, head)
+  uint16_t* part_o16;  // [B*Hq*slots_per_head][128 threads][D/2] bf16 normalized partials
+  int* xcd_ctr;        // 8 per-XCD item counters (zeroed by the launch)
 };
 
 // mode: 0 block-sparse (mask), 1 dense causal, 2 dense causal + ground-truth maxima
 hipError_t launch_attn(const AttnArgs& a, int mode, hipStream_t st);
 
-// Key-chunked block-sparse work: chunk size, item counts and workspace bytes.
-int sparse_chunk_blocks(int nb);
-int sparse_rotate(int nchunk);
-long long sparse_items_per_group(int nb, int group, int chunk);
-size_t sparse_workspace_bytes(int B, int Hkv, int group, int nb, int D, int chunk);
+// Work plan of the block-sparse kernel for one shape: which path, key chunks,
+// item / slot counts and the workspace it needs.
+struct SparsePlan {
+  int xcd;                    // XCD-owned key chunks with persistent workgroups
+  int chunk, nchunk;
+  int rotate;                 // circular sweep (rows cut into chunks, other path)
+  long long items_per_group;  // other path: (row, chunk) items per (batch, KV group)
+  int njobs;                  // XCD path: (batch, KV group, chunk) jobs
+  long long slots_per_head;   // XCD path: partial slots per (batch, head)
+  size_t workspace_bytes;
+};
+SparsePlan sparse_plan(int B, int Hkv, int group, int nb, int D);
 
 struct GateArgs {
   const uint16_t* q;   // bf16 [B,Hq,S,D]

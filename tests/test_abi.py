@@ -234,6 +234,15 @@ def test_workspace_sizes():
     assert lib.seer_attn_workspace_size(ctypes.byref(s3)) == 0
     s4 = _shape(b=1, hq=2, hkv=1, s=64 * 1024 + 1, d=64)
     assert lib.seer_attn_workspace_size(ctypes.byref(s4)) == 2 * (1025 + 513 + 1) * 64 * 65 * 4
+    # rows of >= 1280 blocks with >= 64 (batch, KV group, 128-block chunk) jobs
+    # take the XCD-owned path: rows qb >= 128 own qb // 128 + 1 slots of a
+    # 64 x D bf16 partial and 64 fp32 log-sum-exps; 256 bytes of item counters
+    for nb5, d5 in ((1300, 128), (2048, 64)):
+        s5 = _shape(b=1, hq=16, hkv=8, s=64 * nb5 - 3, d=d5)
+        slots = sum(q // 128 + 1 for q in range(128, nb5))
+        assert lib.seer_attn_workspace_size(ctypes.byref(s5)) == 16 * slots * 64 * (2 * d5 + 4) + 256
+    s6 = _shape(b=1, hq=4, hkv=2, s=64 * 1300, d=128)             # 2 x 11 jobs: the other path
+    assert lib.seer_attn_workspace_size(ctypes.byref(s6)) == 4 * (1300 + 788 + 276) * 64 * 129 * 4
     assert lib.seer_gt_workspace_size(ctypes.byref(s)) == align(2 * 4 * (nb * (nb + 1) // 2) * 64 * 4)
     want = (align(2 * 4 * nb * 64 * 4) + align(2 * 2 * nb * 192 * 4) + align(2 * 4 * nb * 32 * 4)
             + align(2 * 4 * nb * 32 * 4))

@@ -178,6 +178,54 @@ def test_sparse_multichunk_all_ones_matches_dense():
     check_lse(host(la), host(lb), "all-ones vs dense LSE", tol=1e-4)
 
 
+XCD_CASES = [
+    # rows of >= 1280 blocks and >= 64 (batch, KV group, 128-block chunk) jobs:
+    # the XCD-owned persistent path with bf16 partials
+    ("d64_s83183_g2_f32", Shape(1, 16, 8, 64 * 1300 - 17, 64), torch.float32),
+    ("d128_s82565_g1_bf16", Shape(1, 8, 8, 64 * 1290 + 5, 128), torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("name,shape,dt", XCD_CASES, ids=[c[0] for c in XCD_CASES])
+def test_sparse_xcd_rows(name, shape, dt):
+    """Rows cut into 128-block key chunks owned by XCDs (persistent workgroups,
+    bf16 partials, merge kernel): chunk-boundary rows, a ragged last block, an
+    empty row, rows active only in their first chunk, only on the diagonal,
+    only in the first and last chunk (empty chunks between), with a full chunk,
+    and without the diagonal."""
+    seed = 60 + shape.head_dim
+    nb = shape.nb
+    m = synth.gen_block_mask(shape, seed + 1, 0.85).mask.copy()
+    m[0, 1, nb - 1, :] = 0                       # no active key at all: O = 0, LSE = -inf
+    m[0, 2, nb - 2, :] = 0
+    m[0, 2, nb - 2, :5] = 1                      # only the first chunk contributes
+    m[0, 3, 600, :] = 0
+    m[0, 3, 600, 600] = 1                        # only the diagonal (in the fifth chunk)
+    m[0, 4, nb - 3, :] = 0
+    m[0, 4, nb - 3, [0, 3, nb - 5, nb - 3]] = 1  # first and last chunk only
+    m[0, 5, 700, 256:384] = 1                    # one whole chunk active
+    m[0, 6, 900, 900] = 0                        # diagonal off
+    m = synth.gen_random_upper_noise(m, seed + 2)
+    rows = sample_rows(shape.batch, shape.heads_q, nb, 2, seed + 3)
+    rows += [(0, h, x) for h in (0, shape.heads_q - 1) for c in range(128, nb, 128) for x in (c - 1, c, c + 1)]
+    rows += [(0, 1, nb - 1), (0, 2, nb - 2), (0, 3, 600), (0, 4, nb - 3), (0, 5, 700), (0, 6, 900)]
+    _run_sampled(shape, seed, m, dt, sorted(set(rows)), name)
+
+
+def test_sparse_xcd_all_ones_matches_dense():
+    """An all-ones mask through the XCD-owned path agrees with the dense kernel
+    to the rounding of its bf16 partial outputs (2^-9 relative per chunk)."""
+    seer = _seer()
+    shape = Shape(1, 8, 8, 64 * 1290, 128)
+    q, k, v = (dev_bf16(x) for x in synth.gen_qkv(shape, 45))
+    ones = torch.ones((1, 8, shape.nb, shape.nb), dtype=torch.uint8, device="cuda")
+    a, la = seer.seer_block_sparse_attn_fwd(q, k, v, ones, out_dtype=torch.float32, want_lse=True)
+    b, lb = seer.seer_block_sparse_attn_fwd(q, k, v, None, out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    check_close(host(a), host(b), "xcd all-ones vs dense O", max_abs=2e-3, mean_abs=1e-4)
+    check_lse(host(la), host(lb), "xcd all-ones vs dense LSE", tol=1e-4)
+
+
 @pytest.mark.parametrize("name", ["llama8b_s32k_90", "llama8b_s128k_90"])
 def test_workload_sampled(name):
     """The Llama-3.1-8B-shaped layers at full length with their seeded masks, in
@@ -187,6 +235,6 @@ def test_workload_sampled(name):
     shape = w["shape"]
     minfo = synth.workload_mask(name)
     rows = sample_rows(shape.batch, shape.heads_q, shape.nb, 1, 9)
-    extra = [x for c in range(512, shape.nb, 512) for x in (c - 1, c)]
+    extra = [x for c in range(128, shape.nb, 128) for x in (c - 1, c)]
     rows = sorted(set(rows) | {(0, 5, x) for x in extra})
     _run_sampled(shape, w["seed"], minfo.mask, torch.bfloat16, rows, name)

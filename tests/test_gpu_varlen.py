@@ -21,20 +21,20 @@ def _seer():
     return seer
 
 
-def _pack(lens, D, seed):
+def _pack(lens, D, seed, hq=HQ, hkv=HKV):
     """Per-sequence bf16 q, k, v ([1, H, len, D]) and their packed [H, T, D] forms."""
     seqs = []
     for i, n in enumerate(lens):
         if n == 0:
             seqs.append(None)
             continue
-        q, k, v = synth.gen_qkv(Shape(1, HQ, HKV, n, D), seed + i)
+        q, k, v = synth.gen_qkv(Shape(1, hq, hkv, n, D), seed + i)
         seqs.append((q, k, v))
     def cat(idx, H):
         parts = [s[idx][0] for s in seqs if s is not None]
         return np.ascontiguousarray(np.concatenate(parts, axis=1)) if parts else np.zeros((H, 0, D), np.uint16)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(int).tolist()
-    return seqs, cat(0, HQ), cat(1, HKV), cat(2, HKV), cu
+    return seqs, cat(0, hq), cat(1, hkv), cat(2, hkv), cu
 
 
 def _masks(lens, seed, p):
@@ -104,6 +104,36 @@ def test_varlen_long_sequence_key_chunks():
     q2, k2, v2 = seqs[1]
     o2, _ = oracle.attention(q2, k2, v2, masks[1][None])
     check_close(o_h[:, cu[1]:cu[2]][None], o2, "short seq O")
+
+
+def test_varlen_long_sequence_xcd_path():
+    """A sequence of 1300 blocks with 8 KV heads (the XCD-owned path: 128-block
+    chunks, per-XCD item counters, bf16 partials) packed after a short one, so
+    the long sequence's rows start at a nonzero packed offset."""
+    seer = _seer()
+    hq = hkv = 8
+    lens = [2000, 64 * 1300 - 9]
+    seqs, qp, kp, vp, cu = _pack(lens, 64, 310, hq, hkv)
+    say(f"[varlen xcd] lens={lens}")
+    masks = [synth.gen_block_mask(Shape(1, hq, hkv, n, 64), 311 + i, 0.9).mask[0] for i, n in enumerate(lens)]
+    flat = np.concatenate([m.reshape(-1) for m in masks])
+    out, lse = seer.seer_block_sparse_attn_varlen_fwd(dev_bf16(qp), dev_bf16(kp), dev_bf16(vp), cu, dev_u8(flat),
+                                                      out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    o_h, l_h = host(out), host(lse)
+    q, k, v = seqs[1]
+    nb = (lens[1] + 63) // 64
+    rows = [(0, h, i) for h in (0, 5, 7) for i in (0, 127, 128, 129, 640, 1279, 1280, nb - 1)]
+    o_ref, l_ref = oracle.attention_rows(q, k, v, masks[1][None], rows)
+    base = cu[1]
+    got = np.concatenate([o_h[h, base + 64 * i:base + 64 * i + 64][: len(o_ref[n])] for n, (_, h, i) in enumerate(rows)])
+    got_l = np.concatenate([l_h[h, base + 64 * i:base + 64 * i + 64][: len(l_ref[n])]
+                            for n, (_, h, i) in enumerate(rows)])
+    check_close(got, np.concatenate(o_ref), "xcd long seq O (sampled)")
+    check_lse(got_l, np.concatenate(l_ref), "xcd long seq LSE (sampled)")
+    q0, k0, v0 = seqs[0]
+    o0, _ = oracle.attention(q0, k0, v0, masks[0][None])
+    check_close(o_h[:, cu[0]:cu[1]][None], o0, "short seq O")
 
 
 def test_varlen_gate_and_gt():
