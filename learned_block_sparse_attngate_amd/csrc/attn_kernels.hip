@@ -967,19 +967,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     const float lse2 = ltot > 0.f ? m + __log2f(ltot) : -INFINITY;
     if (it.qb >= p.chunk) {
-      // normalized bf16 partial in register order (value 16 mt + r of the
-      // thread is oacc[mt][r]) and its log2-sum-exp
+      // normalized bf16 partial: the thread's 8-value group g (oacc[g / 2]
+      // values 8 (g % 2) ..) is 16 bytes at uint4 index g * kThreads + tid of
+      // the slot, so each store instruction writes 1 KiB contiguous
       const long long slot = static_cast<long long>(it.bh) * p.slots_per_head +
                              xcd_slot_base(it.qb, p.chunk) + it.c;
-      uint4* po = reinterpret_cast<uint4*>(p.part_o16 + (slot * kBlock * D) + static_cast<long long>(tid) * HALF);
+      uint4* po = reinterpret_cast<uint4*>(p.part_o16 + slot * kBlock * D) + tid;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
-          po[2 * mt + h2] = make_uint4(pack_bf16x2(oacc[mt][8 * h2 + 0] * inv, oacc[mt][8 * h2 + 1] * inv),
-                                       pack_bf16x2(oacc[mt][8 * h2 + 2] * inv, oacc[mt][8 * h2 + 3] * inv),
-                                       pack_bf16x2(oacc[mt][8 * h2 + 4] * inv, oacc[mt][8 * h2 + 5] * inv),
-                                       pack_bf16x2(oacc[mt][8 * h2 + 6] * inv, oacc[mt][8 * h2 + 7] * inv));
+          po[(2 * mt + h2) * kThreads] =
+              make_uint4(pack_bf16x2(oacc[mt][8 * h2 + 0] * inv, oacc[mt][8 * h2 + 1] * inv),
+                         pack_bf16x2(oacc[mt][8 * h2 + 2] * inv, oacc[mt][8 * h2 + 3] * inv),
+                         pack_bf16x2(oacc[mt][8 * h2 + 4] * inv, oacc[mt][8 * h2 + 5] * inv),
+                         pack_bf16x2(oacc[mt][8 * h2 + 6] * inv, oacc[mt][8 * h2 + 7] * inv));
       if (hl == 0) p.part_l[slot * kBlock + q_local] = lse2;
     } else {
       const int t = it.qb * kBlock + q_local;
@@ -1023,7 +1025,7 @@ __global__ void attn_xcd_counters_init(int* ctr) {
 
 // Merge of the bf16 partials written by attn_sparse_xcd_kernel:
 // O = sum_c w_c O_c / sum_c w_c, w_c = 2^(L_c - max L), LSE = max L + log2(sum w).
-// One workgroup per row qb >= C, thread layout as in the writer. The slots are
+// One workgroup per row qb >= C, thread and value layout as in the writer. The slots are
 // read kXcdMergeBatch at a time, all loads of a batch issued before any is
 // used, so the merge runs at memory bandwidth rather than one latency per slot.
 constexpr int kXcdMergeBatch = 4;
@@ -1055,7 +1057,7 @@ __global__ __launch_bounds__(kThreads) void attn_xcd_combine_kernel(AttnArgs p) 
   for (int i = 0; i < HALF; ++i) acc[i] = 0.f;
   float wsum = 0.f;
   if (lmax > -INFINITY) {
-    const uint4* src = reinterpret_cast<const uint4*>(p.part_o16 + slot0 * kBlock * D) + tid * NV;
+    const uint4* src = reinterpret_cast<const uint4*>(p.part_o16 + slot0 * kBlock * D) + tid;
     for (int c0 = 0; c0 < n; c0 += kXcdMergeBatch) {
       uint4 v[kXcdMergeBatch][NV];
       float w[kXcdMergeBatch];
@@ -1065,7 +1067,7 @@ __global__ __launch_bounds__(kThreads) void attn_xcd_combine_kernel(AttnArgs p) 
         const int cc = ok ? c0 + u : c0;           // a slot that exists; its weight is 0 below
         w[u] = ok ? lse[cc * kBlock] : -INFINITY;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) v[u][i] = src[static_cast<long long>(cc) * (kBlock * D / 8) + i];
+        for (int i = 0; i < NV; ++i) v[u][i] = src[static_cast<long long>(cc) * (kBlock * D / 8) + i * kThreads];
       }
 #pragma unroll
       for (int u = 0; u < kXcdMergeBatch; ++u) {

@@ -34,7 +34,7 @@ struct AttnArgs {
   int xcd;             // 1: this path (chunk = 128 blocks)
   int njobs;           // (batch, KV group, chunk) jobs
   long long slots_per_head;   // partial-output slots per (batch, head)
-  uint16_t* part_o16;  // [B*Hq*slots_per_head][128 threads][D/2] bf16 normalized partials
+  uint16_t* part_o16;  // [B*Hq*slots_per_head][D/16 groups][128 threads][8] bf16 normalized partials
   int* xcd_ctr;        // 8 per-XCD item counters (zeroed by the launch)
 };
 
