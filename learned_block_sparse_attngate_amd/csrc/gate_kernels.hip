@@ -22,9 +22,13 @@
 //  gate_gemm        fp32 LDS-tiled GEMM (64 x 64 tiles, 4 x 4 per thread),
 //                   used for the two projections and for the causal tiles of
 //                   the block logits Q' K'^T.
-//  gate_softmax_mask one workgroup per score row: max / sum reductions, the
-//                   normalized row, and either the threshold or an exact
-//                   4-pass radix select for top-k (ties to the lower index).
+//  gate_softmax_mask_wave
+//                   one wavefront per score row (rows up to 4096 blocks), the
+//                   row in registers: max / sum reductions, the normalized
+//                   row, and either the threshold or the exact k-th largest
+//                   for top-k (exponent by ballot counts, mantissa by radix
+//                   passes; ties to the lower index).
+//  gate_softmax_mask the same with one workgroup per row, for longer rows.
 //  gate_rope        in-place block-level RoPE of Q' / K' (fp64 angles).
 //  gate_kl, gate_dproj, gate_dweight, gate_loss
 //                   the distillation step: KL rows and dz, dQ' / dK' GEMMs,
@@ -359,6 +363,213 @@ __global__ __launch_bounds__(kST) void gate_softmax_mask_kernel(GateArgs a, Topk
                    tk.k[z % a.Hq]);
 }
 
+// This wave's LDS accesses so far have completed, and the compiler moves no
+// memory access across the point.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ int wave_max_int(int x) {
+  for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off, kWave));
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum_int(int x) {
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+// Same row computation as gate_softmax_mask_kernel with one wavefront per row
+// and the row in registers: lane l holds elements 256 t + 4 l + e (t < G,
+// e < 4), so each load and store instruction covers 1 KiB of scores (256 B of
+// mask) contiguous. Four independent rows per workgroup and no workgroup
+// barrier: the reductions are cross-lane, the radix select's histogram is a
+// per-wave LDS array. Rows up to 256 G blocks.
+//
+// Each element is carried as the bit pattern of its probability, with the
+// entries past the causal end as -0.0 (sign bit set): no probability has that
+// bit, so those entries never match a radix prefix (whose mask includes the
+// sign bit) and compare below every probability as signed integers, and all
+// the later steps are integer compares on the keys alone.
+template <int G>
+__global__ __launch_bounds__(256) void gate_softmax_mask_wave_kernel(GateArgs a, TopkTable tk) {
+  __shared__ __align__(16) uint32_t hist_all[4][256];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long long row = static_cast<long long>(blockIdx.x) * 4 + wave;
+  if (row >= static_cast<long long>(a.B) * a.Hq * a.nb) return;
+  const int nb = a.nb;
+  const int z = static_cast<int>(row / nb), i = static_cast<int>(row - static_cast<long long>(z) * nb);
+  const int n = i + 1;                                  // causal entries of this row
+  float* srow = a.scores + static_cast<size_t>(row) * nb;
+  uint8_t* mrow = a.mask + static_cast<size_t>(row) * nb;
+  const bool vec = (nb & 3) == 0;                       // rows start 16-byte aligned
+
+  float v[G][4];                                        // logits; -inf past the causal end
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    const int j0 = 256 * t + 4 * lane;
+    if (vec && j0 + 3 < n) {
+      const float4 x = *reinterpret_cast<const float4*>(srow + j0);
+      v[t][0] = x.x; v[t][1] = x.y; v[t][2] = x.z; v[t][3] = x.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[t][e] = j0 + e < n ? srow[j0 + e] : -INFINITY;
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < G; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, v[t][e]);
+  mx = wave_max(mx);
+  float sum = 0.f;
+#pragma unroll
+  for (int t = 0; t < G; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = v[t][e] == -INFINITY ? -0.0f : expf(v[t][e] - mx);
+      v[t][e] = x;
+      sum += x;
+    }
+  sum = wave_sum(sum);
+  const float inv = 1.0f / sum;
+  uint32_t key[G][4];
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[t][e] = __float_as_uint(v[t][e] * inv);
+    const int j0 = 256 * t + 4 * lane;
+    const float p0 = __uint_as_float(key[t][0] & 0x7fffffffu), p1 = __uint_as_float(key[t][1] & 0x7fffffffu);
+    const float p2 = __uint_as_float(key[t][2] & 0x7fffffffu), p3 = __uint_as_float(key[t][3] & 0x7fffffffu);
+    if (vec) {
+      if (j0 < nb) *reinterpret_cast<float4*>(srow + j0) = make_float4(p0, p1, p2, p3);
+    } else {
+      if (j0 < nb) srow[j0] = p0;
+      if (j0 + 1 < nb) srow[j0 + 1] = p1;
+      if (j0 + 2 < nb) srow[j0 + 2] = p2;
+      if (j0 + 3 < nb) srow[j0 + 3] = p3;
+    }
+  }
+
+  // keep: key > lim as signed integers, plus (top-k) the first kk equal to lim
+  const int k = tk.k[z % a.Hq];
+  int32_t lim = -1;                                     // every causal entry
+  int kk = 0;
+  if (a.mode == 0) {
+    // p > T: bit patterns above T's for T > 0, above +0 for T = 0, every
+    // entry for T < 0, none for a NaN T
+    const float T = a.threshold;
+    lim = T > 0.f ? static_cast<int32_t>(__float_as_uint(T)) : (T == 0.f ? 0 : (T < 0.f ? -1 : INT32_MAX));
+  } else if (k < n) {
+    // exact k-th largest probability (probabilities are >= 0: their bit
+    // patterns order like the values). Its exponent field first, by binary
+    // search on wave-wide counts of keys >= 2^e (ballots, no LDS); then the
+    // mantissa 8 bits at a time from bit 22, with a per-wave LDS histogram in
+    // which lane L owns bins 255-4L .. 252-4L.
+    auto count_ge = [&](int32_t c) {
+      int cnt = 0;
+#pragma unroll
+      for (int t = 0; t < G; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(static_cast<int32_t>(key[t][e]) >= c));
+      return cnt;
+    };
+    int32_t kmax = INT32_MIN;
+#pragma unroll
+    for (int t = 0; t < G; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kmax = max(kmax, static_cast<int32_t>(key[t][e]));
+    int lo = 0, hi = wave_max_int(kmax) >> 23;          // count(>= 2^lo) = n >= k; the answer is <= hi
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (count_ge(mid << 23) >= k) lo = mid;
+      else hi = mid - 1;
+    }
+    uint32_t* hist = hist_all[wave];
+    uint32_t prefix = static_cast<uint32_t>(lo) << 23, pmask = 0xff800000u;
+    kk = k - count_ge((lo + 1) << 23);                  // how many of the exponent's bin to keep
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass < 2 ? 15 - 8 * pass : 0;
+      const uint32_t width = pass < 2 ? 255u : 127u;
+      *reinterpret_cast<uint4*>(hist + 4 * lane) = make_uint4(0, 0, 0, 0);
+      wave_lds_sync();
+#pragma unroll
+      for (int t = 0; t < G; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((key[t][e] & pmask) == prefix) atomicAdd(&hist[(key[t][e] >> shift) & width], 1u);
+      wave_lds_sync();
+      const uint4 c4 = *reinterpret_cast<const uint4*>(hist + 252 - 4 * lane);
+      const int cnt4[4] = {static_cast<int>(c4.w), static_cast<int>(c4.z), static_cast<int>(c4.y),
+                           static_cast<int>(c4.x)};     // bins 255-4L, 254-4L, 253-4L, 252-4L
+      const int own = cnt4[0] + cnt4[1] + cnt4[2] + cnt4[3];
+      const int inc = wave_inclusive_scan(own, lane);
+      int above = inc - own;                            // count in bins above this lane's
+      int bin = 0, rem = 0;
+      bool found = false;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (above < kk && above + cnt4[e] >= kk) {
+          found = true;
+          bin = 255 - 4 * lane - e;
+          rem = kk - above;
+        }
+        above += cnt4[e];
+      }
+      const int src = static_cast<int>(__builtin_ctzll(__builtin_amdgcn_ballot_w64(found)));
+      bin = __shfl(bin, src, kWave);
+      kk = __shfl(rem, src, kWave);
+      prefix |= static_cast<uint32_t>(bin) << shift;
+      pmask |= width << shift;
+      wave_lds_sync();                                  // the histogram is read before the next pass clears it
+    }
+    lim = static_cast<int32_t>(prefix);
+    // when no more entries equal the k-th value than are kept, keep them all
+    int eq_total = 0;
+#pragma unroll
+    for (int t = 0; t < G; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) eq_total += key[t][e] == prefix;
+    if (wave_sum_int(eq_total) <= kk) {
+      lim -= 1;                                         // > prefix - 1  <=>  >= prefix
+      kk = 0;
+    }
+  }
+  // the kk entries equal to lim with the lowest indices are kept as well
+  int before = 0;                                       // such entries at lower indices
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    uint32_t keep = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) keep |= static_cast<uint32_t>(static_cast<int32_t>(key[t][e]) > lim) << (8 * e);
+    if (kk > 0) {
+      int eq = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) eq += key[t][e] == static_cast<uint32_t>(lim);
+      const int inc = wave_inclusive_scan(eq, lane);
+      int b = before + inc - eq;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (key[t][e] == static_cast<uint32_t>(lim)) {
+          if (b < kk) keep |= 1u << (8 * e);
+          ++b;
+        }
+      before += __shfl(inc, kWave - 1, kWave);
+    }
+    const int j0 = 256 * t + 4 * lane;
+    if (vec) {
+      if (j0 < nb) *reinterpret_cast<uint32_t*>(mrow + j0) = keep;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j0 + e < nb) mrow[j0 + e] = static_cast<uint8_t>(keep >> (8 * e));
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Decode-stage gate ("SeerAttention: Self-distilled Attention Gating for
 // Efficient Long-context Prefilling", responses on decoding): no query
@@ -672,8 +883,17 @@ hipError_t launch_gate_logits(const GateArgs& a, hipStream_t st) {
 hipError_t launch_gate(const GateArgs& a, const TopkTable& tk, hipStream_t st) {
   hipError_t e = launch_gate_logits(a, st);
   if (e != hipSuccess) return e;
-  dim3 gs(a.nb, a.B * a.Hq);
-  hipLaunchKernelGGL(gate_softmax_mask_kernel, gs, dim3(kST), static_cast<size_t>(a.nb) * sizeof(float), st, a, tk);
+  const long long rows = static_cast<long long>(a.B) * a.Hq * a.nb;
+  const dim3 gw(static_cast<unsigned>((rows + 3) / 4));
+  if (a.nb <= 256) hipLaunchKernelGGL(gate_softmax_mask_wave_kernel<1>, gw, dim3(256), 0, st, a, tk);
+  else if (a.nb <= 512) hipLaunchKernelGGL(gate_softmax_mask_wave_kernel<2>, gw, dim3(256), 0, st, a, tk);
+  else if (a.nb <= 1024) hipLaunchKernelGGL(gate_softmax_mask_wave_kernel<4>, gw, dim3(256), 0, st, a, tk);
+  else if (a.nb <= 2048) hipLaunchKernelGGL(gate_softmax_mask_wave_kernel<8>, gw, dim3(256), 0, st, a, tk);
+  else if (a.nb <= 4096) hipLaunchKernelGGL(gate_softmax_mask_wave_kernel<16>, gw, dim3(256), 0, st, a, tk);
+  else {
+    dim3 gs(a.nb, a.B * a.Hq);
+    hipLaunchKernelGGL(gate_softmax_mask_kernel, gs, dim3(kST), static_cast<size_t>(a.nb) * sizeof(float), st, a, tk);
+  }
   return hipGetLastError();
 }
 

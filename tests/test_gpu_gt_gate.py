@@ -104,22 +104,80 @@ def test_gate_topk_matches_oracle(topk):
     sc_ref = oracle.gate_scores(q, k, wq, wk)
     mask, scores = seer.seer_gate_fwd(dev_bf16(q), dev_bf16(k), dev_f32(wq), dev_f32(wk), mode="topk", topk=topk)
     torch.cuda.synchronize()
-    got = mask.cpu().numpy()
-    ks = np.broadcast_to(np.asarray(topk), (4,))
-    nb = shape.nb
+    _check_topk_mask(mask.cpu().numpy(), sc_ref, topk)
+
+
+def _check_topk_mask(got, sc_ref, topk):
+    """Every row keeps exactly min(k, i+1) causal blocks, and agrees with the
+    oracle's top-k except for scores within the band of the row's k-th one."""
+    B, H, nb, _ = sc_ref.shape
+    ks = np.broadcast_to(np.asarray(topk), (H,))
     want = oracle.topk_mask(sc_ref, topk)
     bad = 0
-    for h in range(4):
-        for i in range(nb):
-            kk = min(int(ks[h]), i + 1)
-            assert int(got[0, h, i].sum()) == kk
-            assert not got[0, h, i, i + 1:].any()
-            row = sc_ref[0, h, i, :i + 1]
-            kth = np.sort(row)[::-1][kk - 1]
-            outside = np.abs(row - kth) > MASK_BAND
-            bad += int(((got[0, h, i, :i + 1] != want[0, h, i, :i + 1]) & outside).sum())
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                kk = min(int(ks[h]), i + 1)
+                assert int(got[b, h, i].sum()) == kk, f"row {b},{h},{i}"
+                assert not got[b, h, i, i + 1:].any()
+                row = sc_ref[b, h, i, :i + 1]
+                kth = np.partition(row, i + 1 - kk)[i + 1 - kk]
+                outside = np.abs(row - kth) > MASK_BAND
+                bad += int(((got[b, h, i, :i + 1] != want[b, h, i, :i + 1]) & outside).sum())
     say(f"  top-k {topk}: {bad} mismatches outside the band")
     assert bad == 0
+
+
+# Rows longer than one wavefront's 256-element pass, aligned and not, up to the
+# register-resident limit (4096 blocks) and one past it (a workgroup per row).
+LONG_GATE_CASES = [
+    ("nb300", 300, [7, 150]),
+    ("nb701", 701, [33, 700]),
+    ("nb1500", 1500, [106, 1]),
+    ("nb2100", 2100, [210, 5]),
+    ("nb4100", 4100, [410, 64]),
+]
+
+
+@pytest.mark.parametrize("name,nb,topk", LONG_GATE_CASES, ids=[c[0] for c in LONG_GATE_CASES])
+def test_gate_long_rows_match_oracle(name, nb, topk):
+    seer = _seer()
+    shape = Shape(1, 2, 1, 64 * nb - 5, 64)
+    say(f"[gate long rows {name}] shape={shape} topk={topk}")
+    q, k, wq, wk = _gate_inputs(shape, 66, 64)
+    sc_ref = oracle.gate_scores(q, k, wq, wk)
+    mask, scores = seer.seer_gate_fwd(dev_bf16(q), dev_bf16(k), dev_f32(wq), dev_f32(wk), mode="topk", topk=topk)
+    torch.cuda.synchronize()
+    err = np.abs(host(scores) - sc_ref)
+    say(f"  scores max-abs {err.max():.3e}")
+    assert err.max() < 1e-5
+    _check_topk_mask(mask.cpu().numpy(), sc_ref, topk)
+    T = 1.5 / nb
+    mask_t, _ = seer.seer_gate_fwd(dev_bf16(q), dev_bf16(k), dev_f32(wq), dev_f32(wk), mode="threshold", threshold=T)
+    torch.cuda.synchronize()
+    _check_threshold_mask(mask_t.cpu().numpy(), sc_ref, T, f"T={T:.3e}")
+
+
+@pytest.mark.parametrize("nb", [517, 1101], ids=["nb517", "nb1101"])
+def test_gate_flat_long_rows_keep_lowest_indices(nb):
+    """W_q = 0: every causal score of row i is 1/(i+1), so top-k keeps blocks
+    0 .. k-1 (ties to the lower index, across the row's 256-element passes)."""
+    seer = _seer()
+    shape = Shape(1, 1, 1, 64 * nb, 64)
+    q, k, _ = synth.gen_qkv(shape, 67, want_v=False)
+    wq = np.zeros((1, 64, 64), np.float32)
+    wk = synth.gen_gate_weights(1, 64, 64, 68)[1]
+    kk = 300
+    mask, scores = seer.seer_gate_fwd(dev_bf16(q), dev_bf16(k), dev_f32(wq), dev_f32(wk), mode="topk", topk=kk)
+    torch.cuda.synchronize()
+    m = mask.cpu().numpy()[0, 0]
+    s = host(scores)[0, 0]
+    for i in (0, 255, 256, 299, 300, 511, nb - 1):
+        assert np.all(s[i, :i + 1] == np.float32(1.0) / np.float32(i + 1)) and not s[i, i + 1:].any()
+        want = np.zeros(nb, np.uint8)
+        want[:min(kk, i + 1)] = 1
+        assert np.array_equal(m[i], want), f"row {i}"
+    assert np.array_equal(m.sum(1), np.minimum(kk, np.arange(1, nb + 1)))
 
 
 def test_gate_flat_scores_ties_and_strictness():
