@@ -19,9 +19,10 @@
 // Kernels:
 //  gate_pool        HBM-bound: one workgroup per (head, block) streams the 64
 //                   token rows once with 16-byte loads and reduces in LDS.
-//  gate_gemm        fp32 LDS-tiled GEMM (64 x 64 tiles, 4 x 4 per thread),
-//                   used for the two projections and for the causal tiles of
-//                   the block logits Q' K'^T.
+//  gate_gemm        fp32 LDS-tiled GEMM on the fp32 matrix cores (64 x 64
+//                   tiles, a 32 x 32 quadrant per wavefront), used for the
+//                   two projections, the causal tiles of the block logits
+//                   Q' K'^T and the distillation step's gradients.
 //  gate_softmax_mask_wave
 //                   one wavefront per score row (rows up to 4096 blocks), the
 //                   row in registers: max / sum reductions, the normalized
@@ -69,9 +70,20 @@ __global__ __launch_bounds__(kPoolThreads) void gate_pool_kernel(GateArgs a) {
   float sum[8], mx[8], mn[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) { sum[e] = 0.f; mx[e] = -INFINITY; mn[e] = INFINITY; }
-  for (int r = rg; r < n; r += NRG) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(t0 + r) * D + 8 * c);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  // all of the thread's rows are loaded before any is reduced (one memory
+  // round trip per workgroup); rows past a ragged last block re-read the
+  // block's last row and are skipped below
+  constexpr int RPT = kBlock / NRG;       // rows per thread
+  uint4 rows[RPT];
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    const int r = min(rg + u * NRG, n - 1);
+    rows[u] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(t0 + r) * D + 8 * c);
+  }
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    if (rg + u * NRG >= n) continue;
+    const uint32_t w[4] = {rows[u].x, rows[u].y, rows[u].z, rows[u].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
@@ -114,64 +126,65 @@ constexpr int kGT = 256;
 constexpr int kBM = 64, kBN = 64, kBK = 16;
 
 // acc += A(m0 .. m0+63, k) * Bm(k, n0 .. n0+63) over k in [k0, k1), where
-// A(m, k) = A[m*lda + k] (A_T = false) or A[k*lda + m] (A_T = true).
+// A(m, k) = A[m*lda + k] (A_T = false) or A[k*lda + m] (A_T = true), on the
+// fp32 matrix cores: wave w owns the 32 x 32 quadrant at rows 32 (w & 1),
+// columns 32 (w >> 1), and lane l's element r is its entry
+// [8 (r / 4) + 4 (l / 32) + r % 4][l % 32] (v_mfma_f32_32x32x2_f32: lane l
+// supplies A[l % 32][l / 32] and B[l / 32][l % 32] of each 32 x 2 x 32 step).
 template <bool A_T, bool B_T>
-__device__ __forceinline__ void gemm_accum(float (&acc)[4][4], const float* __restrict__ A, int lda,
+__device__ __forceinline__ void gemm_accum(f32x16_t& acc, const float* __restrict__ A, int lda,
                                            const float* __restrict__ B, int ldb, int M, int N, int k0, int k1,
                                            int m0, int n0) {
   __shared__ float As[kBK][kBM + 4];
   __shared__ float Bs[kBK][kBN + 4];
   const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
-  for (int kb = k0; kb < k1; kb += kBK) {
-    // A tile 64 x 16 (stored transposed), B tile 16 x 64
+  const int lane = tid & 63, w = tid >> 6;
+  const int qm = 32 * (w & 1) + (lane & 31), qn = 32 * (w >> 1) + (lane & 31), kh = lane >> 5;
+  // the next chunk's operands are loaded into registers while this chunk's
+  // products run: A tile 64 x 16 (stored transposed), B tile 16 x 64
+  float ra[4], rb[4];
+  auto gload = [&](int kb) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int idx = tid + kGT * e;         // 0..1023
-      int am, ak;
-      if (A_T) { ak = idx >> 6; am = idx & 63; } else { am = idx >> 4; ak = idx & 15; }
+      const int am = A_T ? (idx & 63) : (idx >> 4), ak = A_T ? (idx >> 6) : (idx & 15);
       const int gm = m0 + am, gk = kb + ak;
-      float av = 0.f;
-      if (gm < M && gk < k1) av = A_T ? A[static_cast<size_t>(gk) * lda + gm] : A[static_cast<size_t>(gm) * lda + gk];
-      As[ak][am] = av;
-      int bk, bn;
-      if (B_T) { bn = idx >> 4; bk = idx & 15; } else { bk = idx >> 6; bn = idx & 63; }
+      ra[e] = 0.f;
+      if (gm < M && gk < k1) ra[e] = A_T ? A[static_cast<size_t>(gk) * lda + gm] : A[static_cast<size_t>(gm) * lda + gk];
+      const int bn = B_T ? (idx >> 4) : (idx & 63), bk = B_T ? (idx & 15) : (idx >> 6);
       const int gn = n0 + bn, gk2 = kb + bk;
-      float bv = 0.f;
-      if (gn < N && gk2 < k1) bv = B_T ? B[static_cast<size_t>(gn) * ldb + gk2] : B[static_cast<size_t>(gk2) * ldb + gn];
-      Bs[bk][bn] = bv;
+      rb[e] = 0.f;
+      if (gn < N && gk2 < k1) rb[e] = B_T ? B[static_cast<size_t>(gn) * ldb + gk2] : B[static_cast<size_t>(gk2) * ldb + gn];
+    }
+  };
+  if (k0 < k1) gload(k0);
+  for (int kb = k0; kb < k1; kb += kBK) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + kGT * e;
+      As[A_T ? (idx >> 6) : (idx & 15)][A_T ? (idx & 63) : (idx >> 4)] = ra[e];
+      Bs[B_T ? (idx & 15) : (idx >> 6)][B_T ? (idx >> 4) : (idx & 63)] = rb[e];
     }
     __syncthreads();
+    if (kb + kBK < k1) gload(kb + kBK);
 #pragma unroll
-    for (int kk = 0; kk < kBK; ++kk) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
-    }
+    for (int kk = 0; kk < kBK; kk += 2)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[kk + kh][qm], Bs[kk + kh][qn], acc, 0, 0, 0);
     __syncthreads();
   }
 }
 
-__device__ __forceinline__ void gemm_store(const float (&acc)[4][4], float* __restrict__ C, int ldc, int M, int N,
+__device__ __forceinline__ void gemm_store(const f32x16_t& acc, float* __restrict__ C, int ldc, int M, int N,
                                            int m0, int n0, float alpha, bool causal_only) {
   const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
+  const int lane = tid & 63, w = tid >> 6;
+  const int gn = n0 + 32 * (w >> 1) + (lane & 31);
+  if (gn >= N) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gm = m0 + ty * 4 + i;
-    if (gm >= M) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gn = n0 + tx * 4 + j;
-      if (gn >= N || (causal_only && gn > gm)) continue;
-      C[static_cast<size_t>(gm) * ldc + gn] = acc[i][j] * alpha;
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int gm = m0 + 32 * (w & 1) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (gm >= M || (causal_only && gn > gm)) continue;
+    C[static_cast<size_t>(gm) * ldc + gn] = acc[r] * alpha;
   }
 }
 
@@ -180,7 +193,7 @@ template <bool B_T>
 __device__ __forceinline__ void gemm_tile(const float* __restrict__ A, int lda, const float* __restrict__ B,
                                           int ldb, float* __restrict__ C, int ldc, int M, int N, int K,
                                           int m0, int n0, float alpha, bool causal_only) {
-  float acc[4][4] = {};
+  f32x16_t acc = {};
   gemm_accum<false, B_T>(acc, A, lda, B, ldb, M, N, 0, K, m0, n0);
   gemm_store(acc, C, ldc, M, N, m0, n0, alpha, causal_only);
 }
@@ -787,7 +800,7 @@ __global__ __launch_bounds__(kGT) void gate_dproj_kernel(GateArgs a) {
   const int hk = a.wk_per_kv ? h / a.group : h;
   const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * kBN;
   const float* dz = a.scores + static_cast<size_t>(z) * a.nb * a.nb;
-  float acc[4][4] = {};
+  f32x16_t acc = {};
   if (zz < nq) {
     const float* kg = a.kg + (static_cast<size_t>(b) * hwk + hk) * a.nb * a.Dg;
     gemm_accum<false, false>(acc, dz, a.nb, kg, a.Dg, a.nb, a.Dg, 0, min(a.nb, m0 + kBM), m0, n0);
@@ -806,7 +819,7 @@ __global__ __launch_bounds__(kGT) void gate_dproj_kernel(GateArgs a) {
 __global__ __launch_bounds__(kGT) void gate_dweight_kernel(GateArgs a) {
   const int zz = blockIdx.z;
   const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * kBN;
-  float acc[4][4] = {};
+  f32x16_t acc = {};
   if (zz < a.Hq) {
     if (m0 >= a.D) return;                   // uniform per workgroup
     for (int b = 0; b < a.B; ++b) {
