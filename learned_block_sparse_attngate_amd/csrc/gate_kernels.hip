@@ -751,6 +751,82 @@ __global__ __launch_bounds__(256) void gate_rope_kernel(float* __restrict__ x, i
 // dz overwriting the logits in place. A row whose ground truth sums to 0 has
 // no target distribution and contributes nothing (loss 0, dz 0).
 // ---------------------------------------------------------------------------
+// gate_kl_kernel with one wavefront per row (rows up to 256 G blocks), the
+// row in registers in the layout of gate_softmax_mask_wave_kernel. Entries
+// past the causal end load as logit -inf and gt 0, so they drop out of every
+// sum and their dz is 0 without a per-element test.
+template <int G>
+__global__ __launch_bounds__(256) void gate_kl_wave_kernel(GateArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long long row = static_cast<long long>(blockIdx.x) * 4 + wave;
+  if (row >= static_cast<long long>(a.B) * a.Hq * a.nb) return;
+  const int nb = a.nb;
+  const int i = static_cast<int>(row % nb);
+  const int n = i + 1;
+  float* zrow = a.scores + static_cast<size_t>(row) * nb;
+  const float* grow = a.gt + static_cast<size_t>(row) * nb;
+  const bool vec = (nb & 3) == 0;
+  float zv[G][4], gv[G][4];
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    const int j0 = 256 * t + 4 * lane;
+    if (vec && j0 + 3 < n) {
+      const float4 x = *reinterpret_cast<const float4*>(zrow + j0);
+      const float4 y = *reinterpret_cast<const float4*>(grow + j0);
+      zv[t][0] = x.x; zv[t][1] = x.y; zv[t][2] = x.z; zv[t][3] = x.w;
+      gv[t][0] = y.x; gv[t][1] = y.y; gv[t][2] = y.z; gv[t][3] = y.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        zv[t][e] = j0 + e < n ? zrow[j0 + e] : -INFINITY;
+        gv[t][e] = j0 + e < n ? grow[j0 + e] : 0.f;
+      }
+    }
+  }
+  float mx = -INFINITY, gsum = 0.f;
+#pragma unroll
+  for (int t = 0; t < G; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mx = fmaxf(mx, zv[t][e]);
+      gsum += gv[t][e];
+    }
+  mx = wave_max(mx);
+  gsum = wave_sum(gsum);
+  float l = 0.f;
+#pragma unroll
+  for (int t = 0; t < G; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) l += expf(zv[t][e] - mx);
+  l = wave_sum(l);
+  const float lse = mx + logf(l);
+  const bool valid = gsum > 0.f;             // a row without ground-truth mass contributes nothing
+  const float inv_g = valid ? 1.0f / gsum : 0.f;
+  const float inv_rows = 1.0f / (static_cast<float>(a.B) * a.Hq * a.nb);
+  float kl = 0.f;
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    float dz[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ls = zv[t][e] - lse;
+      const float pj = gv[t][e] * inv_g;
+      if (pj > 0.f) kl += pj * (logf(pj) - ls);
+      dz[e] = valid ? (expf(ls) - pj) * inv_rows : 0.f;
+    }
+    const int j0 = 256 * t + 4 * lane;
+    if (vec) {
+      if (j0 < nb) *reinterpret_cast<float4*>(zrow + j0) = make_float4(dz[0], dz[1], dz[2], dz[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j0 + e < nb) zrow[j0 + e] = dz[e];
+    }
+  }
+  kl = wave_sum(kl);
+  if (lane == 0) a.row_loss[row] = kl;
+}
+
 __global__ __launch_bounds__(kST) void gate_kl_kernel(GateArgs a) {
   __shared__ float red[kST / kWave];
   const int i = blockIdx.x;
@@ -844,15 +920,26 @@ __global__ __launch_bounds__(kGT) void gate_dweight_kernel(GateArgs a) {
   }
 }
 
-// loss = mean of the row divergences: one workgroup, fixed summation order, fp64
-__global__ __launch_bounds__(kST) void gate_loss_kernel(GateArgs a) {
-  __shared__ double red[kST];
+// loss = mean of the row divergences, in fp64 and a fixed order (bitwise
+// repeatable), by one workgroup: thread t
+// adds rows t, t + 1024, ... in turn with 16 loads in flight, then a fixed
+// tree over the threads.
+constexpr int kLossThreads = 1024;
+__global__ __launch_bounds__(kLossThreads) void gate_loss_kernel(GateArgs a) {
+  __shared__ double red[kLossThreads];
   const long long n = static_cast<long long>(a.B) * a.Hq * a.nb;
   double s = 0.0;
-  for (long long r = threadIdx.x; r < n; r += kST) s += a.row_loss[r];
+  for (long long r0 = threadIdx.x; r0 < n; r0 += 16 * kLossThreads) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = r0 + u * kLossThreads < n ? a.row_loss[r0 + u * kLossThreads] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (r0 + u * kLossThreads < n) s += v[u];
+  }
   red[threadIdx.x] = s;
   __syncthreads();
-  for (int w = kST / 2; w > 0; w >>= 1) {
+  for (int w = kLossThreads / 2; w > 0; w >>= 1) {
     if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
@@ -930,7 +1017,16 @@ hipError_t launch_decode_gate(const DecodeGateArgs& a, const TopkTable& tk, hipS
 hipError_t launch_gate_distill(const GateArgs& a, hipStream_t st) {
   hipError_t e = launch_gate_logits(a, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gate_kl_kernel, dim3(a.nb, a.B * a.Hq), dim3(kST), 0, st, a);
+  {
+    const long long rows = static_cast<long long>(a.B) * a.Hq * a.nb;
+    const dim3 gw(static_cast<unsigned>((rows + 3) / 4));
+    if (a.nb <= 256) hipLaunchKernelGGL(gate_kl_wave_kernel<1>, gw, dim3(256), 0, st, a);
+    else if (a.nb <= 512) hipLaunchKernelGGL(gate_kl_wave_kernel<2>, gw, dim3(256), 0, st, a);
+    else if (a.nb <= 1024) hipLaunchKernelGGL(gate_kl_wave_kernel<4>, gw, dim3(256), 0, st, a);
+    else if (a.nb <= 2048) hipLaunchKernelGGL(gate_kl_wave_kernel<8>, gw, dim3(256), 0, st, a);
+    else if (a.nb <= 4096) hipLaunchKernelGGL(gate_kl_wave_kernel<16>, gw, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(gate_kl_kernel, dim3(a.nb, a.B * a.Hq), dim3(kST), 0, st, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int nq = a.B * a.Hq;
   dim3 gd((a.nb + kBM - 1) / kBM, (a.Dg + kBN - 1) / kBN, 2 * nq);
@@ -944,7 +1040,7 @@ hipError_t launch_gate_distill(const GateArgs& a, hipStream_t st) {
   dim3 gw((3 * a.D + kBM - 1) / kBM, (a.Dg + kBN - 1) / kBN, a.Hq + hwk);
   hipLaunchKernelGGL(gate_dweight_kernel, gw, dim3(kGT), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(gate_loss_kernel, dim3(1), dim3(kST), 0, st, a);
+  hipLaunchKernelGGL(gate_loss_kernel, dim3(1), dim3(kLossThreads), 0, st, a);
   return hipGetLastError();
 }
 
