@@ -726,20 +726,31 @@ __global__ __launch_bounds__(kST) void decode_gate_kernel(DecodeGateArgs a, Topk
 // are computed in fp64 so that long sequences keep the angle exact. `sign` =
 // -1 rotates back (the transpose, used by the gradient).
 // ---------------------------------------------------------------------------
+constexpr int kRopeRows = 8;               // rows rotated per thread with one angle
 __global__ __launch_bounds__(256) void gate_rope_kernel(float* __restrict__ x, int rows, int nb, int dg,
                                                         double base, double sign) {
   const int half = dg / 2;
   const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;   // over nb * half
-  const int z = blockIdx.y;
-  if (z >= rows || idx >= static_cast<long long>(nb) * half) return;
+  if (idx >= static_cast<long long>(nb) * half) return;
   const int i = static_cast<int>(idx / half), d = static_cast<int>(idx - static_cast<long long>(i) * half);
   const double ang = sign * static_cast<double>(i) * pow(base, -2.0 * d / dg);
   double sn, cs;
   sincos(ang, &sn, &cs);
-  float* r = x + (static_cast<size_t>(z) * nb + i) * dg;
-  const double x1 = r[d], x2 = r[d + half];
-  r[d] = static_cast<float>(x1 * cs - x2 * sn);
-  r[d + half] = static_cast<float>(x2 * cs + x1 * sn);
+  const int z0 = blockIdx.y * kRopeRows;
+  float x1[kRopeRows], x2[kRopeRows];
+#pragma unroll
+  for (int u = 0; u < kRopeRows; ++u) {
+    const float* r = x + (static_cast<size_t>(min(z0 + u, rows - 1)) * nb + i) * dg;
+    x1[u] = r[d];
+    x2[u] = r[d + half];
+  }
+#pragma unroll
+  for (int u = 0; u < kRopeRows; ++u) {
+    if (z0 + u >= rows) break;
+    float* r = x + (static_cast<size_t>(z0 + u) * nb + i) * dg;
+    r[d] = static_cast<float>(static_cast<double>(x1[u]) * cs - static_cast<double>(x2[u]) * sn);
+    r[d + half] = static_cast<float>(static_cast<double>(x2[u]) * cs + static_cast<double>(x1[u]) * sn);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -948,7 +959,7 @@ __global__ __launch_bounds__(kLossThreads) void gate_loss_kernel(GateArgs a) {
 
 hipError_t launch_rope(const GateArgs& a, float* x, int rows, double sign, hipStream_t st) {
   const long long n = static_cast<long long>(a.nb) * (a.Dg / 2);
-  dim3 g(static_cast<unsigned>((n + 255) / 256), rows);
+  dim3 g(static_cast<unsigned>((n + 255) / 256), (rows + kRopeRows - 1) / kRopeRows);
   hipLaunchKernelGGL(gate_rope_kernel, g, dim3(256), 0, st, x, rows, a.nb, a.Dg, a.rope_base, sign);
   return hipGetLastError();
 }
