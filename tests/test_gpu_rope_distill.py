@@ -117,6 +117,32 @@ def test_distill_matches_oracle(name, shape, dg, per_kv, theta):
     _check_distill(got, want, name)
 
 
+# Rows longer than one wavefront's 256-element pass (aligned and not) and past
+# the register-resident limit of 4096 blocks (a workgroup per row), with a
+# seeded lower-triangular target map in place of the (costly) oracle ground
+# truth, one row of it zeroed.
+LONG_DISTILL_CASES = [
+    ("nb600", 600, 5e5),
+    ("nb1501", 1501, 0.0),
+    ("nb4100", 4100, 5e5),
+]
+
+
+@pytest.mark.parametrize("name,nb,theta", LONG_DISTILL_CASES, ids=[c[0] for c in LONG_DISTILL_CASES])
+def test_distill_long_rows_match_oracle(name, nb, theta):
+    seer = _seer()
+    shape = Shape(1, 2, 1, 64 * nb - 7, 64)
+    say(f"[distill long rows {name}] shape={shape} theta={theta}")
+    q, k, wq, wk = _gate_inputs(shape, 76, 64, var=4.0 / 64)
+    gt = np.tril(np.random.default_rng(77).random((1, 2, nb, nb))).astype(np.float32)
+    gt[0, 0, nb // 3, :] = 0.0
+    want = oracle.gate_distill(q, k, wq, wk, gt, rope_theta=theta or None)
+    got = seer.seer_gate_distill_bwd(dev_bf16(q), dev_bf16(k), dev_f32(wq), dev_f32(wk), dev_f32(gt),
+                                     rope_theta=theta)
+    torch.cuda.synchronize()
+    _check_distill(got, want, name)
+
+
 def test_distill_end_to_end_and_descent():
     """GPU ground truth -> GPU distillation step against the oracle's ground
     truth -> oracle step; then one gradient step lowers the GPU loss."""
