@@ -397,6 +397,9 @@ def main():
     gate_avg = float(np.mean(gate_ms))
     s_real = 1.0 - tiles / causal_tiles
     achieved = sparse_flop / attn_avg / 1e9                     # TFLOP/s of the attention kernel
+    # the gate call's compulsory HBM bytes: Q and K read once (bf16), the
+    # fp32 scores and the u8 mask written once
+    gate_bytes = 2 * B * S * D * (Hq + Hkv) + B * Hq * nb * nb * (4 + 1)
     rec = {
         "metric": METRIC,
         "value": round(sparse_flop / ms_step / 1e9, 3),
@@ -428,6 +431,11 @@ def main():
                      "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(args.workload)},
+        "gate": {"kernel": "seer_gate_fwd (pool, projections, block RoPE, causal logits, softmax + top-k mask)",
+                 "ms": round(gate_avg, 4), "bound": "hbm",
+                 "compulsory_bytes": gate_bytes,
+                 "achieved": round(gate_bytes / gate_avg / 1e6, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(gate_bytes / gate_avg / 1e6 / PEAK_HBM_GBS, 4)},
         "decode": decode,
         "varlen": varlen,
         "peak_computed": computed_peak(),
