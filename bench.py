@@ -79,6 +79,31 @@ def measured_traffic(workload: str):
         return None
 
 
+MFMA_COUNTERS = os.path.join(ROOT, "profiles", "attn_sparse_llama8b_s128k_90_mfma_lds_counters.md")
+
+
+def measured_mfma_busy(workload: str):
+    """Fraction of the main block-sparse kernel's cycles its MFMA pipes were
+    busy (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs) and
+    the engine clock during it, from the committed counter summary; None if
+    that summary is missing, for another workload, or for other kernel source."""
+    import hashlib
+    import re
+    try:
+        text = open(MFMA_COUNTERS).read()
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if workload not in text.splitlines()[0] or f"attn_kernels.hip sha256 `{src}`" not in text:
+        return None
+    busy = re.search(r"The MFMA pipes are busy ([0-9.]+)% of the kernel's cycles", text)
+    clk = re.search(r"The engine clock during the kernel is ([0-9.]+) GHz", text)
+    if not busy or not clk:
+        return None
+    return {"mfma_busy": round(float(busy.group(1)) / 100.0, 4), "engine_clock_ghz": float(clk.group(1)),
+            "source": "profiles/attn_sparse_llama8b_s128k_90_mfma_lds_counters.md"}
+
+
 def computed_peak():
     """Dense bf16 MFMA peak from the agent's compute-unit count and maximum
     engine clock as rocminfo reports them (4096 FLOP per clock per CU on
@@ -397,6 +422,7 @@ def main():
     gate_avg = float(np.mean(gate_ms))
     s_real = 1.0 - tiles / causal_tiles
     achieved = sparse_flop / attn_avg / 1e9                     # TFLOP/s of the attention kernel
+    peak = computed_peak()
     # the gate call's compulsory HBM bytes: Q and K read once (bf16), the
     # fp32 scores and the u8 mask written once
     gate_bytes = 2 * B * S * D * (Hq + Hkv) + B * Hq * nb * nb * (4 + 1)
@@ -408,6 +434,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms_median": round(float(np.median(step_ms)), 4),
+        "step_ms_min": round(float(np.min(step_ms)), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -430,7 +458,11 @@ def main():
         "roofline": {"kernel": "seer_block_sparse_attn_fwd (one call: main block-sparse kernel + merge of partial outputs)",
                      "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(args.workload)},
+                     "traffic": measured_traffic(args.workload),
+                     "attention_ms_median": round(float(np.median(attn_ms)), 4),
+                     "attention_ms_min": round(float(np.min(attn_ms)), 4),
+                     "frac_of_computed_peak": None if peak is None else round(achieved / peak["bf16_tflops"], 4),
+                     "counters": measured_mfma_busy(args.workload)},
         "gate": {"kernel": "seer_gate_fwd (pool, projections, block RoPE, causal logits, softmax + top-k mask)",
                  "ms": round(gate_avg, 4), "bound": "hbm",
                  "compulsory_bytes": gate_bytes,
@@ -438,7 +470,7 @@ def main():
                  "frac": round(gate_bytes / gate_avg / 1e6 / PEAK_HBM_GBS, 4)},
         "decode": decode,
         "varlen": varlen,
-        "peak_computed": computed_peak(),
+        "peak_computed": peak,
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu:
