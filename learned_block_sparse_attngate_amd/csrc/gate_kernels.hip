@@ -416,7 +416,11 @@ __global__ __launch_bounds__(256) void gate_softmax_mask_wave_kernel(GateArgs a,
   const int n = i + 1;                                  // causal entries of this row
   float* srow = a.scores + static_cast<size_t>(row) * nb;
   uint8_t* mrow = a.mask + static_cast<size_t>(row) * nb;
-  const bool vec = (nb & 3) == 0;                       // rows start 16-byte aligned
+  // 16-byte score and 4-byte mask accesses only for whole groups of 4 and
+  // where the row pointers allow them (the caller's maps need only 4-byte
+  // and 1-byte alignment)
+  const bool vec = (nb & 3) == 0 && (reinterpret_cast<uintptr_t>(srow) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(mrow) & 3) == 0;
 
   float v[G][4];                                        // logits; -inf past the causal end
 #pragma unroll
@@ -776,7 +780,9 @@ __global__ __launch_bounds__(256) void gate_kl_wave_kernel(GateArgs a) {
   const int n = i + 1;
   float* zrow = a.scores + static_cast<size_t>(row) * nb;
   const float* grow = a.gt + static_cast<size_t>(row) * nb;
-  const bool vec = (nb & 3) == 0;
+  // 16-byte accesses only for whole groups of 4 and where both row pointers
+  // allow them (gt needs only 4-byte alignment)
+  const bool vec = (nb & 3) == 0 && ((reinterpret_cast<uintptr_t>(zrow) | reinterpret_cast<uintptr_t>(grow)) & 15) == 0;
   float zv[G][4], gv[G][4];
 #pragma unroll
   for (int t = 0; t < G; ++t) {

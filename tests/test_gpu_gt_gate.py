@@ -202,6 +202,50 @@ def test_gate_flat_scores_ties_and_strictness():
         assert np.array_equal(m2[0, 0, i], want)
 
 
+def _offset_view(shape, dtype, elems):
+    """A contiguous tensor whose data starts `elems` elements into its buffer."""
+    n = int(np.prod(shape))
+    return torch.zeros(n + elems, dtype=dtype, device="cuda")[elems:].view(shape)
+
+
+@pytest.mark.parametrize("mode", ["topk", "threshold"])
+def test_gate_misaligned_maps_equal_aligned(mode):
+    """Scores 4 bytes and mask 1 byte past 16-byte alignment (allowed by the
+    ABI; varlen maps start at such offsets) give the same bits as aligned
+    maps, at a row length that is a multiple of 4 (the 16-byte path)."""
+    seer = _seer()
+    shape = Shape(1, 2, 1, 64 * 300, 64)
+    q, k, wq, wk = (dev_bf16(x) if i < 2 else dev_f32(x) for i, x in enumerate(_gate_inputs(shape, 69, 64)))
+    nb = shape.nb
+    kw = dict(mode="topk", topk=[17, 90]) if mode == "topk" else dict(mode="threshold", threshold=1.5 / nb)
+    m0, s0 = seer.seer_gate_fwd(q, k, wq, wk, **kw)
+    sc1 = _offset_view((1, 2, nb, nb), torch.float32, 1)
+    mk1 = _offset_view((1, 2, nb, nb), torch.uint8, 1)
+    assert sc1.data_ptr() % 16 == 4 and mk1.data_ptr() % 4 == 1
+    m1, s1 = seer.seer_gate_fwd(q, k, wq, wk, scores=sc1, block_mask=mk1, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(s0, s1) and torch.equal(m0, m1)
+
+
+def test_distill_misaligned_gt_equals_aligned():
+    """A ground-truth map 4 bytes past 16-byte alignment gives the same loss
+    and gradients as an aligned one (rows a multiple of 4 blocks long)."""
+    seer = _seer()
+    shape = Shape(1, 2, 1, 64 * 300, 64)
+    q, k, wq, wk = (dev_bf16(x) if i < 2 else dev_f32(x) for i, x in enumerate(_gate_inputs(shape, 70, 64)))
+    nb = shape.nb
+    gt_np = np.tril(np.random.default_rng(71).random((1, 2, nb, nb))).astype(np.float32)
+    gt0 = dev_f32(gt_np)
+    gt1 = _offset_view((1, 2, nb, nb), torch.float32, 1)
+    gt1.copy_(gt0)
+    assert gt1.data_ptr() % 16 == 4
+    a = seer.seer_gate_distill_bwd(q, k, wq, wk, gt0, rope_theta=5e5)
+    b = seer.seer_gate_distill_bwd(q, k, wq, wk, gt1, rope_theta=5e5)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 def test_gate_to_sparse_attention_end_to_end():
     """Gate mask -> block-sparse attention, checked against the oracle's own gate + attention."""
     seer = _seer()
