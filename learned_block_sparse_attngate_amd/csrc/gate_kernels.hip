@@ -36,7 +36,9 @@
 //                   weight-gradient GEMMs, fixed-order loss reduction.
 //  decode_kcomp, decode_logits, decode_gate
 //                   decode stage: pooled and projected key blocks, 8 lanes
-//                   per logit, then the row softmax and mask.
+//                   per logit, then the row softmax and mask (a workgroup per
+//                   row: with one row per head, four wavefronts per row hide
+//                   more latency than one).
 #include <math.h>
 
 #include "seer_device.h"
@@ -405,17 +407,13 @@ __device__ __forceinline__ int wave_sum_int(int x) {
 // bit, so those entries never match a radix prefix (whose mask includes the
 // sign bit) and compare below every probability as signed integers, and all
 // the later steps are integer compares on the keys alone.
+// The row's first n of nb entries are its logits (the rest are written as
+// probability 0 and mask 0); k is its top-k count (mode 1); hist is this
+// wavefront's 256-word LDS histogram.
 template <int G>
-__global__ __launch_bounds__(256) void gate_softmax_mask_wave_kernel(GateArgs a, TopkTable tk) {
-  __shared__ __align__(16) uint32_t hist_all[4][256];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long long row = static_cast<long long>(blockIdx.x) * 4 + wave;
-  if (row >= static_cast<long long>(a.B) * a.Hq * a.nb) return;
-  const int nb = a.nb;
-  const int z = static_cast<int>(row / nb), i = static_cast<int>(row - static_cast<long long>(z) * nb);
-  const int n = i + 1;                                  // causal entries of this row
-  float* srow = a.scores + static_cast<size_t>(row) * nb;
-  uint8_t* mrow = a.mask + static_cast<size_t>(row) * nb;
+__device__ __forceinline__ void wave_softmax_mask_row(float* srow, uint8_t* mrow, int n, int nb, int mode,
+                                                      float threshold, int k, uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
   // 16-byte score and 4-byte mask accesses only for whole groups of 4 and
   // where the row pointers allow them (the caller's maps need only 4-byte
   // and 1-byte alignment)
@@ -470,13 +468,12 @@ __global__ __launch_bounds__(256) void gate_softmax_mask_wave_kernel(GateArgs a,
   }
 
   // keep: key > lim as signed integers, plus (top-k) the first kk equal to lim
-  const int k = tk.k[z % a.Hq];
   int32_t lim = -1;                                     // every causal entry
   int kk = 0;
-  if (a.mode == 0) {
+  if (mode == 0) {
     // p > T: bit patterns above T's for T > 0, above +0 for T = 0, every
     // entry for T < 0, none for a NaN T
-    const float T = a.threshold;
+    const float T = threshold;
     lim = T > 0.f ? static_cast<int32_t>(__float_as_uint(T)) : (T == 0.f ? 0 : (T < 0.f ? -1 : INT32_MAX));
   } else if (k < n) {
     // exact k-th largest probability (probabilities are >= 0: their bit
@@ -504,7 +501,6 @@ __global__ __launch_bounds__(256) void gate_softmax_mask_wave_kernel(GateArgs a,
       if (count_ge(mid << 23) >= k) lo = mid;
       else hi = mid - 1;
     }
-    uint32_t* hist = hist_all[wave];
     uint32_t prefix = static_cast<uint32_t>(lo) << 23, pmask = 0xff800000u;
     kk = k - count_ge((lo + 1) << 23);                  // how many of the exponent's bin to keep
 #pragma unroll
@@ -586,6 +582,19 @@ __global__ __launch_bounds__(256) void gate_softmax_mask_wave_kernel(GateArgs a,
     }
   }
 }
+
+// Prefill rows: row i of head z has the causal entries j <= i.
+template <int G>
+__global__ __launch_bounds__(256) void gate_softmax_mask_wave_kernel(GateArgs a, TopkTable tk) {
+  __shared__ __align__(16) uint32_t hist_all[4][256];
+  const int wave = threadIdx.x >> 6;
+  const long long row = static_cast<long long>(blockIdx.x) * 4 + wave;
+  if (row >= static_cast<long long>(a.B) * a.Hq * a.nb) return;
+  const int z = static_cast<int>(row / a.nb), i = static_cast<int>(row - static_cast<long long>(z) * a.nb);
+  wave_softmax_mask_row<G>(a.scores + static_cast<size_t>(row) * a.nb, a.mask + static_cast<size_t>(row) * a.nb,
+                           i + 1, a.nb, a.mode, a.threshold, tk.k[z % a.Hq], hist_all[wave]);
+}
+
 
 // ---------------------------------------------------------------------------
 // Decode-stage gate ("SeerAttention: Self-distilled Attention Gating for

@@ -52,17 +52,21 @@ def test_compress_k_full_and_incremental(shape, per_kv):
     assert torch.equal(kc2[:, :, :shape.nb], kc[:, :, :shape.nb])
 
 
-@pytest.mark.parametrize("per_kv", [False, True], ids=["wk_per_q", "wk_per_kv"])
-def test_decode_gate_matches_oracle(per_kv):
+@pytest.mark.parametrize("per_kv,shape", [(False, Shape(2, 8, 2, 64 * 300 - 33, 128)),
+                                           (True, Shape(2, 8, 2, 64 * 300 - 33, 128)),
+                                           (False, Shape(1, 4, 1, 64 * 2101 - 5, 64)),
+                                           (True, Shape(1, 4, 2, 64 * 4100, 64))],
+                         ids=["wk_per_q", "wk_per_kv", "nb2101", "nb4100_kvw"])
+def test_decode_gate_matches_oracle(per_kv, shape):
     seer = _seer()
-    shape = Shape(2, 8, 2, 64 * 300 - 33, 128)
     say(f"[decode gate] shape={shape} per_kv={per_kv}")
     qd, k, _, wk = _inputs(shape, 91, per_kv, var=4.0 / 128)
     kc_ref = oracle.decode_kcomp(k, wk, shape.heads_q, wk_per_kv_head=per_kv)
     sc_ref = oracle.decode_gate_scores(qd, kc_ref, wk_per_kv_head=per_kv)
     kc = seer.seer_decode_compress_k(dev_bf16(k), dev_f32(wk), shape.heads_q, wk_per_kv_head=per_kv)
     nb = shape.nb
-    for mode, arg in (("threshold", 1.5 / nb), ("threshold", 0.5 / nb), ("topk", 20), ("topk", [3, 40] * 4)):
+    for mode, arg in (("threshold", 1.5 / nb), ("threshold", 0.5 / nb), ("topk", 20),
+                      ("topk", [3, 40] * (shape.heads_q // 2))):
         kw = dict(threshold=arg) if mode == "threshold" else dict(topk=arg)
         mask, scores = seer.seer_decode_gate_fwd(dev_bf16(qd), kc, shape.seq_len, shape.heads_kv,
                                                  wk_per_kv_head=per_kv, mode=mode, **kw)
