@@ -235,36 +235,36 @@ __global__ __launch_bounds__(kThreadsDec) void decode_attn_kernel(DecodeAttnArgs
 // Merge the key splits of one (batch, head): O = sum_s 2^(m_s - M) acc_s / L,
 // L = sum_s 2^(m_s - M) l_s, LSE = (M + log2 L) ln 2; in dense mode the raw
 // block maxima become the 1D max-pooled map gt_j = 2^(r_j - log2-sum-exp).
-// The splits are spread over the workgroup's threads.
+// 1024 threads per row, so that the row takes few memory round trips: thread
+// s reads split s's (max, sum) (splits <= kMaxSplits), then thread (part, d)
+// sums dim d over splits part, part + P, ... with 8 loads in flight.
+constexpr int kThreadsComb = 1024;
 template <int D>
-__global__ __launch_bounds__(kThreadsDec) void decode_combine_kernel(DecodeAttnArgs a) {
-  constexpr int P = kThreadsDec / D;
+__global__ __launch_bounds__(kThreadsComb) void decode_combine_kernel(DecodeAttnArgs a) {
+  constexpr int P = kThreadsComb / D;
+  constexpr int NW = kThreadsComb / kWave;
   __shared__ float w_s[kMaxSplits];
-  __shared__ float red[kThreadsDec / kWave];
+  __shared__ float red[NW];
   __shared__ float o_s[P][D];
   const int z = blockIdx.x;                  // b * Hq + h
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* pp = a.part + static_cast<size_t>(z) * a.nsplit * (D + 2);
-  float mx = -INFINITY;
-  for (int s = tid; s < a.nsplit; s += kThreadsDec) mx = fmaxf(mx, pp[static_cast<size_t>(s) * (D + 2) + D]);
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  const bool has = tid < a.nsplit;
+  const float ms = has ? pp[static_cast<size_t>(tid) * (D + 2) + D] : -INFINITY;
+  const float lsp = has ? pp[static_cast<size_t>(tid) * (D + 2) + D + 1] : 0.f;
+  float mx = wave_max(ms);
+  if (lane == 0) red[wave] = mx;
   __syncthreads();
   float M = red[0];
-  for (int w = 1; w < kThreadsDec / kWave; ++w) M = fmaxf(M, red[w]);
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, red[w]);
   __syncthreads();
-  float ls = 0.f;
-  for (int s = tid; s < a.nsplit; s += kThreadsDec) {
-    const float* pr = pp + static_cast<size_t>(s) * (D + 2);
-    const float w = (M > -INFINITY && pr[D] > -INFINITY) ? __builtin_amdgcn_exp2f(pr[D] - M) : 0.f;
-    w_s[s] = w;
-    ls = fmaf(pr[D + 1], w, ls);
-  }
-  ls = wave_sum(ls);
-  if ((tid & 63) == 0) red[tid >> 6] = ls;
+  const float wt = (M > -INFINITY && ms > -INFINITY) ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
+  if (has) w_s[tid] = wt;
+  const float ls = wave_sum(lsp * wt);
+  if (lane == 0) red[wave] = ls;
   __syncthreads();
   float L = 0.f;
-  for (int w = 0; w < kThreadsDec / kWave; ++w) L += red[w];
+  for (int w = 0; w < NW; ++w) L += red[w];
   const int d = tid % D, part = tid / D;
   float o8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // independent sums: many loads in flight
   int s = part;
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kThreadsDec) void decode_combine_kernel(DecodeAttnA
     if (tid == 0 && a.lse != nullptr) a.lse[z] = lse2 * 0.69314718055994530942f;
   }
   if (a.gt != nullptr)
-    for (int j = tid; j < a.nb; j += kThreadsDec) {
+    for (int j = tid; j < a.nb; j += kThreadsComb) {
       float* gp = a.gt + static_cast<size_t>(z) * a.nb + j;
       *gp = L > 0.f ? __builtin_amdgcn_exp2f(*gp - lse2) : 0.f;
     }
@@ -327,8 +327,8 @@ hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t st) {
   else launch_decode_attn_d<128>(a, grid, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.D == 64) hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(a.B * a.Hq), dim3(kThreadsDec), 0, st, a);
-  else hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(a.B * a.Hq), dim3(kThreadsDec), 0, st, a);
+  if (a.D == 64) hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(a.B * a.Hq), dim3(kThreadsComb), 0, st, a);
+  else hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(a.B * a.Hq), dim3(kThreadsComb), 0, st, a);
   return hipGetLastError();
 }
 
