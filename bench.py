@@ -279,6 +279,12 @@ def main():
     import synth
     import learned_block_sparse_attngate_amd as seer
 
+    w = synth.WORKLOADS.get(args.workload)
+    if w is None or not isinstance(w["sparsity"], (float, tuple)):
+        usable = [k for k, v in synth.WORKLOADS.items() if isinstance(v["sparsity"], (float, tuple))]
+        print(f"bench.py needs a workload with a seeded block mask, one of {usable} (got {args.workload})",
+              file=sys.stderr)
+        sys.exit(2)
     seer.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
