@@ -223,7 +223,7 @@ seer_status seer_attn_maxpool_gt(const seer_shape* shape, const void* q, const v
  *   wk_per_kv_head); block_mask [B,Hq,nb] uint8 = score > threshold, or the
  *   top-k per (b,h) (ties to the lower j, all blocks if nb <= k); scores
  *   [B,Hq,nb] fp32 (required: it holds the logits, then the scores).
- *   nb <= 16384. No workspace.
+ *   q and kcomp 16-byte aligned. nb <= 16384. No workspace.
  * seer_decode_attn_fwd: O[b,h] = sum_u softmax_u(q[b,h] . K[b,g,u] / sqrt(D))
  *   V[b,g,u] over the keys of the blocks active in block_mask[b,h,:] (NULL:
  *   every block); out [B,Hq,D] in out_dtype, lse [B,Hq] (natural log) or

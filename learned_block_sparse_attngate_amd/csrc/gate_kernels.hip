@@ -703,13 +703,20 @@ __global__ __launch_bounds__(256) void decode_logits_kernel(DecodeGateArgs a) {
   if (j < a.nb) {
     const float4* kr = reinterpret_cast<const float4*>(
         a.kcomp + ((static_cast<size_t>(b) * hwk + w) * a.kcomp_blocks + j) * a.D + sub * dpl);
-    const uint16_t* qr = a.q + static_cast<size_t>(z) * a.D + sub * dpl;
-    for (int i = 0; i < dpl / 4; ++i) {
-      const float4 v = kr[i];
-      acc = fmaf(v.x, bf16_to_f32(qr[4 * i]), acc);
-      acc = fmaf(v.y, bf16_to_f32(qr[4 * i + 1]), acc);
-      acc = fmaf(v.z, bf16_to_f32(qr[4 * i + 2]), acc);
-      acc = fmaf(v.w, bf16_to_f32(qr[4 * i + 3]), acc);
+    // the lane's dpl query values as 16-byte loads (8 bf16 each; q rows are
+    // 16-byte aligned and dpl is 8 or 16)
+    const uint4* qr = reinterpret_cast<const uint4*>(a.q + static_cast<size_t>(z) * a.D + sub * dpl);
+    for (int i8 = 0; i8 < dpl / 8; ++i8) {
+      const uint4 qv = qr[i8];
+      const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float4 v = kr[2 * i8 + h];
+        acc = fmaf(v.x, __uint_as_float(qw[2 * h] << 16), acc);
+        acc = fmaf(v.y, __uint_as_float(qw[2 * h] & 0xffff0000u), acc);
+        acc = fmaf(v.z, __uint_as_float(qw[2 * h + 1] << 16), acc);
+        acc = fmaf(v.w, __uint_as_float(qw[2 * h + 1] & 0xffff0000u), acc);
+      }
     }
   }
   acc += __shfl_xor(acc, 1);

@@ -346,8 +346,9 @@ seer_status seer_decode_gate_fwd(const seer_shape* shape, int32_t wk_per_kv_head
   if (kcomp_blocks < nb)
     return fail(SEER_ERR_INVALID_ARG, "kcomp_blocks (%d) is smaller than the cache's %d blocks", kcomp_blocks, nb);
   if (empty) return ok();
-  if (q == nullptr || kcomp == nullptr || block_mask == nullptr || scores == nullptr || !aligned(kcomp, 16))
-    return fail(SEER_ERR_INVALID_ARG, "q, kcomp (16-byte aligned), scores and block_mask must be non-NULL");
+  if (q == nullptr || kcomp == nullptr || block_mask == nullptr || scores == nullptr || !aligned(kcomp, 16) ||
+      !aligned(q, 16))
+    return fail(SEER_ERR_INVALID_ARG, "q and kcomp (16-byte aligned), scores and block_mask must be non-NULL");
   if (!aligned(scores, 4)) return fail(SEER_ERR_INVALID_ARG, "scores must be 4-byte aligned");
   if ((st = check_device()) != SEER_OK) return st;
   seer::DecodeGateArgs a = decode_gate_args(shape, wk_per_kv_head);

@@ -149,6 +149,9 @@ def test_decode_validation():
                                     None, None) == B.SEER_ERR_INVALID_ARG
     assert lib.seer_decode_gate_fwd(ctypes.byref(s), 0, FAKE, FAKE, 16, B.SEER_MASK_THRESHOLD, 0.1, 1, None, None,
                                     FAKE, None) == B.SEER_ERR_INVALID_ARG          # scores hold the logits
+    assert lib.seer_decode_gate_fwd(ctypes.byref(s), 0, ctypes.c_void_p(0x10008), FAKE, 16, B.SEER_MASK_THRESHOLD, 0.1, 1, None,
+                                    FAKE, FAKE, None) == B.SEER_ERR_INVALID_ARG    # q not 16-byte aligned
+    assert b"16-byte aligned" in lib.seer_last_error()
     big = _shape(hq=32, hkv=2, s=1000)              # 16 query heads per KV head
     need = lib.seer_decode_attn_workspace_size(ctypes.byref(s))
     assert need > 0
