@@ -56,22 +56,32 @@ def parse():
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "attn_sparse_llama8b_s128k_90_counters.md")
-KERNEL_SRC = os.path.join(ROOT, "learned_block_sparse_attngate_amd", "csrc", "attn_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "learned_block_sparse_attngate_amd", "csrc", f) for f in ("attn_kernels.hip", "tile_ops.h")]
+
+
+def attention_source_digest():
+    """sha256 over the attention kernels' source files (attn_kernels.hip, then
+    tile_ops.h), which the committed counter summaries record."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str):
     """HBM bytes per attention call from the committed FETCH_SIZE / WRITE_SIZE
     summary, or None if that summary is missing, is for another workload, or
     was taken on a different version of the attention kernels' source."""
-    import hashlib
     try:
         text = open(COUNTERS).read()
-        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        src = attention_source_digest()
     except OSError:
         return None
     fields = dict(line.split(":", 1) for line in text.splitlines() if line.startswith("- ") and ":" in line)
     fields = {k[2:].strip(): v.strip().strip("`") for k, v in fields.items()}
-    if fields.get("workload") != workload or fields.get("attn_kernels.hip sha256") != src:
+    if fields.get("workload") != workload or fields.get("attention source sha256") != src:
         return None
     try:
         return int(fields["HBM bytes per call"])
@@ -87,14 +97,13 @@ def measured_mfma_busy(workload: str):
     busy (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs) and
     the engine clock during it, from the committed counter summary; None if
     that summary is missing, for another workload, or for other kernel source."""
-    import hashlib
     import re
     try:
         text = open(MFMA_COUNTERS).read()
-        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        src = attention_source_digest()
     except OSError:
         return None
-    if workload not in text.splitlines()[0] or f"attn_kernels.hip sha256 `{src}`" not in text:
+    if workload not in text.splitlines()[0] or f"attention source sha256 `{src}`" not in text:
         return None
     busy = re.search(r"The MFMA pipes are busy ([0-9.]+)% of the kernel's cycles", text)
     clk = re.search(r"The engine clock during the kernel is ([0-9.]+) GHz", text)

@@ -8,229 +8,248 @@
 // the gate is distilled against the attention map max-pooled along the
 // sequence (1D), which the dense mode here also emits.
 //
-// Design for CDNA4: the work is bound by reading the selected K/V blocks
-// (a few FLOP per byte), so it stays on the vector units and is organized for
-// memory parallelism:
-//  * one workgroup per (batch, KV head, key split): the query heads of a GQA
-//    group are processed together, so a block that several of them select is
-//    read once; a block no head of the group selects is never read (the
-//    split's active blocks are compacted on chip first);
-//  * the next active block's K and V are loaded into registers while the
-//    current one is processed, so every workgroup keeps two blocks in flight;
-//  * the key range is split so that B * Hkv * splits fills the GPU; each
-//    split keeps an online softmax per head and writes an unnormalized
-//    partial (sum of p v, running max, sum of p) that a small kernel merges;
-//  * Q . K: a lane quad per key, each lane a quarter of the head dimension,
-//    quad shuffles for the sums; P . V: a thread per (8 dims, key group) with
-//    16-byte V loads, partial sums kept per thread and reduced once per split;
-//  * softmax in the log2 domain (the query is pre-scaled by log2(e)/sqrt(D)).
+// Design for CDNA4: the work is bound by reading the selected K/V blocks, so
+// the arithmetic has to stay far below the memory time. It runs on the
+// matrix cores with the prefill kernels' tile machinery:
+//  * one wavefront per (batch, KV head, key split). The query heads of the
+//    GQA group are the 32 columns of S^T = K Q^T (columns past the group are
+//    zero), so a block that any head of the group selects is read once and
+//    costs 32 MFMAs; a block no head selects is never read (the split's
+//    active blocks are compacted on chip first);
+//  * K and V tiles go HBM -> LDS with buffer_load ... lds in the prefill's
+//    swizzled layout and are read with the same operand reads; P^T goes from
+//    the S^T registers straight into O^T = V^T P^T. The wave owns its two
+//    tile buffers, so the copy of block n+1's K starts as soon as block n's K
+//    operands are in registers (V likewise) and no barrier is needed;
+//  * each head (lane column) keeps an exact running max; keys past the cache
+//    and heads that did not select a block get -inf scores (P = 0);
+//  * the key range is split so that about kDecodeWaves wavefronts cover the
+//    cache; each split writes an unnormalized partial (sum of p v, running
+//    max, sum of p) per head, which a small kernel merges;
+//  * softmax in the log2 domain (scores scaled by log2(e)/sqrt(D)).
 #include "seer_device.h"
 #include "seer_internal.h"
+#include "tile_ops.h"
 
 namespace seer {
 
 namespace {
 
-constexpr int kThreadsDec = 256;
 constexpr int kMaxSplitBlocks = 256;         // blocks per key split (on-chip active list)
 constexpr int kMaxSplits = 1024;
+constexpr int kDecodeWaves = 1024;           // split wavefronts per call, about (4 per CU)
 
-template <int D, int G8>
-__global__ __launch_bounds__(kThreadsDec) void decode_attn_kernel(DecodeAttnArgs a) {
-  constexpr int DQ = D / 4;                  // Q . K: dims per lane (a lane quad per key)
-  constexpr int NV = D / 8;                  // P . V: groups of 8 dims (one 16-byte load)
-  constexpr int KG = kThreadsDec / NV;       // P . V: key groups
-  constexpr int KPT = kBlock / KG;           // P . V: keys per thread
-  constexpr int NW = kThreadsDec / kWave;
-  __shared__ float qs[G8][D];                // queries of the group, scaled to log2 units
-  __shared__ float ps[2][G8][kBlock];        // scores, then probabilities (double buffered by block)
-  __shared__ float alpha_s[2][G8];
-  __shared__ float m_s[G8], l_s[G8];
-  __shared__ uint16_t list[kMaxSplitBlocks];
-  __shared__ uint8_t list_act[kMaxSplitBlocks];
-  __shared__ int wcnt[NW];
-  __shared__ float red[NW][G8][D];
+template <int D>
+__global__ __launch_bounds__(kWave) void decode_attn_kernel(DecodeAttnArgs a) {
+  constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
+  constexpr int KS = D / 16;                 // MFMA k-steps of S^T
+  constexpr int MT = D / 32;                 // MFMA m-tiles of O^T
+  constexpr int RPI = 64 / CPR;              // tile rows per copy instruction
+  constexpr int NDMA = kBlock / RPI;         // copy instructions per tile and operand
+  __shared__ uint4 Ks[kBlock * CPR];
+  __shared__ uint4 Vs[kBlock * CPR];
+  __shared__ uint32_t list[kMaxSplitBlocks]; // block offset in the split | active heads << 16
 
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31, hl = lane >> 5;
   const int split = blockIdx.x;
   const int zg = blockIdx.y;                 // b * Hkv + g
   const int b = zg / a.Hkv, g = zg - b * a.Hkv;
-  const int G = a.group;                     // <= G8, the compiled bound
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int G = a.group;                     // <= kDecodeMaxGroup
   const int h_base = b * a.Hq + g * G;       // first query head (b, g*G)
   const int j0 = split * a.bps, j1 = min(a.nb, j0 + a.bps);
 
-  for (int i = tid; i < G * D; i += kThreadsDec) {
-    const int h = i / D, d = i - h * D;
-    qs[h][d] = bf16_to_f32(a.q[static_cast<size_t>(h_base + h) * D + d]) * a.scale_log2;
-  }
-  if (tid < G) {
-    m_s[tid] = -INFINITY;
-    l_s[tid] = 0.f;
-  }
   // active list of this split: blocks that some head of the group selects
-  int cnt;
-  {
-    const int j = j0 + tid;
-    unsigned act = 0;
-    if (j < j1)
-      for (int h = 0; h < G; ++h)
-        if (a.mask == nullptr || a.mask[static_cast<size_t>(h_base + h) * a.nb + j] != 0) act |= 1u << h;
-    const int f = act != 0;
-    const int inc = wave_inclusive_scan(f, lane);
-    if (lane == kWave - 1) wcnt[wave] = inc;
-    __syncthreads();
-    int base = 0;
-    for (int w2 = 0; w2 < wave; ++w2) base += wcnt[w2];
-    if (f) {
-      list[base + inc - 1] = static_cast<uint16_t>(j - j0);
-      list_act[base + inc - 1] = static_cast<uint8_t>(act);
+  int cnt = 0;
+  for (int jb = j0; jb < j1; jb += kWave) {
+    const int j = jb + lane;
+    uint32_t act = 0;
+    if (j < j1) {
+      if (a.mask == nullptr) {
+        act = (1u << G) - 1u;
+      } else {
+        for (int h = 0; h < G; ++h)
+          if (a.mask[static_cast<size_t>(h_base + h) * a.nb + j] != 0) act |= 1u << h;
+      }
     }
-    cnt = 0;
-    for (int w2 = 0; w2 < NW; ++w2) cnt += wcnt[w2];
-    __syncthreads();
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(act != 0);
+    if (act != 0) {
+      const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u)));
+      list[cnt + below] = static_cast<uint32_t>(j - j0) | (act << 16);
+    }
+    cnt += __popcll(bal);
   }
+  // B operand of S^T = K Q^T: column l32 is query head h_base + l32 (zero past
+  // the group), dims 16 ks + 8 hl .. +7
+  const bool col = l32 < G;
+  uint4 qreg[KS];
+  {
+    const uint16_t* qrow = a.q + static_cast<size_t>(h_base + (col ? l32 : 0)) * D + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qreg[ks] = col ? *reinterpret_cast<const uint4*>(qrow + 16 * ks) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();                           // the list is in LDS
+  wait_vm_le<0>();                           // and the Q rows in registers
 
+  // copies of the tile at token t0 (rows past the cache read as zeros):
+  // instruction i moves rows RPI i .. RPI i + RPI - 1, 1 KiB further on in
+  // memory and in LDS; the immediate offset carries i % 4 (it holds 12 bits)
+  uint32_t kofs[4], vofs;
+  {
+    const int r0 = lane / CPR, pc = lane % CPR;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kofs[u] = static_cast<uint32_t>(r0 * 2 * D + 16 * (pc ^ swz_k<D>(r0 + RPI * u)));
+    vofs = static_cast<uint32_t>(r0 * 2 * D + 16 * (pc ^ swz_v<D>(r0)));
+  }
   const uint16_t* kbase = a.k + static_cast<size_t>(zg) * a.S * D;
   const uint16_t* vbase = a.v + static_cast<size_t>(zg) * a.S * D;
-  const int uq = tid >> 2, c = tid & 3;      // Q . K: key, dim quarter
-  const int dg = tid % NV, kg = tid / NV;    // P . V: dim group, key group
-
-  float acc[G8][8];
-#pragma unroll
-  for (int h = 0; h < G8; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-
-  // K slice (key uq, dims c*DQ ..) and V rows (keys kg + KG*i, dims dg*8 ..) of list entry n
-  auto load = [&](int n, uint4 (&kr)[DQ / 8], uint4 (&vr)[KPT]) {
-    const int t0 = (j0 + list[n]) * kBlock;
-    const int n_tok = min(kBlock, a.S - t0);
-    const uint4* kp = reinterpret_cast<const uint4*>(kbase + (static_cast<size_t>(t0) + min(uq, n_tok - 1)) * D + c * DQ);
-#pragma unroll
-    for (int i = 0; i < DQ / 8; ++i) kr[i] = kp[i];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int u = kg + KG * i;
-      vr[i] = *reinterpret_cast<const uint4*>(vbase + (static_cast<size_t>(t0) + min(u, n_tok - 1)) * D + dg * 8);
-    }
+  auto issue = [&](const uint16_t* base, uint4* buf, bool is_k, int t0) {
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + static_cast<size_t>(t0) * D), 0,
+                                                      (a.S - t0) * 2 * D, kBufferWord3);
+    char* dst = reinterpret_cast<char*>(buf);
+    static_for<NDMA>([&](auto I) {
+      constexpr int i = decltype(I)::value, hi = i / 4;
+      const uint32_t ofs = is_k ? (D == 128 ? kofs[i & 3] : kofs[0]) : vofs;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + 4096 * hi), 16, ofs + 4096 * hi, 0,
+                                               1024 * (i % 4), 0);
+    });
   };
+  uint32_t kaddr[KS], vaddr[MT];
+  {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kaddr[ks] = lds_addr(Ks) + l32 * 2 * D + 16 * ((2 * ks + hl) ^ swz_k<D>(l32));
+    const int G4 = lane >> 4, jj = (lane >> 2) & 3, aa = lane & 3;
+    const int key = 4 * (G4 >> 1) + jj;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      vaddr[mt] = lds_addr(Vs) + key * 2 * D + 16 * ((4 * mt + 2 * (G4 & 1) + (aa >> 1)) ^ swz_v<D>(key)) + 8 * (aa & 1);
+  }
 
-  auto process = [&](int n, const uint4 (&kr)[DQ / 8], const uint4 (&vr)[KPT]) {
-    const int buf = n & 1;
-    const unsigned act = list_act[n];
-    const int t0 = (j0 + list[n]) * kBlock;
-    const int n_tok = min(kBlock, a.S - t0);
-    // Q . K for the active heads
-    float kf[DQ];
+  const float c = a.scale_log2;
+  float m = -INFINITY, lsum = 0.f;
+  f32x16_t oacc[MT];
 #pragma unroll
-    for (int i = 0; i < DQ / 8; ++i) {
-      const uint32_t wv[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kf[8 * i + 2 * e] = __uint_as_float(wv[e] << 16);
-        kf[8 * i + 2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
-      }
-    }
-    for (int h = 0; h < G; ++h) {
-      if (!(act >> h & 1u)) continue;        // uniform
-      float dot = 0.f;
-#pragma unroll
-      for (int i = 0; i < DQ; ++i) dot = fmaf(kf[i], qs[h][c * DQ + i], dot);
-      dot += __shfl_xor(dot, 1);
-      dot += __shfl_xor(dot, 2);
-      if (c == 0) ps[buf][h][uq] = uq < n_tok ? dot : -INFINITY;
-    }
-    __syncthreads();
-    // online softmax per head (wave w takes heads w, w + 4)
-    for (int h = wave; h < G; h += NW) {
-      if (!(act >> h & 1u)) continue;        // uniform per wave
-      const float sv = ps[buf][h][lane];
-      const float bmax = wave_max(sv);
-      const float mold = m_s[h];
-      const float mnew = fmaxf(mold, bmax);
-      const float pe = __builtin_amdgcn_exp2f(sv - mnew);     // 0 for keys past the cache
-      const float bsum = wave_sum(pe);
-      ps[buf][h][lane] = pe;
-      if (lane == 0) {
-        const float al = __builtin_amdgcn_exp2f(mold - mnew);   // 0 on the first block
-        alpha_s[buf][h] = al;
-        l_s[h] = l_s[h] * al + bsum;
-        m_s[h] = mnew;
-        if (a.gt != nullptr) a.gt[static_cast<size_t>(h_base + h) * a.nb + j0 + list[n]] = bmax;   // raw, log2
-      }
-    }
-    __syncthreads();
-    // P . V: each V element read once for every head
-    float vf[KPT][8];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const uint32_t wv[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vf[i][2 * e] = __uint_as_float(wv[e] << 16);
-        vf[i][2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G8; ++h) {
-      if (h >= G || !(act >> h & 1u)) continue;
-      const float al = alpha_s[buf][h];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= al;
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const float p = ps[buf][h][kg + KG * i];   // 0 past the cache
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[i][e], acc[h][e]);
-      }
-    }
-    // no barrier here: the next block writes the other ps / alpha buffer, and
-    // the one after that comes after two more barriers
-  };
+  for (int i = 0; i < MT; ++i) oacc[i] = f32x16_t{};
 
   if (cnt > 0) {
-    uint4 kA[DQ / 8], vA[KPT], kB[DQ / 8], vB[KPT];
-    load(0, kA, vA);
-    for (int n = 0; n < cnt; n += 2) {
-      if (n + 1 < cnt) load(n + 1, kB, vB);
-      process(n, kA, vA);
-      if (n + 1 >= cnt) break;
-      if (n + 2 < cnt) load(n + 2, kA, vA);
-      process(n + 1, kB, vB);
+    // list entries are read with waits of their own, outside the compiler's
+    // view of the copies in flight (it would otherwise wait for all of them),
+    // and kept in scalar registers (the copies take a scalar base address)
+    uint32_t e = __builtin_amdgcn_readfirstlane(lds_read_u32(lds_addr(&list[0])));
+    int t0 = (j0 + static_cast<int>(e & 0xffffu)) * kBlock;
+    issue(kbase, Ks, true, t0);
+    issue(vbase, Vs, false, t0);
+    const bool want_gt = a.gt != nullptr;
+    const uint32_t all_heads = (1u << G) - 1u;
+    for (int n = 0; n < cnt; ++n) {
+      const uint32_t act = e >> 16;
+      const int jcur = j0 + static_cast<int>(e & 0xffffu);
+      const int tcur = t0;
+      const bool more = n + 1 < cnt;
+      if (more) {
+        e = __builtin_amdgcn_readfirstlane(lds_read_u32(lds_addr(&list[n + 1])));
+        t0 = (j0 + static_cast<int>(e & 0xffffu)) * kBlock;
+      }
+      // K of this block has landed once only its V copy (and the previous
+      // block's map store) is younger
+      if (want_gt && n > 0) wait_vm_le<NDMA + 1>();
+      else wait_vm_le<NDMA>();
+      u32x4_t kr[2 * KS];
+      read_k_tile<D>(kaddr, kr);
+      if (more) issue(kbase, Ks, true, t0);
+      f32x16_t sacc[2];
+      sacc[0] = f32x16_t{};
+      sacc[1] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          sacc[mt] = mfma_32x32x16(__builtin_bit_cast(uint4, kr[2 * ks + mt]), qreg[ks], sacc[mt]);
+      // -inf for keys past the cache and for heads that did not select the
+      // block (columns past the group compute on zero queries and are never
+      // stored); most blocks are whole and selected by every head
+      const int n_tok = min(kBlock, a.S - tcur);
+      const bool on = col && ((act >> l32) & 1u);
+      if (n_tok < kBlock || act != all_heads) {
+        // key 32 mt + 8 (r / 4) + 4 hl + r % 4 >= n_tok, with the lane's part on the right
+        const int lim = on ? n_tok - 4 * hl : -kBlock;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * mt + 8 * (r >> 2) + (r & 3) >= lim) sacc[mt][r] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
+      const float bmax = pair_max(mx) * c;   // block max of the head, log2 units
+      // V of this block has landed once only the next block's K copy is younger
+      if (more) wait_vm_le<NDMA>();
+      else wait_vm_le<0>();
+      u32x2_t vr[8 * MT];
+      read_v_tile<D>(vaddr, vr);
+      if (want_gt && hl == 0 && on) a.gt[static_cast<size_t>(h_base + l32) * a.nb + jcur] = bmax;
+      if (more) issue(vbase, Vs, false, t0);
+      // online softmax (exact running max) and O^T += V^T P^T
+      const float mn = fmaxf(m, bmax);
+      if (__builtin_amdgcn_ballot_w64(mn > m)) {
+        const float alpha = mn > m ? __builtin_amdgcn_exp2f(m - mn) : 1.f;   // m = -inf: 0
+        lsum *= alpha;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) oacc[i] *= alpha;
+      }
+      m = mn;
+      const float mu = m == -INFINITY ? 0.f : m;   // no score yet: P = exp2(-inf) = 0
+      uint4 pb[4];
+      float ls = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          float ev[8];
+#pragma unroll
+          for (int s8 = 0; s8 < 8; ++s8) {
+            ev[s8] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][8 * hh + s8], c, -mu));
+            ls += ev[s8];
+          }
+          pb[2 * mt + hh] = make_uint4(pack_bf16x2(ev[0], ev[1]), pack_bf16x2(ev[2], ev[3]),
+                                       pack_bf16x2(ev[4], ev[5]), pack_bf16x2(ev[6], ev[7]));
+        }
+      lsum += ls;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const u32x2_t lo = vr[(ks * MT + mt) * 2], hi = vr[(ks * MT + mt) * 2 + 1];
+          oacc[mt] = mfma_32x32x16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[ks], oacc[mt]);
+        }
     }
   }
 
-  // ---- partial of this split: sum over the key groups, then (acc, max, sum) per head
+  // partial of this split per head: O^T column l32, dims 32 mt + 8 r4 + 4 hl ..
+  const float ltot = pair_sum(lsum);
+  if (col) {
+    float* pr = a.part + (static_cast<size_t>(h_base + l32) * a.nsplit + split) * (D + 2);
 #pragma unroll
-  for (int h = 0; h < G8; ++h)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = acc[h][e];
-#pragma unroll
-      for (int o = NV; o < kWave; o <<= 1) x += __shfl_xor(x, o);   // key groups inside the wave
-      acc[h][e] = x;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dim = 32 * mt + 8 * r4 + 4 * hl;
+        *reinterpret_cast<float2*>(pr + dim) = make_float2(oacc[mt][4 * r4 + 0], oacc[mt][4 * r4 + 1]);
+        *reinterpret_cast<float2*>(pr + dim + 2) = make_float2(oacc[mt][4 * r4 + 2], oacc[mt][4 * r4 + 3]);
+      }
+    if (hl == 0) {
+      pr[D] = m;
+      pr[D + 1] = ltot;
     }
-  if (lane < NV) {
-#pragma unroll
-    for (int h = 0; h < G8; ++h)
-      if (h < G)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) red[wave][h][dg * 8 + e] = acc[h][e];
-  }
-  __syncthreads();
-  for (int i = tid; i < G * D; i += kThreadsDec) {
-    const int h = i / D, d = i - h * D;
-    float t = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) t += red[w2][h][d];
-    a.part[(static_cast<size_t>(h_base + h) * a.nsplit + split) * (D + 2) + d] = t;
-  }
-  if (tid < G) {
-    float* pr = a.part + (static_cast<size_t>(h_base + tid) * a.nsplit + split) * (D + 2);
-    pr[D] = m_s[tid];
-    pr[D + 1] = l_s[tid];
   }
 }
+
 
 // Merge the key splits of one (batch, head): O = sum_s 2^(m_s - M) acc_s / L,
 // L = sum_s 2^(m_s - M) l_s, LSE = (M + log2 L) ln 2; in dense mode the raw
@@ -298,13 +317,11 @@ __global__ __launch_bounds__(kThreadsComb) void decode_combine_kernel(DecodeAttn
 
 }  // namespace
 
-// Key splits: about 512 (batch, KV head, split) workgroups, 8 to 256 blocks
-// per split, at most 1024 splits. At 128k (8 KV heads, 2048 blocks) 512
-// workgroups of 32 blocks measured 47 us against 50 us for 1024 of 16 and
-// 59 us for 2048 of 8: fewer, longer splits pay the per-split setup less often.
+// Key splits: about kDecodeWaves (batch, KV head, split) wavefronts, 8 to
+// 256 blocks per split, at most kMaxSplits splits.
 void decode_split(int B, int Hkv, int nb, int* nsplit, int* bps) {
   const long long groups = static_cast<long long>(B) * Hkv;
-  long long target = groups > 0 ? (512 + groups - 1) / groups : 1;
+  long long target = groups > 0 ? (kDecodeWaves + groups - 1) / groups : 1;
   if (target < 1) target = 1;
   long long per = (nb + target - 1) / target;
   if (per < 8) per = 8;
@@ -314,19 +331,10 @@ void decode_split(int B, int Hkv, int nb, int* nsplit, int* bps) {
   *nsplit = nb > 0 ? static_cast<int>((nb + per - 1) / per) : 1;
 }
 
-template <int D>
-void launch_decode_attn_d(const DecodeAttnArgs& a, dim3 grid, hipStream_t st) {
-  // register arrays sized by the smallest compiled group bound that fits
-  if (a.group <= 1) hipLaunchKernelGGL((decode_attn_kernel<D, 1>), grid, dim3(kThreadsDec), 0, st, a);
-  else if (a.group <= 2) hipLaunchKernelGGL((decode_attn_kernel<D, 2>), grid, dim3(kThreadsDec), 0, st, a);
-  else if (a.group <= 4) hipLaunchKernelGGL((decode_attn_kernel<D, 4>), grid, dim3(kThreadsDec), 0, st, a);
-  else hipLaunchKernelGGL((decode_attn_kernel<D, kDecodeMaxGroup>), grid, dim3(kThreadsDec), 0, st, a);
-}
-
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t st) {
   const dim3 grid(a.nsplit, a.B * a.Hkv);
-  if (a.D == 64) launch_decode_attn_d<64>(a, grid, st);
-  else launch_decode_attn_d<128>(a, grid, st);
+  if (a.D == 64) hipLaunchKernelGGL(decode_attn_kernel<64>, grid, dim3(kWave), 0, st, a);
+  else hipLaunchKernelGGL(decode_attn_kernel<128>, grid, dim3(kWave), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.D == 64) hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(a.B * a.Hq), dim3(kThreadsComb), 0, st, a);
