@@ -409,16 +409,12 @@ __device__ __forceinline__ int wave_sum_int(int x) {
 // the later steps are integer compares on the keys alone.
 // The row's first n of nb entries are its logits (the rest are written as
 // probability 0 and mask 0); k is its top-k count (mode 1); hist is this
-// wavefront's 256-word LDS histogram.
+// wavefront's 256-word LDS histogram. vec: the row's scores may be accessed
+// as 16-byte groups and its mask bytes as 4-byte groups.
 template <int G>
 __device__ __forceinline__ void wave_softmax_mask_row(float* srow, uint8_t* mrow, int n, int nb, int mode,
-                                                      float threshold, int k, uint32_t* hist) {
+                                                      float threshold, int k, bool vec, uint32_t* hist) {
   const int lane = threadIdx.x & 63;
-  // 16-byte score and 4-byte mask accesses only for whole groups of 4 and
-  // where the row pointers allow them (the caller's maps need only 4-byte
-  // and 1-byte alignment)
-  const bool vec = (nb & 3) == 0 && (reinterpret_cast<uintptr_t>(srow) & 15) == 0 &&
-                   (reinterpret_cast<uintptr_t>(mrow) & 3) == 0;
 
   float v[G][4];                                        // logits; -inf past the causal end
 #pragma unroll
@@ -587,12 +583,18 @@ __device__ __forceinline__ void wave_softmax_mask_row(float* srow, uint8_t* mrow
 template <int G>
 __global__ __launch_bounds__(256) void gate_softmax_mask_wave_kernel(GateArgs a, TopkTable tk) {
   __shared__ __align__(16) uint32_t hist_all[4][256];
-  const int wave = threadIdx.x >> 6;
+  // the row, its pointers and the access width are wave-uniform: scalar
+  // addresses and branches
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const long long row = static_cast<long long>(blockIdx.x) * 4 + wave;
   if (row >= static_cast<long long>(a.B) * a.Hq * a.nb) return;
   const int z = static_cast<int>(row / a.nb), i = static_cast<int>(row - static_cast<long long>(z) * a.nb);
+  // 16-byte score and 4-byte mask accesses when every row allows them (the
+  // caller's maps need only 4-byte and 1-byte alignment)
+  const bool vec = (a.nb & 3) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.mask) & 3) == 0;
   wave_softmax_mask_row<G>(a.scores + static_cast<size_t>(row) * a.nb, a.mask + static_cast<size_t>(row) * a.nb,
-                           i + 1, a.nb, a.mode, a.threshold, tk.k[z % a.Hq], hist_all[wave]);
+                           i + 1, a.nb, a.mode, a.threshold, tk.k[z % a.Hq], vec, hist_all[wave]);
 }
 
 
@@ -788,7 +790,8 @@ __global__ __launch_bounds__(256) void gate_rope_kernel(float* __restrict__ x, i
 // sum and their dz is 0 without a per-element test.
 template <int G>
 __global__ __launch_bounds__(256) void gate_kl_wave_kernel(GateArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));   // wave-uniform row
+  const int lane = threadIdx.x & 63;
   const long long row = static_cast<long long>(blockIdx.x) * 4 + wave;
   if (row >= static_cast<long long>(a.B) * a.Hq * a.nb) return;
   const int nb = a.nb;
@@ -796,9 +799,9 @@ __global__ __launch_bounds__(256) void gate_kl_wave_kernel(GateArgs a) {
   const int n = i + 1;
   float* zrow = a.scores + static_cast<size_t>(row) * nb;
   const float* grow = a.gt + static_cast<size_t>(row) * nb;
-  // 16-byte accesses only for whole groups of 4 and where both row pointers
-  // allow them (gt needs only 4-byte alignment)
-  const bool vec = (nb & 3) == 0 && ((reinterpret_cast<uintptr_t>(zrow) | reinterpret_cast<uintptr_t>(grow)) & 15) == 0;
+  // 16-byte accesses when every row allows them (gt needs only 4-byte
+  // alignment)
+  const bool vec = (nb & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.scores) | reinterpret_cast<uintptr_t>(a.gt)) & 15) == 0;
   float zv[G][4], gv[G][4];
 #pragma unroll
   for (int t = 0; t < G; ++t) {
