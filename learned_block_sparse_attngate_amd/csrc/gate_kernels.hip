@@ -729,14 +729,235 @@ __global__ __launch_bounds__(256) void decode_logits_kernel(DecodeGateArgs a) {
 
 // One workgroup per (batch, query head): softmax over every block, in place,
 // and the mask.
-__global__ __launch_bounds__(kST) void decode_gate_kernel(DecodeGateArgs a, TopkTable tk) {
-  extern __shared__ float row[];             // nb floats
-  const int z = blockIdx.x;                  // b * Hq + h
-  float* srow = a.scores + static_cast<size_t>(z) * a.nb;
-  for (int j = threadIdx.x; j < a.nb; j += kST) row[j] = srow[j];
-  __syncthreads();
-  softmax_mask_row(row, srow, a.mask + static_cast<size_t>(z) * a.nb, a.nb, a.nb, a.mode, a.threshold,
-                   tk.k[z % a.Hq]);
+// Decode rows: one workgroup of four wavefronts per row z = b * Hq + h (with
+// one row per (batch, head) a single wavefront per row has too little work to
+// hide its latency). The steps of wave_softmax_mask_row, with every maximum,
+// count and histogram taken over the four wavefronts through LDS; wavefront w
+// holds entries 1024 t + 256 w + 4 lane + e of the row, and every entry is
+// valid (the newest token sees every cached block).
+constexpr int kRowWaves = 4;
+template <int G>
+__global__ __launch_bounds__(kRowWaves * kWave) void decode_gate_kernel(DecodeGateArgs a, TopkTable tk) {
+  __shared__ float redf[2][kRowWaves];
+  __shared__ int redi[2][kRowWaves];
+  __shared__ __align__(16) uint32_t hist[3][256];      // one per mantissa pass, zeroed up front
+  __shared__ int tab[G][kRowWaves];                   // entries equal to the k-th value per 256-entry chunk
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int z = blockIdx.x;
+  const int nb = a.nb;
+  float* srow = a.scores + static_cast<size_t>(z) * nb;
+  uint8_t* mrow = a.mask + static_cast<size_t>(z) * nb;
+  // 16-byte score and 4-byte mask accesses when every row allows them
+  const bool vec = (nb & 3) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.mask) & 3) == 0;
+  for (int i = threadIdx.x; i < 3 * 256; i += kRowWaves * kWave) hist[i >> 8][i & 255] = 0u;
+
+  // workgroup-wide reductions, one barrier each: consecutive reductions use
+  // alternate slots, so a slot is rewritten only after the next barrier
+  int slot = 0;
+  auto all_max = [&](float x) {
+    x = wave_max(x);
+    if (lane == 0) redf[slot][wave] = x;
+    __syncthreads();
+    const float r = fmaxf(fmaxf(redf[slot][0], redf[slot][1]), fmaxf(redf[slot][2], redf[slot][3]));
+    slot ^= 1;
+    return r;
+  };
+  auto all_sum = [&](float x) {
+    x = wave_sum(x);
+    if (lane == 0) redf[slot][wave] = x;
+    __syncthreads();
+    const float r = (redf[slot][0] + redf[slot][1]) + (redf[slot][2] + redf[slot][3]);
+    slot ^= 1;
+    return r;
+  };
+  auto all_max_int = [&](int x) {                     // x: wave-uniform or per lane
+    x = wave_max_int(x);
+    if (lane == 0) redi[slot][wave] = x;
+    __syncthreads();
+    const int r = max(max(redi[slot][0], redi[slot][1]), max(redi[slot][2], redi[slot][3]));
+    slot ^= 1;
+    return r;
+  };
+  auto all_add_int = [&](int x) {                     // x: wave-uniform
+    if (lane == 0) redi[slot][wave] = x;
+    __syncthreads();
+    const int r = redi[slot][0] + redi[slot][1] + redi[slot][2] + redi[slot][3];
+    slot ^= 1;
+    return r;
+  };
+
+  float v[G][4];
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    const int j0 = 1024 * t + 256 * wave + 4 * lane;
+    if (vec && j0 + 3 < nb) {
+      const float4 x = *reinterpret_cast<const float4*>(srow + j0);
+      v[t][0] = x.x; v[t][1] = x.y; v[t][2] = x.z; v[t][3] = x.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[t][e] = j0 + e < nb ? srow[j0 + e] : -INFINITY;
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < G; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, v[t][e]);
+  mx = all_max(mx);
+  float sum = 0.f;
+#pragma unroll
+  for (int t = 0; t < G; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = v[t][e] == -INFINITY ? -0.0f : expf(v[t][e] - mx);
+      v[t][e] = x;
+      sum += x;
+    }
+  sum = all_sum(sum);
+  const float inv = 1.0f / sum;
+  uint32_t key[G][4];                                 // probability bit patterns; -0 past the row
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[t][e] = __float_as_uint(v[t][e] * inv);
+    const int j0 = 1024 * t + 256 * wave + 4 * lane;
+    const float p0 = __uint_as_float(key[t][0] & 0x7fffffffu), p1 = __uint_as_float(key[t][1] & 0x7fffffffu);
+    const float p2 = __uint_as_float(key[t][2] & 0x7fffffffu), p3 = __uint_as_float(key[t][3] & 0x7fffffffu);
+    if (vec) {
+      if (j0 < nb) *reinterpret_cast<float4*>(srow + j0) = make_float4(p0, p1, p2, p3);
+    } else {
+      if (j0 < nb) srow[j0] = p0;
+      if (j0 + 1 < nb) srow[j0 + 1] = p1;
+      if (j0 + 2 < nb) srow[j0 + 2] = p2;
+      if (j0 + 3 < nb) srow[j0 + 3] = p3;
+    }
+  }
+
+  // keep: key > lim as signed integers, plus (top-k) the first kk equal to lim
+  const int k = tk.k[z % a.Hq];
+  int32_t lim = -1;                                   // every entry
+  int kk = 0;
+  if (a.mode == 0) {
+    const float T = a.threshold;
+    lim = T > 0.f ? static_cast<int32_t>(__float_as_uint(T)) : (T == 0.f ? 0 : (T < 0.f ? -1 : INT32_MAX));
+  } else if (k < nb) {
+    // exponent of the k-th largest probability by binary search on counts of
+    // keys >= 2^e, then its mantissa 8 bits at a time from bit 22
+    auto count_ge = [&](int32_t c) {
+      int cnt = 0;
+#pragma unroll
+      for (int t = 0; t < G; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(static_cast<int32_t>(key[t][e]) >= c));
+      return all_add_int(cnt);
+    };
+    int32_t kmax = INT32_MIN;
+#pragma unroll
+    for (int t = 0; t < G; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kmax = max(kmax, static_cast<int32_t>(key[t][e]));
+    int lo = 0, hi = all_max_int(kmax) >> 23;           // count(>= 2^lo) = nb >= k; the answer is <= hi
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (count_ge(mid << 23) >= k) lo = mid;
+      else hi = mid - 1;
+    }
+    uint32_t prefix = static_cast<uint32_t>(lo) << 23, pmask = 0xff800000u;
+    kk = k - count_ge((lo + 1) << 23);
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass < 2 ? 15 - 8 * pass : 0;
+      const uint32_t width = pass < 2 ? 255u : 127u;
+      uint32_t* h = hist[pass];
+#pragma unroll
+      for (int t = 0; t < G; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((key[t][e] & pmask) == prefix) atomicAdd(&h[(key[t][e] >> shift) & width], 1u);
+      __syncthreads();
+      // every wavefront reads the whole histogram and takes the same bin;
+      // lane L owns bins 255-4L .. 252-4L
+      const uint4 c4 = *reinterpret_cast<const uint4*>(h + 252 - 4 * lane);
+      const int cnt4[4] = {static_cast<int>(c4.w), static_cast<int>(c4.z), static_cast<int>(c4.y),
+                           static_cast<int>(c4.x)};
+      const int own = cnt4[0] + cnt4[1] + cnt4[2] + cnt4[3];
+      const int inc = wave_inclusive_scan(own, lane);
+      int above = inc - own;
+      int bin = 0, rem = 0;
+      bool found = false;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (above < kk && above + cnt4[e] >= kk) {
+          found = true;
+          bin = 255 - 4 * lane - e;
+          rem = kk - above;
+        }
+        above += cnt4[e];
+      }
+      const int src = static_cast<int>(__builtin_ctzll(__builtin_amdgcn_ballot_w64(found)));
+      bin = __shfl(bin, src, kWave);
+      kk = __shfl(rem, src, kWave);
+      prefix |= static_cast<uint32_t>(bin) << shift;
+      pmask |= width << shift;
+    }
+    lim = static_cast<int32_t>(prefix);
+    int eq = 0;
+#pragma unroll
+    for (int t = 0; t < G; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) eq += key[t][e] == prefix;
+    if (all_add_int(wave_sum_int(eq)) <= kk) {        // no more equal to the k-th value than are kept
+      lim -= 1;
+      kk = 0;
+    }
+  }
+  // the kk entries equal to lim with the lowest indices are kept as well:
+  // count them per 256-entry chunk first
+  if (kk > 0) {
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+      int eq = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) eq += key[t][e] == static_cast<uint32_t>(lim);
+      eq = wave_sum_int(eq);
+      if (lane == 0) tab[t][wave] = eq;
+    }
+    __syncthreads();
+  }
+  int before = 0;                                     // equal entries in the chunks before this one
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    uint32_t keep = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) keep |= static_cast<uint32_t>(static_cast<int32_t>(key[t][e]) > lim) << (8 * e);
+    if (kk > 0) {
+      int b0 = before;
+      for (int w = 0; w < wave; ++w) b0 += tab[t][w];
+      int eq = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) eq += key[t][e] == static_cast<uint32_t>(lim);
+      const int inc = wave_inclusive_scan(eq, lane);
+      int b = b0 + inc - eq;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (key[t][e] == static_cast<uint32_t>(lim)) {
+          if (b < kk) keep |= 1u << (8 * e);
+          ++b;
+        }
+      before += tab[t][0] + tab[t][1] + tab[t][2] + tab[t][3];
+    }
+    const int j0 = 1024 * t + 256 * wave + 4 * lane;
+    if (vec) {
+      if (j0 < nb) *reinterpret_cast<uint32_t*>(mrow + j0) = keep;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j0 + e < nb) mrow[j0 + e] = static_cast<uint8_t>(keep >> (8 * e));
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1045,8 +1266,12 @@ hipError_t launch_decode_gate(const DecodeGateArgs& a, const TopkTable& tk, hipS
                      st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_gate_kernel, dim3(a.B * a.Hq), dim3(kST), static_cast<size_t>(a.nb) * sizeof(float), st,
-                     a, tk);
+  const dim3 grid(a.B * a.Hq), block(kRowWaves * kWave);
+  if (a.nb <= 1024) hipLaunchKernelGGL(decode_gate_kernel<1>, grid, block, 0, st, a, tk);
+  else if (a.nb <= 2048) hipLaunchKernelGGL(decode_gate_kernel<2>, grid, block, 0, st, a, tk);
+  else if (a.nb <= 4096) hipLaunchKernelGGL(decode_gate_kernel<4>, grid, block, 0, st, a, tk);
+  else if (a.nb <= 8192) hipLaunchKernelGGL(decode_gate_kernel<8>, grid, block, 0, st, a, tk);
+  else hipLaunchKernelGGL(decode_gate_kernel<16>, grid, block, 0, st, a, tk);
   return hipGetLastError();
 }
 
