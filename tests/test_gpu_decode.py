@@ -90,6 +90,31 @@ def test_decode_gate_matches_oracle(per_kv, shape):
         assert bad == 0
 
 
+
+@pytest.mark.parametrize("mode", ["topk", "threshold"])
+def test_decode_gate_misaligned_maps_equal_aligned(mode):
+    """Scores 4 bytes and mask 1 byte past 16-byte alignment (the ABI asks
+    only for 4- and 1-byte alignment) give the same bits as aligned maps, at a
+    row length that is a multiple of 4 (the 16-byte path when aligned)."""
+    seer = _seer()
+    shape = Shape(2, 8, 2, 64 * 1200, 64)
+    say(f"[decode gate misaligned] shape={shape} mode={mode}")
+    qd, k, _, wk = _inputs(shape, 93, False, var=4.0 / 128)
+    kc = seer.seer_decode_compress_k(dev_bf16(k), dev_f32(wk), shape.heads_q)
+    nb = shape.nb
+    kw = dict(mode="topk", topk=[5, 120] * (shape.heads_q // 2)) if mode == "topk" else dict(mode="threshold", threshold=1.5 / nb)
+    q = dev_bf16(qd)
+    m0, s0 = seer.seer_decode_gate_fwd(q, kc, shape.seq_len, shape.heads_kv, **kw)
+    n = shape.batch * shape.heads_q * nb
+    sc1 = torch.zeros(n + 1, dtype=torch.float32, device="cuda")[1:].view(shape.batch, shape.heads_q, nb)
+    mk1 = torch.zeros(n + 1, dtype=torch.uint8, device="cuda")[1:].view(shape.batch, shape.heads_q, nb)
+    assert sc1.data_ptr() % 16 == 4 and mk1.data_ptr() % 4 == 1
+    m1, s1 = seer.seer_decode_gate_fwd(q, kc, shape.seq_len, shape.heads_kv, scores=sc1, block_mask=mk1, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(s0, s1) and torch.equal(m0, m1)
+    if mode == "topk":
+        assert torch.equal(m0.sum(-1).cpu(), torch.tensor([5, 120] * (shape.heads_q // 2)).repeat(shape.batch, 1))
+
 DECODE_CASES = [
     # name, shape, mask density (None: dense), out dtype
     ("llama8b_s131072_p10", Shape(1, 32, 8, 131072, 128), 0.1, torch.bfloat16),
