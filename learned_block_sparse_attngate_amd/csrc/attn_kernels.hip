@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   auto compute = [&](auto diag_tag, int kb, int next, bool first) {
     constexpr bool kDiag = decltype(diag_tag)::value;   // the diagonal tile needs element causality
     // ---- K: wait for the copy (only V of this tile and newer stores may be outstanding)
-    wait_vmcnt(first ? NDMA : NDMA + stores_pending);
+    wait_vm(first ? NDMA : NDMA + stores_pending);
     wg_barrier();
     u32x4_t kr[2 * KS];                           // kr[2 ks + mt]: keys 32 mt + l32, dims 16 ks + 8 hl ..
     read_k_tile<D>(kaddr, kr);
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
     }
 
     // ---- V: wait for the copy (the K copy of `next` and this tile's store may be newer)
-    wait_vmcnt((next >= 0 ? NDMA : 0) + stores_now);
+    wait_vm((next >= 0 ? NDMA : 0) + stores_now);
     wg_barrier();
     u32x2_t vr[8 * MT];                            // vr[(ks MT + mt) 2 + u]: dims 32 mt + .., keys 16 ks + 8 u + ..
     read_v_tile<D>(vaddr, vr);
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
       compute(std::true_type{}, qb, nxt, true);
       issued = cnt > 0;
     } else if (has_diag) {
-      wait_vmcnt(0);                            // the early copy of the diagonal tile is not used
+      wait_vm(0);                            // the early copy of the diagonal tile is not used
       wg_barrier();
     }
     if (cnt > 0) {
@@ -539,17 +539,6 @@ constexpr int kXcdDefaultChunk = 128;    // 4 MiB of K/V at D = 128: one XCD's L
 constexpr int kXcdMinBlocks = 1280;      // rows of 80k tokens and more
 constexpr int kXcdSlots = 128;           // resident workgroups per XCD: 32 CUs x 4
 
-// s_waitcnt vmcnt(n) for the counts the persistent kernel uses; anything else
-// waits for every operation in flight.
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 4: __builtin_amdgcn_s_waitcnt(0x0f74); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0f78); break;
-    case 12: __builtin_amdgcn_s_waitcnt(0x0f7c); break;
-    case 16: __builtin_amdgcn_s_waitcnt(0x4f70); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0f70); break;
-  }
-}
 
 // Job at position t of XCD x's sequence, or -1 past its end. Positions 2i and
 // 2i+1 take jobs 16i + x and 16i + 15 - x; the first job past the end ends it.

@@ -41,17 +41,6 @@ template <int D> __device__ __forceinline__ int swz_v(int row) { return D == 128
 // with lgkmcnt waits; a fence would also wait for every copy in flight.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left at their maxima)
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0f70); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0x0f71); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0f74); break;
-    case 5: __builtin_amdgcn_s_waitcnt(0x0f75); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0f78); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0f79); break;
-  }
-}
 
 // LDS reads outside the compiler's view of the copies in flight; each waits
 // for its own result before returning.
@@ -158,6 +147,22 @@ template <int N>
 __device__ __forceinline__ void wait_vm_le() {
   static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xf00 | ((N >> 4) << 14));
+}
+
+// s_waitcnt vmcnt(n) for a count known only at run time: the counts the
+// kernels use have their own instruction; any other count waits for every
+// operation in flight, which is always safe
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 1: wait_vm_le<1>(); break;
+    case 4: wait_vm_le<4>(); break;
+    case 5: wait_vm_le<5>(); break;
+    case 8: wait_vm_le<8>(); break;
+    case 9: wait_vm_le<9>(); break;
+    case 12: wait_vm_le<12>(); break;
+    case 16: wait_vm_le<16>(); break;
+    default: wait_vm_le<0>(); break;
+  }
 }
 
 }  // namespace seer
