@@ -55,8 +55,9 @@ def test_compress_k_full_and_incremental(shape, per_kv):
 @pytest.mark.parametrize("per_kv,shape", [(False, Shape(2, 8, 2, 64 * 300 - 33, 128)),
                                            (True, Shape(2, 8, 2, 64 * 300 - 33, 128)),
                                            (False, Shape(1, 4, 1, 64 * 2101 - 5, 64)),
-                                           (True, Shape(1, 4, 2, 64 * 4100, 64))],
-                         ids=["wk_per_q", "wk_per_kv", "nb2101", "nb4100_kvw"])
+                                           (True, Shape(1, 4, 2, 64 * 4100, 64)),
+                                           (False, Shape(1, 4, 1, 64 * 9000 + 7, 64))],
+                         ids=["wk_per_q", "wk_per_kv", "nb2101", "nb4100_kvw", "nb9001"])
 def test_decode_gate_matches_oracle(per_kv, shape):
     seer = _seer()
     say(f"[decode gate] shape={shape} per_kv={per_kv}")
