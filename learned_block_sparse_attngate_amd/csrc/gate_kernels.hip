@@ -221,15 +221,28 @@ __global__ __launch_bounds__(kGT) void gate_proj_kernel(GateArgs a) {
   }
 }
 
-// Causal 64 x 64 tiles of the block logits z = Q' K'^T / sqrt(D).
-__global__ __launch_bounds__(kGT) void gate_logits_kernel(GateArgs a) {
-  // triangular decode of blockIdx.x -> (ti, tj), tj <= ti
-  const int idx = blockIdx.x;
+// Causal 64 x 64 tiles of the block logits z = Q' K'^T / sqrt(D). One
+// workgroup per (row z = b * Hq + h, causal tile); ntri tiles per row.
+// Workgroup w runs on XCD w % 8: when the rows split evenly over the 8 XCDs,
+// XCD x takes whole rows z = x, x + 8, ... in turn, so each row's Q' and K'
+// are fetched into one XCD's L2 instead of all eight.
+__global__ __launch_bounds__(kGT) void gate_logits_kernel(GateArgs a, int ntri) {
+  const int w = blockIdx.x;
+  const int nz = a.B * a.Hq;
+  int z, idx;
+  if (nz % 8 == 0) {
+    const int i = w / 8;
+    z = w % 8 + 8 * (i / ntri);
+    idx = i % ntri;
+  } else {
+    z = w / ntri;
+    idx = w % ntri;
+  }
+  // triangular decode of idx -> (ti, tj), tj <= ti
   int ti = static_cast<int>((sqrtf(8.0f * idx + 1.0f) - 1.0f) * 0.5f);
   while ((ti + 1) * (ti + 2) / 2 <= idx) ++ti;
   while (ti * (ti + 1) / 2 > idx) --ti;
   const int tj = idx - ti * (ti + 1) / 2;
-  const int z = blockIdx.y;                  // b * Hq + h
   const int b = z / a.Hq, h = z % a.Hq;
   const int hk = a.wk_per_kv ? h / a.group : h;
   const int hwk = a.wk_per_kv ? a.Hkv : a.Hq;
@@ -1230,8 +1243,13 @@ hipError_t launch_gate_logits(const GateArgs& a, hipStream_t st) {
   }
 
   const int T = (a.nb + kBM - 1) / kBM;
-  dim3 gl(T * (T + 1) / 2, a.B * a.Hq);
-  hipLaunchKernelGGL(gate_logits_kernel, gl, dim3(kGT), 0, st, a);
+  const int ntri = T * (T + 1) / 2;
+  const long long nwg = static_cast<long long>(ntri) * a.B * a.Hq;
+  // a 1D grid holds fewer than 2^32 work-items (any score map that fits in
+  // device memory is far below this)
+  if (nwg * kGT > 0xffffffffLL) return hipErrorInvalidValue;
+  const dim3 gl(static_cast<unsigned>(nwg));
+  hipLaunchKernelGGL(gate_logits_kernel, gl, dim3(kGT), 0, st, a, ntri);
   return hipGetLastError();
 }
 
