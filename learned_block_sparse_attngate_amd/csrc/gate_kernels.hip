@@ -428,6 +428,10 @@ template <int G>
 __device__ __forceinline__ void wave_softmax_mask_row(float* srow, uint8_t* mrow, int n, int nb, int mode,
                                                       float threshold, int k, bool vec, uint32_t* hist) {
   const int lane = threadIdx.x & 63;
+  // 256-entry groups that hold causal entries (wave-uniform): the later ones
+  // hold only -0.0 keys, which no count, histogram or maximum below can see,
+  // so short rows skip them
+  const int gn = (n + 255) >> 8;
 
   float v[G][4];                                        // logits; -inf past the causal end
 #pragma unroll
@@ -449,13 +453,19 @@ __device__ __forceinline__ void wave_softmax_mask_row(float* srow, uint8_t* mrow
   mx = wave_max(mx);
   float sum = 0.f;
 #pragma unroll
-  for (int t = 0; t < G; ++t)
+  for (int t = 0; t < G; ++t) {
+    if (t < gn) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = v[t][e] == -INFINITY ? -0.0f : expf(v[t][e] - mx);
-      v[t][e] = x;
-      sum += x;
+      for (int e = 0; e < 4; ++e) {
+        const float x = v[t][e] == -INFINITY ? -0.0f : expf(v[t][e] - mx);
+        v[t][e] = x;
+        sum += x;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[t][e] = -0.0f;
     }
+  }
   sum = wave_sum(sum);
   const float inv = 1.0f / sum;
   uint32_t key[G][4];
@@ -494,16 +504,18 @@ __device__ __forceinline__ void wave_softmax_mask_row(float* srow, uint8_t* mrow
       int cnt = 0;
 #pragma unroll
       for (int t = 0; t < G; ++t)
+        if (t < gn)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(static_cast<int32_t>(key[t][e]) >= c));
+          for (int e = 0; e < 4; ++e)
+            cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(static_cast<int32_t>(key[t][e]) >= c));
       return cnt;
     };
     int32_t kmax = INT32_MIN;
 #pragma unroll
     for (int t = 0; t < G; ++t)
+      if (t < gn)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) kmax = max(kmax, static_cast<int32_t>(key[t][e]));
+        for (int e = 0; e < 4; ++e) kmax = max(kmax, static_cast<int32_t>(key[t][e]));
     int lo = 0, hi = wave_max_int(kmax) >> 23;          // count(>= 2^lo) = n >= k; the answer is <= hi
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -520,9 +532,10 @@ __device__ __forceinline__ void wave_softmax_mask_row(float* srow, uint8_t* mrow
       wave_lds_sync();
 #pragma unroll
       for (int t = 0; t < G; ++t)
+        if (t < gn)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if ((key[t][e] & pmask) == prefix) atomicAdd(&hist[(key[t][e] >> shift) & width], 1u);
+          for (int e = 0; e < 4; ++e)
+            if ((key[t][e] & pmask) == prefix) atomicAdd(&hist[(key[t][e] >> shift) & width], 1u);
       wave_lds_sync();
       const uint4 c4 = *reinterpret_cast<const uint4*>(hist + 252 - 4 * lane);
       const int cnt4[4] = {static_cast<int>(c4.w), static_cast<int>(c4.z), static_cast<int>(c4.y),
@@ -553,8 +566,9 @@ __device__ __forceinline__ void wave_softmax_mask_row(float* srow, uint8_t* mrow
     int eq_total = 0;
 #pragma unroll
     for (int t = 0; t < G; ++t)
+      if (t < gn)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) eq_total += key[t][e] == prefix;
+        for (int e = 0; e < 4; ++e) eq_total += key[t][e] == prefix;
     if (wave_sum_int(eq_total) <= kk) {
       lim -= 1;                                         // > prefix - 1  <=>  >= prefix
       kk = 0;
@@ -567,7 +581,7 @@ __device__ __forceinline__ void wave_softmax_mask_row(float* srow, uint8_t* mrow
     uint32_t keep = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) keep |= static_cast<uint32_t>(static_cast<int32_t>(key[t][e]) > lim) << (8 * e);
-    if (kk > 0) {
+    if (kk > 0 && t < gn) {
       int eq = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) eq += key[t][e] == static_cast<uint32_t>(lim);
