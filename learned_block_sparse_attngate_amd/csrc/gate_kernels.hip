@@ -1077,11 +1077,15 @@ __global__ __launch_bounds__(256) void gate_kl_wave_kernel(GateArgs a) {
     }
   mx = wave_max(mx);
   gsum = wave_sum(gsum);
+  // 256-entry groups holding causal entries (wave-uniform); the later ones
+  // add nothing to l or the loss and take dz = 0
+  const int gn = (n + 255) >> 8;
   float l = 0.f;
 #pragma unroll
   for (int t = 0; t < G; ++t)
+    if (t < gn)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) l += expf(zv[t][e] - mx);
+      for (int e = 0; e < 4; ++e) l += expf(zv[t][e] - mx);
   l = wave_sum(l);
   const float lse = mx + logf(l);
   const bool valid = gsum > 0.f;             // a row without ground-truth mass contributes nothing
@@ -1090,13 +1094,15 @@ __global__ __launch_bounds__(256) void gate_kl_wave_kernel(GateArgs a) {
   float kl = 0.f;
 #pragma unroll
   for (int t = 0; t < G; ++t) {
-    float dz[4];
+    float dz[4] = {0.f, 0.f, 0.f, 0.f};
+    if (t < gn) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float ls = zv[t][e] - lse;
-      const float pj = gv[t][e] * inv_g;
-      if (pj > 0.f) kl += pj * (logf(pj) - ls);
-      dz[e] = valid ? (expf(ls) - pj) * inv_rows : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const float ls = zv[t][e] - lse;
+        const float pj = gv[t][e] * inv_g;
+        if (pj > 0.f) kl += pj * (logf(pj) - ls);
+        dz[e] = valid ? (expf(ls) - pj) * inv_rows : 0.f;
+      }
     }
     const int j0 = 256 * t + 4 * lane;
     if (vec) {
