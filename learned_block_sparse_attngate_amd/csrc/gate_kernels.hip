@@ -137,15 +137,34 @@ template <bool A_T, bool B_T>
 __device__ __forceinline__ void gemm_accum(f32x16_t& acc, const float* __restrict__ A, int lda,
                                            const float* __restrict__ B, int ldb, int M, int N, int k0, int k1,
                                            int m0, int n0) {
-  __shared__ float As[kBK][kBM + 4];
-  __shared__ float Bs[kBK][kBN + 4];
+  __shared__ __align__(16) float As[kBK][kBM + 4];
+  __shared__ __align__(16) float Bs[kBK][kBN + 4];
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int qm = 32 * (w & 1) + (lane & 31), qn = 32 * (w >> 1) + (lane & 31), kh = lane >> 5;
+  // 16-byte loads (one per operand and thread) for chunks inside the matrices
+  // when the strides and bases allow them; 4-byte loads otherwise
+  const bool vec_ok = (((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0) &&
+                      ((lda | ldb | k0) & 3) == 0 && m0 + kBM <= M && n0 + kBN <= N;
   // the next chunk's operands are loaded into registers while this chunk's
   // products run: A tile 64 x 16 (stored transposed), B tile 16 x 64
   float ra[4], rb[4];
+  bool rvec = false;                         // ra / rb hold one 16-byte group each
+  // 16-byte group of thread t: A (m, k..k+3) or, transposed, (k, m..m+3);
+  // B (k, n..n+3) or, transposed, (n, k..k+3)
+  const int va_r = A_T ? (tid >> 4) : (tid >> 2), va_c = A_T ? 4 * (tid & 15) : 4 * (tid & 3);
+  const int vb_r = B_T ? (tid >> 2) : (tid >> 4), vb_c = B_T ? 4 * (tid & 3) : 4 * (tid & 15);
   auto gload = [&](int kb) {
+    rvec = vec_ok && kb + kBK <= k1;
+    if (rvec) {
+      const float4 x = A_T ? *reinterpret_cast<const float4*>(A + static_cast<size_t>(kb + va_r) * lda + m0 + va_c)
+                           : *reinterpret_cast<const float4*>(A + static_cast<size_t>(m0 + va_r) * lda + kb + va_c);
+      const float4 y = B_T ? *reinterpret_cast<const float4*>(B + static_cast<size_t>(n0 + vb_r) * ldb + kb + vb_c)
+                           : *reinterpret_cast<const float4*>(B + static_cast<size_t>(kb + vb_r) * ldb + n0 + vb_c);
+      ra[0] = x.x; ra[1] = x.y; ra[2] = x.z; ra[3] = x.w;
+      rb[0] = y.x; rb[1] = y.y; rb[2] = y.z; rb[3] = y.w;
+      return;
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int idx = tid + kGT * e;         // 0..1023
@@ -161,11 +180,26 @@ __device__ __forceinline__ void gemm_accum(f32x16_t& acc, const float* __restric
   };
   if (k0 < k1) gload(k0);
   for (int kb = k0; kb < k1; kb += kBK) {
+    if (rvec) {
+      if (A_T) {
+        *reinterpret_cast<float4*>(&As[va_r][va_c]) = make_float4(ra[0], ra[1], ra[2], ra[3]);
+      } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int idx = tid + kGT * e;
-      As[A_T ? (idx >> 6) : (idx & 15)][A_T ? (idx & 63) : (idx >> 4)] = ra[e];
-      Bs[B_T ? (idx & 15) : (idx >> 6)][B_T ? (idx >> 4) : (idx & 63)] = rb[e];
+        for (int e = 0; e < 4; ++e) As[va_c + e][va_r] = ra[e];
+      }
+      if (B_T) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Bs[vb_c + e][vb_r] = rb[e];
+      } else {
+        *reinterpret_cast<float4*>(&Bs[vb_r][vb_c]) = make_float4(rb[0], rb[1], rb[2], rb[3]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = tid + kGT * e;
+        As[A_T ? (idx >> 6) : (idx & 15)][A_T ? (idx & 63) : (idx >> 4)] = ra[e];
+        Bs[B_T ? (idx & 15) : (idx >> 6)][B_T ? (idx >> 4) : (idx & 63)] = rb[e];
+      }
     }
     __syncthreads();
     if (kb + kBK < k1) gload(kb + kBK);
