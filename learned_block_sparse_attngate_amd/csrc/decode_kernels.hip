@@ -193,6 +193,9 @@ __global__ __launch_bounds__(kWave) void decode_attn_kernel(DecodeAttnArgs a) {
       else wait_vm_le<0>();
       u32x2_t vr[8 * MT];
       read_v_tile<D>(vaddr, vr);
+      // the map store sits between this block's V wait and the next V copy,
+      // which the next K wait counts; the map exists only in dense mode,
+      // where lane 0 always stores, so it is exactly one store instruction
       if (want_gt && hl == 0 && on) a.gt[static_cast<size_t>(h_base + l32) * a.nb + jcur] = bmax;
       if (more) issue(vbase, Vs, false, t0);
       // online softmax (exact running max) and O^T += V^T P^T
