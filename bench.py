@@ -176,6 +176,17 @@ def bench_decode(seer, torch, q, k, v, shape, stream, seed, reps: int = 50):
         return e0.elapsed_time(e1) * 1e3 / reps          # microseconds
 
     step_us = timed(step)
+    # the same step captured once as a HIP graph and replayed: the five
+    # launches of a decode step without the per-launch host work
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph_us = timed(graph.replay)
+    torch.cuda.synchronize()
+    graph_same = bool(torch.equal(out, ref))
     sparse_us = timed(sparse_attn)
     dense_us = timed(dense_attn)
     m = mask.cpu().numpy().astype(bool).reshape(B, Hkv, Hq // Hkv, nb)
@@ -183,11 +194,13 @@ def bench_decode(seer, torch, q, k, v, shape, stream, seed, reps: int = 50):
     blk_bytes = 2 * 64 * D * 2                            # K + V of one block, bf16
     sparse_bytes = union_blocks * blk_bytes + B * Hq * (nb + 4 * D)
     dense_bytes = B * Hkv * nb * blk_bytes + B * Hq * 4 * D
-    print(f"[bench] decode step {step_us:.1f} us; decode attention sparse {sparse_us:.1f} us "
+    print(f"[bench] decode step {step_us:.1f} us ({graph_us:.1f} us replayed as a graph, output "
+          f"{'identical' if graph_same else 'DIFFERENT'}); decode attention sparse {sparse_us:.1f} us "
           f"({sparse_bytes / sparse_us / 1e3:.0f} GB/s), dense {dense_us:.1f} us "
           f"({dense_bytes / dense_us / 1e3:.0f} GB/s)", file=sys.stderr, flush=True)
     return {"workload": f"newest token of the {S}-token cache, top-k {k_dec} of {nb} blocks per head",
-            "step_us": round(step_us, 2), "sparse_attention_us": round(sparse_us, 2),
+            "step_us": round(step_us, 2), "step_us_graph": round(graph_us, 2), "graph_output_identical": graph_same,
+            "sparse_attention_us": round(sparse_us, 2),
             "dense_attention_us": round(dense_us, 2), "speedup_attention": round(dense_us / sparse_us, 3),
             "blocks_read_union": union_blocks, "blocks_selected": int(m.sum()),
             "roofline": {"bound": "hbm", "achieved": round(sparse_bytes / sparse_us / 1e3, 1),
