@@ -14,8 +14,11 @@
 //  * one wavefront per (batch, KV head, key split). The query heads of the
 //    GQA group are the 32 columns of S^T = K Q^T (columns past the group are
 //    zero), so a block that any head of the group selects is read once and
-//    costs 32 MFMAs; a block no head selects is never read (the split's
-//    active blocks are compacted on chip first);
+//    costs 32 MFMAs; a block no head selects is never read. A small kernel
+//    first compacts each group's selected blocks into a list, and the splits
+//    take even shares of it, so that no split reads many more blocks than
+//    the others (a fixed block range per split left the splits that hold the
+//    masks' stripes and sink several times the average);
 //  * K and V tiles go HBM -> LDS with buffer_load ... lds in the prefill's
 //    swizzled layout and are read with the same operand reads; P^T goes from
 //    the S^T registers straight into O^T = V^T P^T. The wave owns its two
@@ -48,7 +51,7 @@ __global__ __launch_bounds__(kWave) void decode_attn_kernel(DecodeAttnArgs a) {
   constexpr int NDMA = kBlock / RPI;         // copy instructions per tile and operand
   __shared__ uint4 Ks[kBlock * CPR];
   __shared__ uint4 Vs[kBlock * CPR];
-  __shared__ uint32_t list[kMaxSplitBlocks]; // block offset in the split | active heads << 16
+  __shared__ uint32_t list[kMaxSplitBlocks]; // block - jbase | selecting heads << 16
 
   const int lane = threadIdx.x;
   const int l32 = lane & 31, hl = lane >> 5;
@@ -59,19 +62,22 @@ __global__ __launch_bounds__(kWave) void decode_attn_kernel(DecodeAttnArgs a) {
   const int h_base = b * a.Hq + g * G;       // first query head (b, g*G)
   const int j0 = split * a.bps, j1 = min(a.nb, j0 + a.bps);
 
-  // active list of this split: blocks that some head of the group selects
+  // active list of this split. Sparse mode: an even share of the KV group's
+  // compacted list (blocks that some head of the group selects), so that
+  // every split reads about as many blocks; dense mode: the block range.
   int cnt = 0;
-  for (int jb = j0; jb < j1; jb += kWave) {
+  if (a.mask != nullptr) {
+    const int total = a.bcount[zg];
+    const int per = (total + a.nsplit - 1) / a.nsplit;    // <= bps
+    const int e0 = min(total, split * per), e1 = min(total, e0 + per);
+    const uint32_t* src = a.blist + static_cast<size_t>(zg) * a.nb;
+    for (int e = e0 + lane; e < e1; e += kWave) list[e - e0] = src[e];   // absolute blocks
+    cnt = e1 - e0;
+  }
+  const int jbase = a.mask != nullptr ? 0 : j0;  // list entries hold block - jbase
+  for (int jb = j0; a.mask == nullptr && jb < j1; jb += kWave) {
     const int j = jb + lane;
-    uint32_t act = 0;
-    if (j < j1) {
-      if (a.mask == nullptr) {
-        act = (1u << G) - 1u;
-      } else {
-        for (int h = 0; h < G; ++h)
-          if (a.mask[static_cast<size_t>(h_base + h) * a.nb + j] != 0) act |= 1u << h;
-      }
-    }
+    const uint32_t act = j < j1 ? (1u << G) - 1u : 0u;
     const uint64_t bal = __builtin_amdgcn_ballot_w64(act != 0);
     if (act != 0) {
       const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
@@ -139,19 +145,19 @@ __global__ __launch_bounds__(kWave) void decode_attn_kernel(DecodeAttnArgs a) {
     // view of the copies in flight (it would otherwise wait for all of them),
     // and kept in scalar registers (the copies take a scalar base address)
     uint32_t e = __builtin_amdgcn_readfirstlane(lds_read_u32(lds_addr(&list[0])));
-    int t0 = (j0 + static_cast<int>(e & 0xffffu)) * kBlock;
+    int t0 = (jbase + static_cast<int>(e & 0xffffu)) * kBlock;
     issue(kbase, Ks, true, t0);
     issue(vbase, Vs, false, t0);
     const bool want_gt = a.gt != nullptr;
     const uint32_t all_heads = (1u << G) - 1u;
     for (int n = 0; n < cnt; ++n) {
       const uint32_t act = e >> 16;
-      const int jcur = j0 + static_cast<int>(e & 0xffffu);
+      const int jcur = jbase + static_cast<int>(e & 0xffffu);
       const int tcur = t0;
       const bool more = n + 1 < cnt;
       if (more) {
         e = __builtin_amdgcn_readfirstlane(lds_read_u32(lds_addr(&list[n + 1])));
-        t0 = (j0 + static_cast<int>(e & 0xffffu)) * kBlock;
+        t0 = (jbase + static_cast<int>(e & 0xffffu)) * kBlock;
       }
       // K of this block has landed once only its V copy (and the previous
       // block's map store) is younger
@@ -254,6 +260,43 @@ __global__ __launch_bounds__(kWave) void decode_attn_kernel(DecodeAttnArgs a) {
 }
 
 
+// Compacted block list of each (batch, KV group) for sparse mode: the blocks
+// that some head of the group selects, ascending, as block | heads << 16, and
+// their count. One workgroup per group; 1024 blocks per round, ordered by a
+// ballot inside each wavefront and the wavefront totals across them.
+constexpr int kListThreads = 1024;
+__global__ __launch_bounds__(kListThreads) void decode_list_kernel(DecodeAttnArgs a) {
+  __shared__ int wsum[kListThreads / kWave];
+  const int zg = blockIdx.x;
+  const int b = zg / a.Hkv, g = zg - b * a.Hkv;
+  const int G = a.group;
+  const int h_base = b * a.Hq + g * G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t* dst = a.blist + static_cast<size_t>(zg) * a.nb;
+  int base = 0;
+  for (int jb = 0; jb < a.nb; jb += kListThreads) {
+    const int j = jb + tid;
+    uint32_t act = 0;
+    if (j < a.nb)
+      for (int h = 0; h < G; ++h)
+        if (a.mask[static_cast<size_t>(h_base + h) * a.nb + j] != 0) act |= 1u << h;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(act != 0);
+    const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u)));
+    if (lane == 0) wsum[wave] = __popcll(bal);
+    __syncthreads();
+    int before = base, tot = 0;
+    for (int w = 0; w < kListThreads / kWave; ++w) {
+      if (w < wave) before += wsum[w];
+      tot += wsum[w];
+    }
+    if (act != 0) dst[before + below] = static_cast<uint32_t>(j) | (act << 16);
+    base += tot;
+    __syncthreads();                         // wsum is rewritten next round
+  }
+  if (tid == 0) a.bcount[zg] = base;
+}
+
 // Merge the key splits of one (batch, head): O = sum_s 2^(m_s - M) acc_s / L,
 // L = sum_s 2^(m_s - M) l_s, LSE = (M + log2 L) ln 2; in dense mode the raw
 // block maxima become the 1D max-pooled map gt_j = 2^(r_j - log2-sum-exp).
@@ -334,7 +377,19 @@ void decode_split(int B, int Hkv, int nb, int* nsplit, int* bps) {
   *nsplit = nb > 0 ? static_cast<int>((nb + per - 1) / per) : 1;
 }
 
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int nb, int D) {
+  int nsplit = 1, bps = 1;
+  decode_split(B, Hkv, nb, &nsplit, &bps);
+  const size_t part = static_cast<size_t>(B) * Hq * nsplit * (D + 2) * sizeof(float);
+  return (part + 15) / 16 * 16 + static_cast<size_t>(B) * Hkv * (static_cast<size_t>(nb) + 1) * sizeof(uint32_t);
+}
+
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t st) {
+  if (a.mask != nullptr) {
+    hipLaunchKernelGGL(decode_list_kernel, dim3(a.B * a.Hkv), dim3(kListThreads), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid(a.nsplit, a.B * a.Hkv);
   if (a.D == 64) hipLaunchKernelGGL(decode_attn_kernel<64>, grid, dim3(kWave), 0, st, a);
   else hipLaunchKernelGGL(decode_attn_kernel<128>, grid, dim3(kWave), 0, st, a);

@@ -367,9 +367,8 @@ seer_status seer_decode_gate_fwd(const seer_shape* shape, int32_t wk_per_kv_head
 size_t seer_decode_attn_workspace_size(const seer_shape* shape) {
   bool empty = false;
   if (check_shape(shape, &empty) != SEER_OK || empty) return 0;
-  int nsplit = 1, bps = 1;
-  seer::decode_split(shape->batch, shape->heads_kv, static_cast<int>(nblocks(shape)), &nsplit, &bps);
-  return static_cast<size_t>(shape->batch) * shape->heads_q * nsplit * (shape->head_dim + 2) * sizeof(float);
+  return seer::decode_workspace_bytes(shape->batch, shape->heads_q, shape->heads_kv, static_cast<int>(nblocks(shape)),
+                                      shape->head_dim);
 }
 
 seer_status seer_decode_attn_fwd(const seer_shape* shape, const void* q, const void* k_cache, const void* v_cache,
@@ -413,6 +412,13 @@ seer_status seer_decode_attn_fwd(const seer_shape* shape, const void* q, const v
   a.out_bf16 = out_dtype == SEER_BF16;
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(shape->head_dim)));
   seer::decode_split(a.B, a.Hkv, a.nb, &a.nsplit, &a.bps);
+  {
+    // block lists after the partials (16-byte aligned)
+    const size_t part_bytes = static_cast<size_t>(a.B) * a.Hq * a.nsplit * (a.D + 2) * sizeof(float);
+    char* base = static_cast<char*>(workspace) + (part_bytes + 15) / 16 * 16;
+    a.blist = reinterpret_cast<uint32_t*>(base);
+    a.bcount = reinterpret_cast<int*>(base + static_cast<size_t>(a.B) * a.Hkv * a.nb * sizeof(uint32_t));
+  }
   hipError_t e = seer::launch_decode_attn(a, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SEER_ERR_HIP, "decode attention launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -120,6 +120,8 @@ struct DecodeAttnArgs {
   float* lse;          // [B,Hq] or null
   float* gt;           // [B,Hq,nb] 1D max-pooled map or null (dense mode only)
   float* part;         // [B*Hq][nsplit][D + 2] partial (acc, max, sum) per key split
+  uint32_t* blist;     // [B*Hkv][nb] block | selecting heads << 16, compacted per KV group (sparse mode)
+  int* bcount;         // [B*Hkv] entries of blist per KV group
   int B, Hq, Hkv, S, D, nb, group;
   int nsplit, bps;     // key splits and blocks per split
   int out_bf16;
@@ -127,6 +129,8 @@ struct DecodeAttnArgs {
 };
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t st);
 void decode_split(int B, int Hkv, int nb, int* nsplit, int* bps);
+// bytes of the decode-attention workspace: partials, then the compacted block lists
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int nb, int D);
 hipError_t launch_gate_distill(const GateArgs& a, hipStream_t st);
 
 }  // namespace seer

@@ -161,9 +161,12 @@ def test_decode_validation():
                                     need, None) == B.SEER_ERR_INVALID_ARG          # gt with a mask
     assert lib.seer_decode_attn_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, B.SEER_F32, None, None, FAKE,
                                     need - 1, None) == B.SEER_ERR_WORKSPACE
-    # partials: one (D + 2)-float record per query head and key split
-    splits = need // (4 * 4 * (128 + 2))
-    assert need == 4 * 4 * splits * (128 + 2) and 1 <= splits <= 16
+    # partials: one (D + 2)-float record per query head and key split (padded
+    # to 16 bytes), then per KV head a compacted list of the 16 blocks and its count
+    lists = 2 * (16 + 1) * 4
+    part = need - lists
+    splits = part // (4 * 4 * (128 + 2))
+    assert part == (4 * 4 * splits * (128 + 2) + 15) // 16 * 16 and 1 <= splits <= 16
 
 
 def test_varlen_validation_and_sizes():
