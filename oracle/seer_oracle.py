@@ -508,16 +508,3 @@ def maxpool_gt(q, k, block: int = BLOCK) -> np.ndarray:
     for (b, h, i), r in zip(rows, maxpool_gt_rows(q, k, rows, block)):
         gt[b, h, i] = r
     return gt
-
-
-# --------------------------------------------------------------------------
-# Work accounting used by reports (counts only; no arithmetic of the method)
-# --------------------------------------------------------------------------
-def executed_tiles(block_mask, seq_len: int, block: int = BLOCK) -> int:
-    """Number of causal (query block, key block) tiles a mask activates."""
-    nb = n_blocks(seq_len, block)
-    if block_mask is None:
-        return nb * (nb + 1) // 2
-    m = np.asarray(block_mask).astype(bool)
-    tri = np.tril(np.ones((nb, nb), dtype=bool))
-    return int((m & tri).sum())

@@ -11,6 +11,8 @@ least one pin. Sources of truth used here:
     1/(i+1); a one-hot V returns the attention probabilities themselves;
   * brute force in pure Python (math.exp loops) on tiny inputs;
   * a hand-computed gate example under tests/golden/;
+  * the bfloat16 format's definition (sign, 8-bit exponent, 7-bit fraction)
+    and torch's bfloat16 dtype, for the widening of raw bf16 bit patterns;
   * invariants the pages state: softmax rows sum to 1 (explainer section 3.4,
     "After softmax, each row sums to 1.0"); the max-pooled value of a block is
     small only if every entry in it is small (section 3.4, "Ground truth
@@ -654,6 +656,83 @@ def pin_decode_masks(O):
             assert [int(x) for x in m[b, h]] == [1 if j in keep else 0 for j in range(40)]
 
 
+# ----------------------------------------------------------------------------
+# bfloat16 inputs: the oracle widens raw bf16 bit patterns (uint16), which is
+# how every seeded generator hands Q, K and V to both sides
+# ----------------------------------------------------------------------------
+def _bf16_definition(bits: int) -> float:
+    """Value of one bfloat16 pattern from the format's definition: 1 sign bit,
+    8 exponent bits (bias 127), 7 fraction bits; exponent 0 is subnormal."""
+    sign = -1.0 if bits >> 15 else 1.0
+    e, m = (bits >> 7) & 0xFF, bits & 0x7F
+    assert e != 0xFF, "inf/NaN patterns are not inputs"
+    mag = math.ldexp(m, -133) if e == 0 else math.ldexp(128 + m, e - 134)
+    return math.copysign(mag, sign)
+
+
+def _torch_widen(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64 through torch's own bfloat16 dtype."""
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def pin_bf16_bits_widening(O):
+    """as_f64 on uint16 patterns gives the exact bfloat16 values: hand-checked
+    patterns, every finite pattern against the format's definition and
+    against torch's bfloat16, signed zeros kept."""
+    table = {0x3F80: 1.0, 0xBF80: -1.0, 0xC020: -2.5, 0x4049: 3.140625, 0x3F81: 1.0 + 2.0 ** -7,
+             0x0001: 2.0 ** -133, 0x0080: 2.0 ** -126, 0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127,
+             0x0000: 0.0, 0x8000: -0.0}
+    keys = np.array(sorted(table), dtype=np.uint16)
+    got = O.as_f64(keys)
+    assert got.dtype == np.float64
+    for b, g in zip(keys.tolist(), got.tolist()):
+        assert g == table[b] and math.copysign(1.0, g) == math.copysign(1.0, table[b]), (hex(b), g)
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = ((allbits >> 7) & 0xFF) != 0xFF
+    pats = allbits[finite]
+    got = O.as_f64(pats)
+    want = np.array([_bf16_definition(int(b)) for b in pats.tolist()])
+    assert np.array_equal(got, want) and np.array_equal(np.signbit(got), np.signbit(want))
+    assert np.array_equal(got, _torch_widen(pats))
+    # shape is kept
+    assert O.as_f64(pats[:24].reshape(2, 3, 4)).shape == (2, 3, 4)
+
+
+def pin_bf16_inputs_match_widened_floats(O):
+    """Every entry point gives bit-identical results on bf16 bit patterns and
+    on the same values widened to float64 by torch."""
+    shape = Shape(1, 4, 2, 150, 16)
+    qb, kb, vb = gen_qkv(shape, 21)
+    qf, kf, vf = _torch_widen(qb), _torch_widen(kb), _torch_widen(vb)
+    m = gen_tiny_mask(shape, 22, p_keep=0.6).mask
+    ob, lb = O.attention(qb, kb, vb, m)
+    of, lf = O.attention(qf, kf, vf, m)
+    assert np.array_equal(ob, of) and np.array_equal(lb, lf)
+    assert np.array_equal(O.maxpool_gt(qb, kb), O.maxpool_gt(qf, kf))
+    assert np.array_equal(O.pool_q(qb), O.pool_q(qf)) and np.array_equal(O.pool_k(kb), O.pool_k(kf))
+    rng = np.random.default_rng(23)
+    wq = rng.standard_normal((4, 16, 16)).astype(np.float32)
+    wk = rng.standard_normal((4, 48, 16)).astype(np.float32)
+    assert np.array_equal(O.gate_scores(qb, kb, wq, wk), O.gate_scores(qf, kf, wq, wk))
+    assert np.array_equal(O.gate_scores(qb, kb, wq, wk, rope_theta=1e4),
+                          O.gate_scores(qf, kf, wq, wk, rope_theta=1e4))
+    gt = O.maxpool_gt(qf, kf)
+    lb_, gqb, gkb = O.gate_distill(qb, kb, wq, wk, gt)
+    lf_, gqf, gkf = O.gate_distill(qf, kf, wq, wk, gt)
+    assert lb_ == lf_ and np.array_equal(gqb, gqf) and np.array_equal(gkb, gkf)
+    qd_b = qb[:, :, -1]
+    qd_f = qf[:, :, -1]
+    wd = rng.standard_normal((4, 48, 16)).astype(np.float32)
+    kcb, kcf = O.decode_kcomp(kb, wd, 4), O.decode_kcomp(kf, wd, 4)
+    assert np.array_equal(kcb, kcf)
+    assert np.array_equal(O.decode_gate_scores(qd_b, kcb), O.decode_gate_scores(qd_f, kcf))
+    dm = (rng.random((1, 4, shape.nb)) < 0.5).astype(np.uint8)
+    for a, b in zip(O.decode_attention(qd_b, kb, vb, dm), O.decode_attention(qd_f, kf, vf, dm)):
+        assert np.array_equal(a, b)
+    assert np.array_equal(O.decode_gt(qd_b, kb), O.decode_gt(qd_f, kf))
+
+
 ATTENTION_PINS = [pin_dense_matches_torch_sdpa, pin_probabilities_via_one_hot_v,
                   pin_constant_v_and_empty_rows, pin_q_zero_closed_form, pin_single_block_row,
                   pin_gqa_equals_mha, pin_bruteforce_python_loops]
@@ -667,4 +746,5 @@ ROPE_PINS = [pin_rope_hand_complex, pin_rope_relative_and_orthogonal, pin_gate_r
 DISTILL_PINS = [pin_distill_finite_differences, pin_distill_loss_definition]
 DECODE_PINS = [pin_decode_attention_matches_sdpa_and_prefill, pin_decode_gt_bruteforce_and_2d, pin_decode_gate,
                pin_decode_masks]
-ALL_PINS = ATTENTION_PINS + GT_PINS + GATE_PINS + MASK_PINS + ROPE_PINS + DISTILL_PINS + DECODE_PINS
+INPUT_PINS = [pin_bf16_bits_widening, pin_bf16_inputs_match_widened_floats]
+ALL_PINS = INPUT_PINS + ATTENTION_PINS + GT_PINS + GATE_PINS + MASK_PINS + ROPE_PINS + DISTILL_PINS + DECODE_PINS

@@ -19,6 +19,9 @@ SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__
 
 # (name, old text, new text, which occurrence of old text to replace)
 MUTATIONS = [
+    ("as_f64_bits_shift", "(a.astype(np.uint32) << 16)", "(a.astype(np.uint32) << 15)", 0),
+    ("as_f64_bits_not_reinterpreted", "<< 16).view(np.float32)", "<< 16).astype(np.float32)", 0),
+    ("as_f64_bits_read_as_integers", "if a.dtype == np.uint16:", "if a.dtype == np.int8:", 0),
     ("pool_k_max_to_min", "out[..., i, 0:D] = blk.max(axis=-2)", "out[..., i, 0:D] = blk.min(axis=-2)", 0),
     ("pool_k_order_swapped",
      "out[..., i, D:2 * D] = blk.min(axis=-2)\n        out[..., i, 2 * D:3 * D] = blk.mean(axis=-2)",
