@@ -148,16 +148,83 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t: torch.Tensor, name: str, dtype: torch.dtype):
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+def _need(t, name: str, dtype: torch.dtype, shape=None):
+    """Validate one tensor before its pointer goes to the C ABI, which takes
+    raw pointers and trusts their extents: type, dtype, exact shape and
+    contiguity (the device is checked by _devices once every shape is).
+    Raises TypeError / ValueError; nothing is launched."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
 
+def _opt(t, name: str, dtype: torch.dtype, shape):
+    if t is not None:
+        _need(t, name, dtype, shape)
+
+
+def _devices(dev: torch.device, **tensors):
+    """Every given tensor is a CUDA (HIP) tensor on the device of q."""
+    if dev.type != "cuda":
+        raise TypeError(f"inputs must be CUDA (HIP) tensors, got device {dev}")
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _out_dtype(dtype: torch.dtype, name: str = "out") -> int:
+    if dtype == torch.bfloat16:
+        return SEER_BF16
+    if dtype == torch.float32:
+        return SEER_F32
+    raise TypeError(f"{name} must be bfloat16 or float32, got {dtype}")
+
+
+def _check_out(out, lse, out_dtype, out_shape, lse_shape) -> int:
+    """A caller-supplied out / lse must match the problem exactly; returns the C dtype of out."""
+    if out is not None:
+        if not isinstance(out, torch.Tensor):
+            raise TypeError(f"out must be a torch.Tensor, got {type(out).__name__}")
+        dt = _out_dtype(out.dtype)
+        _need(out, "out", out.dtype, out_shape)
+    else:
+        dt = _out_dtype(out_dtype, "out_dtype")
+    _opt(lse, "lse", torch.float32, lse_shape)
+    return dt
+
+
+def _dims(q, k, v, rank: int):
+    """q [.., Hq, S, D] with k (and v) [.., Hkv, S, D] (rank 4: batch first;
+    rank 3: packed heads-first), Hq a positive multiple of Hkv."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{n} must be a torch.Tensor, got {type(t).__name__}")
+        if t.dim() != rank:
+            raise ValueError(f"{n} must be {rank}-D, got shape {tuple(t.shape)}")
+    hq, hkv = q.shape[-3], k.shape[-3]
+    if hkv < 1 or hq % hkv != 0:
+        raise ValueError(f"heads of q ({hq}) must be a positive multiple of the heads of k ({hkv})")
+    kv_shape = tuple(q.shape[:-3]) + (hkv,) + tuple(q.shape[-2:])
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, kv_shape)
+    _opt(v, "v", torch.bfloat16, kv_shape)
+    return tuple(q.shape), hkv
+
+
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    """The caller's workspace if it is large enough, else a new one."""
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor")
+        if workspace.device != device:
+            raise ValueError(f"workspace is on {workspace.device}, expected {device}")
     if nbytes == 0:
         return workspace
     if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
@@ -170,6 +237,32 @@ def nblocks(seq_len: int) -> int:
 
 
 # ---------------------------------------------------------------------------
+def _mask_args(mode: str, topk, heads_q: int):
+    if mode not in ("topk", "threshold"):
+        raise ValueError(f"mode must be 'threshold' or 'topk', got {mode!r}")
+    m = SEER_MASK_TOPK if mode == "topk" else SEER_MASK_THRESHOLD
+    per_head, k_uniform = None, 0
+    if m == SEER_MASK_TOPK:
+        if topk is None:
+            raise ValueError("topk mode needs topk")
+        if isinstance(topk, int):
+            k_uniform = topk
+        else:
+            if len(topk) != heads_q:
+                raise ValueError(f"per-head topk needs {heads_q} values")
+            per_head = (ctypes.c_int32 * len(topk))(*[int(x) for x in topk])
+    return m, k_uniform, per_head
+
+
+def _gate_weights(w_q, w_k, heads_q, heads_kv, head_dim, wk_per_kv_head):
+    if not isinstance(w_q, torch.Tensor) or w_q.dim() != 3:
+        raise ValueError("w_q must be a 3-D tensor [Hq, D, Dg]")
+    Dg = w_q.shape[-1]
+    _need(w_q, "w_q", torch.float32, (heads_q, head_dim, Dg))
+    _need(w_k, "w_k", torch.float32, (heads_kv if wk_per_kv_head else heads_q, 3 * head_dim, Dg))
+    return Dg
+
+
 def seer_gate_fwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor, *,
                   mode: str = "threshold", threshold: float = 5e-4,
                   topk: Union[int, Sequence[int], None] = None, wk_per_kv_head: bool = False,
@@ -181,36 +274,21 @@ def seer_gate_fwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torc
     rope_theta > 0 turns on the gate's block-level RoPE (q and k are then the
     model's pre-RoPE Q and K; rope_theta is the model's RoPE base)."""
     lib = load_library()
-    _need(q, "q", torch.bfloat16)
-    _need(k, "k", torch.bfloat16)
-    _need(w_q, "w_q", torch.float32)
-    _need(w_k, "w_k", torch.float32)
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
-    Dg = w_q.shape[-1]
+    (B, Hq, S, D), Hkv = _dims(q, k, None, 4)
+    Dg = _gate_weights(w_q, w_k, Hq, Hkv, D, wk_per_kv_head)
     nb = nblocks(S)
-    shape = make_shape(B, Hq, Hkv, S, D)
+    _opt(block_mask, "block_mask", torch.uint8, (B, Hq, nb, nb))
+    _opt(scores, "scores", torch.float32, (B, Hq, nb, nb))
+    m, k_uniform, per_head = _mask_args(mode, topk, Hq)
     dev = q.device
+    _devices(dev, k=k, w_q=w_q, w_k=w_k, block_mask=block_mask, scores=scores)
+    shape = make_shape(B, Hq, Hkv, S, D)
     if block_mask is None:
         block_mask = torch.empty((B, Hq, nb, nb), dtype=torch.uint8, device=dev)
     if want_scores and scores is None:
         scores = torch.empty((B, Hq, nb, nb), dtype=torch.float32, device=dev)
     if not want_scores:
         scores = None
-    m = SEER_MASK_TOPK if mode == "topk" else SEER_MASK_THRESHOLD
-    if mode not in ("topk", "threshold"):
-        raise ValueError(f"mode must be 'threshold' or 'topk', got {mode!r}")
-    per_head = None
-    k_uniform = 0
-    if m == SEER_MASK_TOPK:
-        if topk is None:
-            raise ValueError("topk mode needs topk")
-        if isinstance(topk, int):
-            k_uniform = topk
-        else:
-            per_head = (ctypes.c_int32 * len(topk))(*[int(x) for x in topk])
-            if len(topk) != Hq:
-                raise ValueError(f"per-head topk needs {Hq} values")
     nbytes = lib.seer_gate_workspace_size(ctypes.byref(shape), Dg, int(wk_per_kv_head), int(scores is not None))
     workspace = _workspace(nbytes, dev, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -228,24 +306,17 @@ def seer_block_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
                                workspace: Optional[torch.Tensor] = None):
     """Causal GQA block-sparse attention (block_mask=None: dense causal). Returns (out, lse or None)."""
     lib = load_library()
-    _need(q, "q", torch.bfloat16)
-    _need(k, "k", torch.bfloat16)
-    _need(v, "v", torch.bfloat16)
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
-    shape = make_shape(B, Hq, Hkv, S, D)
+    (B, Hq, S, D), Hkv = _dims(q, k, v, 4)
+    nb = nblocks(S)
+    _opt(block_mask, "block_mask", torch.uint8, (B, Hq, nb, nb))
+    dt = _check_out(out, lse, out_dtype, (B, Hq, S, D), (B, Hq, S))
     dev = q.device
-    if block_mask is not None:
-        _need(block_mask, "block_mask", torch.uint8)
-        if tuple(block_mask.shape) != (B, Hq, nblocks(S), nblocks(S)):
-            raise ValueError(f"block_mask must be {(B, Hq, nblocks(S), nblocks(S))}, got {tuple(block_mask.shape)}")
+    _devices(dev, k=k, v=v, block_mask=block_mask, out=out, lse=lse)
+    shape = make_shape(B, Hq, Hkv, S, D)
     if out is None:
         out = torch.empty((B, Hq, S, D), dtype=out_dtype, device=dev)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
-    dt = SEER_BF16 if out.dtype == torch.bfloat16 else SEER_F32
-    if out.dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("out must be bfloat16 or float32")
     ws_bytes = 0
     if block_mask is not None:
         workspace = _workspace(lib.seer_attn_workspace_size(ctypes.byref(shape)), dev, workspace)
@@ -263,44 +334,24 @@ def seer_attn_maxpool_gt(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
                          gt: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Dense causal attention plus the 2D-maxpooled map. Returns (out, lse or None, gt)."""
     lib = load_library()
-    _need(q, "q", torch.bfloat16)
-    _need(k, "k", torch.bfloat16)
-    _need(v, "v", torch.bfloat16)
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
+    (B, Hq, S, D), Hkv = _dims(q, k, v, 4)
     nb = nblocks(S)
-    shape = make_shape(B, Hq, Hkv, S, D)
+    dt = _check_out(out, lse, out_dtype, (B, Hq, S, D), (B, Hq, S))
+    _opt(gt, "gt", torch.float32, (B, Hq, nb, nb))
     dev = q.device
+    _devices(dev, k=k, v=v, out=out, lse=lse, gt=gt)
+    shape = make_shape(B, Hq, Hkv, S, D)
     if out is None:
         out = torch.empty((B, Hq, S, D), dtype=out_dtype, device=dev)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
     if gt is None:
         gt = torch.empty((B, Hq, nb, nb), dtype=torch.float32, device=dev)
-    dt = SEER_BF16 if out.dtype == torch.bfloat16 else SEER_F32
-    nbytes = lib.seer_gt_workspace_size(ctypes.byref(shape))
-    workspace = _workspace(nbytes, dev, workspace)
+    workspace = _workspace(lib.seer_gt_workspace_size(ctypes.byref(shape)), dev, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.seer_attn_maxpool_gt(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(out), dt, _ptr(lse),
                                     _ptr(gt), _ptr(workspace), ws_bytes, _stream(dev)))
     return out, lse, gt
-
-
-def _topk_args(mode: str, topk, heads_q: int):
-    if mode not in ("topk", "threshold"):
-        raise ValueError(f"mode must be 'threshold' or 'topk', got {mode!r}")
-    m = SEER_MASK_TOPK if mode == "topk" else SEER_MASK_THRESHOLD
-    per_head, k_uniform = None, 0
-    if m == SEER_MASK_TOPK:
-        if topk is None:
-            raise ValueError("topk mode needs topk")
-        if isinstance(topk, int):
-            k_uniform = topk
-        else:
-            if len(topk) != heads_q:
-                raise ValueError(f"per-head topk needs {heads_q} values")
-            per_head = (ctypes.c_int32 * len(topk))(*[int(x) for x in topk])
-    return m, k_uniform, per_head
 
 
 def seer_decode_compress_k(k_cache: torch.Tensor, w_k: torch.Tensor, heads_q: int, *, wk_per_kv_head: bool = False,
@@ -309,17 +360,26 @@ def seer_decode_compress_k(k_cache: torch.Tensor, w_k: torch.Tensor, heads_q: in
     """(Re)compute the compressed K cache of blocks >= block_begin. Returns kcomp
     [B, Hwk, capacity_blocks, D] fp32."""
     lib = load_library()
-    _need(k_cache, "k_cache", torch.bfloat16)
-    _need(w_k, "w_k", torch.float32)
+    if not isinstance(k_cache, torch.Tensor) or k_cache.dim() != 4:
+        raise ValueError("k_cache must be a 4-D tensor [B, Hkv, S, D]")
     B, Hkv, S, D = k_cache.shape
+    _need(k_cache, "k_cache", torch.bfloat16)
+    if heads_q < 1 or heads_q % Hkv != 0:
+        raise ValueError(f"heads_q ({heads_q}) must be a positive multiple of the cache's {Hkv} heads")
     nb = nblocks(S)
     hwk = Hkv if wk_per_kv_head else heads_q
+    _need(w_k, "w_k", torch.float32, (hwk, 3 * D, D))
+    if kcomp is not None:
+        if not isinstance(kcomp, torch.Tensor) or kcomp.dim() != 4:
+            raise ValueError("kcomp must be a 4-D tensor [B, Hwk, capacity_blocks, D]")
+        _need(kcomp, "kcomp", torch.float32, (B, hwk, kcomp.shape[2], D))
+    dev = k_cache.device
+    _devices(dev, w_k=w_k, kcomp=kcomp)
     if kcomp is None:
-        kcomp = torch.empty((B, hwk, capacity_blocks or nb, D), dtype=torch.float32, device=k_cache.device)
-    _need(kcomp, "kcomp", torch.float32)
+        kcomp = torch.empty((B, hwk, capacity_blocks or nb, D), dtype=torch.float32, device=dev)
     shape = make_shape(B, heads_q, Hkv, S, D)
     _check(lib.seer_decode_compress_k(ctypes.byref(shape), int(wk_per_kv_head), _ptr(k_cache), _ptr(w_k),
-                                      int(block_begin), _ptr(kcomp), int(kcomp.shape[2]), _stream(k_cache.device)))
+                                      int(block_begin), _ptr(kcomp), int(kcomp.shape[2]), _stream(dev)))
     return kcomp
 
 
@@ -329,16 +389,26 @@ def seer_decode_gate_fwd(q: torch.Tensor, kcomp: torch.Tensor, seq_len: int, hea
                          scores: Optional[torch.Tensor] = None, block_mask: Optional[torch.Tensor] = None):
     """Decode gate for one query per head. Returns (block_mask [B,Hq,nb] uint8, scores or None)."""
     lib = load_library()
-    _need(q, "q", torch.bfloat16)
-    _need(kcomp, "kcomp", torch.float32)
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a 3-D tensor [B, Hq, D]")
     B, Hq, D = q.shape
+    _need(q, "q", torch.bfloat16)
+    if heads_kv < 1 or Hq % heads_kv != 0:
+        raise ValueError(f"heads of q ({Hq}) must be a positive multiple of heads_kv ({heads_kv})")
     nb = nblocks(seq_len)
+    if not isinstance(kcomp, torch.Tensor) or kcomp.dim() != 4:
+        raise ValueError("kcomp must be a 4-D tensor [B, Hwk, capacity_blocks, D]")
+    hwk = heads_kv if wk_per_kv_head else Hq
+    _need(kcomp, "kcomp", torch.float32, (B, hwk, kcomp.shape[2], D))
+    _opt(block_mask, "block_mask", torch.uint8, (B, Hq, nb))
+    _opt(scores, "scores", torch.float32, (B, Hq, nb))
+    m, k_uniform, per_head = _mask_args(mode, topk, Hq)
     dev = q.device
+    _devices(dev, kcomp=kcomp, block_mask=block_mask, scores=scores)
     if block_mask is None:
         block_mask = torch.empty((B, Hq, nb), dtype=torch.uint8, device=dev)
     if scores is None:
         scores = torch.empty((B, Hq, nb), dtype=torch.float32, device=dev)
-    m, k_uniform, per_head = _topk_args(mode, topk, Hq)
     shape = make_shape(B, Hq, heads_kv, seq_len, D)
     _check(lib.seer_decode_gate_fwd(ctypes.byref(shape), int(wk_per_kv_head), _ptr(q), _ptr(kcomp),
                                     int(kcomp.shape[2]), m, float(threshold), int(k_uniform), per_head, _ptr(scores),
@@ -354,24 +424,30 @@ def seer_decode_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     """Decode attention of one query per head over the active blocks of the
     cache. Returns (out [B,Hq,D], lse or None, gt [B,Hq,nb] or None)."""
     lib = load_library()
-    _need(q, "q", torch.bfloat16)
-    _need(k_cache, "k_cache", torch.bfloat16)
-    _need(v_cache, "v_cache", torch.bfloat16)
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a 3-D tensor [B, Hq, D]")
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{n} must be a 4-D tensor [B, Hkv, S, D]")
     B, Hq, D = q.shape
     Hkv, S = k_cache.shape[1], k_cache.shape[2]
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError(f"heads of q ({Hq}) must be a positive multiple of the cache's {Hkv} heads")
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, S, D))
+    _need(v_cache, "v_cache", torch.bfloat16, (B, Hkv, S, D))
     nb = nblocks(S)
+    _opt(block_mask, "block_mask", torch.uint8, (B, Hq, nb))
+    dt = _check_out(out, lse, out_dtype, (B, Hq, D), (B, Hq))
+    _opt(gt, "gt", torch.float32, (B, Hq, nb))
     dev = q.device
-    if block_mask is not None:
-        _need(block_mask, "block_mask", torch.uint8)
-        if tuple(block_mask.shape) != (B, Hq, nb):
-            raise ValueError(f"block_mask must be {(B, Hq, nb)}, got {tuple(block_mask.shape)}")
+    _devices(dev, k_cache=k_cache, v_cache=v_cache, block_mask=block_mask, out=out, lse=lse, gt=gt)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=out_dtype, device=dev)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     if want_gt and gt is None:
         gt = torch.empty((B, Hq, nb), dtype=torch.float32, device=dev)
-    dt = SEER_BF16 if out.dtype == torch.bfloat16 else SEER_F32
     shape = make_shape(B, Hq, Hkv, S, D)
     workspace = _workspace(lib.seer_decode_attn_workspace_size(ctypes.byref(shape)), dev, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -398,6 +474,14 @@ def varlen_map_offsets(cu_seqlens: Sequence[int], heads_q: int):
     return offs, n
 
 
+def _varlen_dims(q, k, v, cu_seqlens):
+    (Hq, T, D), Hkv = _dims(q, k, v, 3)
+    cu = [int(x) for x in cu_seqlens]
+    if len(cu) < 1 or cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu[:-1], cu[1:])):
+        raise ValueError(f"cu_seqlens must rise from 0 to the packed length {T}")
+    return Hq, Hkv, T, D, cu, varlen_map_offsets(cu, Hq)[1]
+
+
 def seer_gate_varlen_fwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
                          cu_seqlens: Sequence[int], *, mode: str = "threshold", threshold: float = 5e-4,
                          topk: Union[int, Sequence[int], None] = None, wk_per_kv_head: bool = False,
@@ -406,25 +490,20 @@ def seer_gate_varlen_fwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_
     """Gate of a packed batch (q [Hq,T,D], k [Hkv,T,D]). Returns (block_mask, scores or None),
     each sequence's [Hq, nb_i, nb_i] map concatenated (see varlen_map_offsets)."""
     lib = load_library()
-    _need(q, "q", torch.bfloat16)
-    _need(k, "k", torch.bfloat16)
-    _need(w_q, "w_q", torch.float32)
-    _need(w_k, "w_k", torch.float32)
-    Hq, T, D = q.shape
-    Hkv = k.shape[0]
-    Dg = w_q.shape[-1]
-    if int(cu_seqlens[-1]) != T:
-        raise ValueError(f"cu_seqlens[-1] ({cu_seqlens[-1]}) must equal the packed length {T}")
-    vl = make_varlen(cu_seqlens, Hq, Hkv, D)
+    Hq, Hkv, T, D, cu, n_map = _varlen_dims(q, k, None, cu_seqlens)
+    Dg = _gate_weights(w_q, w_k, Hq, Hkv, D, wk_per_kv_head)
+    _opt(block_mask, "block_mask", torch.uint8, (n_map,))
+    _opt(scores, "scores", torch.float32, (n_map,))
+    m, k_uniform, per_head = _mask_args(mode, topk, Hq)
     dev = q.device
-    n_map = lib.seer_varlen_map_elements(ctypes.byref(vl))
+    _devices(dev, k=k, w_q=w_q, w_k=w_k, block_mask=block_mask, scores=scores)
+    vl = make_varlen(cu, Hq, Hkv, D)
     if block_mask is None:
         block_mask = torch.empty(n_map, dtype=torch.uint8, device=dev)
     if want_scores and scores is None:
         scores = torch.empty(n_map, dtype=torch.float32, device=dev)
     if not want_scores:
         scores = None
-    m, k_uniform, per_head = _topk_args(mode, topk, Hq)
     nbytes = lib.seer_gate_varlen_workspace_size(ctypes.byref(vl), Dg, int(wk_per_kv_head), int(scores is not None))
     workspace = _workspace(nbytes, dev, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -442,24 +521,16 @@ def seer_block_sparse_attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch
     """Causal GQA block-sparse attention of a packed batch (block_mask None: dense).
     Returns (out [Hq,T,D], lse [Hq,T] or None)."""
     lib = load_library()
-    _need(q, "q", torch.bfloat16)
-    _need(k, "k", torch.bfloat16)
-    _need(v, "v", torch.bfloat16)
-    Hq, T, D = q.shape
-    Hkv = k.shape[0]
-    if int(cu_seqlens[-1]) != T:
-        raise ValueError(f"cu_seqlens[-1] ({cu_seqlens[-1]}) must equal the packed length {T}")
-    vl = make_varlen(cu_seqlens, Hq, Hkv, D)
+    Hq, Hkv, T, D, cu, n_map = _varlen_dims(q, k, v, cu_seqlens)
+    _opt(block_mask, "block_mask", torch.uint8, (n_map,))
+    dt = _check_out(out, lse, out_dtype, (Hq, T, D), (Hq, T))
     dev = q.device
-    if block_mask is not None:
-        _need(block_mask, "block_mask", torch.uint8)
-        if block_mask.numel() < lib.seer_varlen_map_elements(ctypes.byref(vl)):
-            raise ValueError("block_mask is smaller than the concatenated per-sequence maps")
+    _devices(dev, k=k, v=v, block_mask=block_mask, out=out, lse=lse)
+    vl = make_varlen(cu, Hq, Hkv, D)
     if out is None:
         out = torch.empty((Hq, T, D), dtype=out_dtype, device=dev)
     if want_lse and lse is None:
         lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
-    dt = SEER_BF16 if out.dtype == torch.bfloat16 else SEER_F32
     ws_need = lib.seer_attn_varlen_workspace_size(ctypes.byref(vl)) if block_mask is not None else 0
     workspace = _workspace(ws_need, dev, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -474,22 +545,18 @@ def seer_attn_maxpool_gt_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
                                 gt: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Dense attention of a packed batch plus each sequence's 2D-maxpooled map. Returns (out, lse or None, gt)."""
     lib = load_library()
-    _need(q, "q", torch.bfloat16)
-    _need(k, "k", torch.bfloat16)
-    _need(v, "v", torch.bfloat16)
-    Hq, T, D = q.shape
-    Hkv = k.shape[0]
-    if int(cu_seqlens[-1]) != T:
-        raise ValueError(f"cu_seqlens[-1] ({cu_seqlens[-1]}) must equal the packed length {T}")
-    vl = make_varlen(cu_seqlens, Hq, Hkv, D)
+    Hq, Hkv, T, D, cu, n_map = _varlen_dims(q, k, v, cu_seqlens)
+    dt = _check_out(out, lse, out_dtype, (Hq, T, D), (Hq, T))
+    _opt(gt, "gt", torch.float32, (n_map,))
     dev = q.device
+    _devices(dev, k=k, v=v, out=out, lse=lse, gt=gt)
+    vl = make_varlen(cu, Hq, Hkv, D)
     if out is None:
         out = torch.empty((Hq, T, D), dtype=out_dtype, device=dev)
     if want_lse and lse is None:
         lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
     if gt is None:
-        gt = torch.empty(lib.seer_varlen_map_elements(ctypes.byref(vl)), dtype=torch.float32, device=dev)
-    dt = SEER_BF16 if out.dtype == torch.bfloat16 else SEER_F32
+        gt = torch.empty(n_map, dtype=torch.float32, device=dev)
     workspace = _workspace(lib.seer_gt_varlen_workspace_size(ctypes.byref(vl)), dev, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.seer_attn_maxpool_gt_varlen(ctypes.byref(vl), _ptr(q), _ptr(k), _ptr(v), _ptr(out), dt, _ptr(lse),
@@ -509,19 +576,16 @@ def seer_gate_distill_bwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w
     """One distillation step of the gate: KL(row-normalized gt || score) averaged
     over query-block rows, and its gradients. Returns (loss [1], grad_wq, grad_wk)."""
     lib = load_library()
-    _need(q, "q", torch.bfloat16)
-    _need(k, "k", torch.bfloat16)
-    _need(w_q, "w_q", torch.float32)
-    _need(w_k, "w_k", torch.float32)
-    _need(gt, "gt", torch.float32)
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
-    Dg = w_q.shape[-1]
+    (B, Hq, S, D), Hkv = _dims(q, k, None, 4)
+    Dg = _gate_weights(w_q, w_k, Hq, Hkv, D, wk_per_kv_head)
     nb = nblocks(S)
-    if tuple(gt.shape) != (B, Hq, nb, nb):
-        raise ValueError(f"gt must be {(B, Hq, nb, nb)}, got {tuple(gt.shape)}")
-    shape = make_shape(B, Hq, Hkv, S, D)
+    _need(gt, "gt", torch.float32, (B, Hq, nb, nb))
+    _opt(loss, "loss", torch.float32, (1,))
+    _opt(grad_wq, "grad_wq", torch.float32, tuple(w_q.shape))
+    _opt(grad_wk, "grad_wk", torch.float32, tuple(w_k.shape))
     dev = q.device
+    _devices(dev, k=k, w_q=w_q, w_k=w_k, gt=gt, loss=loss, grad_wq=grad_wq, grad_wk=grad_wk)
+    shape = make_shape(B, Hq, Hkv, S, D)
     if loss is None:
         loss = torch.empty(1, dtype=torch.float32, device=dev)
     if grad_wq is None:
