@@ -46,8 +46,6 @@
 //    kernel merges the chunks of each row (split-KV); each item walks its
 //    tiles in a circular order phased by its dispatch slot, so the items
 //    resident on an XCD read neighbouring key blocks at the same time.
-#include <stdlib.h>
-
 #include "seer_device.h"
 #include "seer_internal.h"
 #include "tile_ops.h"
@@ -534,8 +532,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
 // that spans several chunks writes a bf16 partial output (normalized by its
 // own sum) and its log2-sum-exp; attn_xcd_combine_kernel merges them. Rows
 // inside the first chunk are one item and are written directly.
-constexpr int kXcdMaxChunk = 128;        // key blocks per chunk at most (two 64-bit flag words)
 constexpr int kXcdDefaultChunk = 128;    // 4 MiB of K/V at D = 128: one XCD's L2
+static_assert(kXcdDefaultChunk <= 128, "an item's flags are two 64-bit ballot words");
 constexpr int kXcdMinBlocks = 1280;      // rows of 80k tokens and more
 constexpr int kXcdSlots = 128;           // resident workgroups per XCD: 32 CUs x 4
 
@@ -1055,22 +1053,10 @@ hipError_t launch_d(const AttnArgs& a, int mode, hipStream_t st) {
 }  // namespace
 
 namespace {
-// Key blocks per chunk of the other block-sparse path. Up to 1024 blocks (64k
+// Key blocks per chunk of the other block-sparse path: up to 1024 blocks (64k
 // tokens) a row is one item; longer rows are cut into chunks of 512 blocks,
-// which the XCDs sweep together. SEER_ATTN_CHUNK overrides the chunk (rounded
-// to a multiple of 16, at most the on-chip list capacity).
-int sweep_chunk_blocks(int nb) {
-  static const int forced = [] {
-    const char* v = getenv("SEER_ATTN_CHUNK");
-    if (v == nullptr) return 0;
-    int x = atoi(v);
-    if (x < 16) x = 16;
-    if (x > kListCap) x = kListCap;
-    return x / 16 * 16;
-  }();
-  if (forced) return forced;
-  return nb > 1024 ? 512 : kListCap;
-}
+// which the XCDs sweep together.
+int sweep_chunk_blocks(int nb) { return nb > 1024 ? 512 : kListCap; }
 }  // namespace
 
 // The XCD-owned path takes rows of at least kXcdMinBlocks blocks when there
@@ -1078,28 +1064,13 @@ int sweep_chunk_blocks(int nb) {
 // measured 1-3% faster than the other path from 80k tokens up, slower at 64k
 // and below, where fewer K/V re-reads miss the L2); otherwise the rows go to
 // attn_fwd_kernel (cut into chunks of 512 blocks above 1024 blocks, with the
-// circular sweep). SEER_ATTN_XCD=0 / 1 forces the choice (1: whenever rows
-// reach a second chunk), SEER_XCD_CHUNK sets its chunk (16..128) and
-// SEER_ATTN_ROTATE=0 turns the sweep off.
+// circular sweep).
 SparsePlan sparse_plan(int B, int Hkv, int group, int nb, int D) {
-  static const int forced_xcd = [] {
-    const char* v = getenv("SEER_ATTN_XCD");
-    return v == nullptr ? -1 : (atoi(v) != 0);
-  }();
-  static const int forced_rotate = [] {
-    const char* v = getenv("SEER_ATTN_ROTATE");
-    return v == nullptr ? -1 : (atoi(v) != 0);
-  }();
-  static const int xcd_chunk = [] {
-    const char* v = getenv("SEER_XCD_CHUNK");
-    int x = v == nullptr ? kXcdDefaultChunk : atoi(v);
-    return x < 16 ? 16 : (x > kXcdMaxChunk ? kXcdMaxChunk : x);
-  }();
   SparsePlan pl{};
-  const int C = xcd_chunk;
+  const int C = kXcdDefaultChunk;
   const long long nch = (nb + C - 1) / C;
   const long long jobs = static_cast<long long>(B) * Hkv * nch;
-  pl.xcd = forced_xcd >= 0 ? (forced_xcd && nb > C) : (nb >= kXcdMinBlocks && jobs >= 64);
+  pl.xcd = nb >= kXcdMinBlocks && jobs >= 64;
   if (pl.xcd) {
     pl.chunk = C;
     pl.nchunk = static_cast<int>(nch);
@@ -1111,7 +1082,7 @@ SparsePlan sparse_plan(int B, int Hkv, int group, int nb, int D) {
   }
   pl.chunk = sweep_chunk_blocks(nb);
   pl.nchunk = (nb + pl.chunk - 1) / pl.chunk;
-  pl.rotate = forced_rotate >= 0 ? forced_rotate : 1;
+  pl.rotate = 1;
   const long long nc = pl.nchunk;
   pl.items_per_group = static_cast<long long>(group) * (nc * nb - static_cast<long long>(pl.chunk) * nc * (nc - 1) / 2);
   if (nb > pl.chunk) {

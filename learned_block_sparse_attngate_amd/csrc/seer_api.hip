@@ -83,16 +83,8 @@ seer_status check_device() {
 // Workgroup order of the attention kernels (see attn_kernels.hip). Measured on
 // MI355X at 32k and 128k tokens: KV-group-major order keeps one group's K/V
 // in the Infinity Cache; for block-sparse rows, head-major inside the group
-// additionally keeps rows of similar density together. SEER_ATTN_SCHED=0..3
-// overrides the choice (results are identical, only the order changes).
-int attn_sched(int mode) {
-  static int env = [] {
-    const char* v = getenv("SEER_ATTN_SCHED");
-    return v ? atoi(v) : -1;
-  }();
-  if (env >= 0 && env <= 3) return env;
-  return mode == 0 ? 3 : 2;
-}
+// additionally keeps rows of similar density together.
+int attn_sched(int mode) { return mode == 0 ? 3 : 2; }
 
 seer::AttnArgs attn_args(const seer_shape* s, const void* q, const void* k, const void* v, int mode) {
   seer::AttnArgs a{};
