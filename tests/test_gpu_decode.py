@@ -160,8 +160,11 @@ def test_decode_dense_and_gt_matches_oracle(shape):
     check_close(host(out), o_ref, "dense O")
     check_lse(host(lse), l_ref, "dense LSE")
     err = np.abs(host(gt) - gt_ref)
-    say(f"  gt max-abs {err.max():.3e}, max rel on entries > 1e-6 {(err / np.maximum(gt_ref, 1e-6)).max():.3e}")
-    assert err.max() <= 1e-4
+    big = gt_ref > 1e-6
+    rel = err[big] / gt_ref[big]
+    say(f"  gt max-abs {err.max():.3e}, max rel on entries > 1e-6 {rel.max():.3e}")
+    assert err.max() <= 1e-6            # the runs show ~1e-8
+    assert rel.max() <= 1e-4
     assert torch.equal(out, out1)                      # an all-ones mask is the dense path
 
 

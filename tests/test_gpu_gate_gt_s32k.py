@@ -1,0 +1,151 @@
+"""The full gate + ground-truth path at 32k tokens (32 query / 8 KV heads,
+head dim 128, gate dim 128, planted hot key blocks, random-init gate weights),
+against the fp64 oracle.
+
+The gate follows "SeerAttention: Learning Intrinsic Sparse Attention in Your
+LLMs", section 3.4 (AttnGate score equation; "Inference Procedure", Method 2:
+a threshold on the block scores, 5e-4 here); the map follows the same
+section's "Training Procedure" (the 2D-maxpooled attention map the gate is
+distilled on, [1, 32, 512, 512] at this size).
+
+With random weights the gate is nearly flat (every causal score is about
+1/(i+1) >= 1/512 > 5e-4), so the mask at T = 5e-4 is close to dense; the
+thresholds 1.5e-3, 2e-3 and 3e-3 cut through the rows and give non-trivial
+masks on the same inputs.
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import MASK_BAND, check_close, check_lse, dev_bf16, dev_f32, host, say, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+WORKLOAD = "gate_gt_s32k"
+THRESHOLDS = (5e-4, 1.5e-3, 2e-3, 3e-3)
+GT_MAX_ABS = 1e-6          # fp32 statistics: the runs show ~1e-7
+GT_MAX_REL = 1e-4          # on entries > 1e-6; the runs show ~1e-6
+
+
+def _seer():
+    import learned_block_sparse_attngate_amd as seer
+    seer.load_library()
+    return seer
+
+
+_CACHE = {}
+
+
+def _inputs():
+    if not _CACHE:
+        w = synth.WORKLOADS[WORKLOAD]
+        shape = w["shape"]
+        q, k, v, planted = synth.gen_planted_qk(shape, w["seed"])
+        wq, wk = synth.gen_gate_weights(shape.heads_q, shape.head_dim, w["gate_dim"], w["seed"] + 100)
+        t0 = time.perf_counter()
+        sc_ref = oracle.gate_scores(q, k, wq, wk)
+        say(f"  oracle gate scores: {time.perf_counter() - t0:.1f} s")
+        _CACHE.update(shape=shape, q=q, k=k, v=v, wq=wq, wk=wk, sc_ref=sc_ref, planted=planted,
+                      dq=dev_bf16(q), dk=dev_bf16(k), dv=dev_bf16(v), dwq=dev_f32(wq), dwk=dev_f32(wk))
+    return _CACHE
+
+
+def _gate(T):
+    c = _inputs()
+    mask, scores = _seer().seer_gate_fwd(c["dq"], c["dk"], c["dwq"], c["dwk"], mode="threshold", threshold=T)
+    torch.cuda.synchronize()
+    return mask.cpu().numpy(), host(scores)
+
+
+def test_gate_scores_and_threshold_masks():
+    """Full [1, 32, 512, 512] score map within 1e-5 of the oracle; masks at
+    every threshold bit-exact outside the 1e-6 band around T; GPU masks nest
+    as T rises (a larger threshold keeps a subset of the blocks)."""
+    say(f"[{WORKLOAD} gate] thresholds {THRESHOLDS}")
+    c = _inputs()
+    sc_ref = c["sc_ref"]
+    nb = c["shape"].nb
+    causal = np.tril(np.ones((nb, nb), dtype=bool))
+    prev = None
+    for T in THRESHOLDS:
+        m, s = _gate(T)
+        err = np.abs(s - sc_ref)
+        say(f"  T={T:.1e}: scores max-abs {err.max():.3e}")
+        assert err.max() < 1e-5
+        want = oracle.threshold_mask(sc_ref, T)
+        band = np.abs(sc_ref - T) <= MASK_BAND
+        diff = (m != want) & ~band
+        active = int((m.astype(bool) & causal).sum())
+        total = int(causal.sum()) * c["shape"].heads_q
+        say(f"  T={T:.1e}: {active} of {total} causal blocks active (sparsity {1 - active / total:.4f}), "
+            f"{int(band.sum())} in the band, {int(diff.sum())} mismatches")
+        assert not diff.any()
+        assert not (m[..., ~causal] != 0).any(), "mask set above the diagonal"
+        if prev is not None:
+            assert not (m.astype(bool) & ~prev.astype(bool)).any(), "masks do not nest as T rises"
+        prev = m
+
+
+@pytest.mark.parametrize("T", [5e-4, 3e-3], ids=["T5e-4", "T3e-3"])
+def test_gate_mask_feeds_sparse_attention(T):
+    """The gate's own mask drives the block-sparse attention at 32k; sampled
+    query blocks of every head against the oracle on that mask."""
+    seer = _seer()
+    c = _inputs()
+    shape = c["shape"]
+    say(f"[{WORKLOAD} gate -> sparse attention] T={T}")
+    mask, _ = seer.seer_gate_fwd(c["dq"], c["dk"], c["dwq"], c["dwk"], mode="threshold", threshold=T,
+                                 want_scores=False)
+    out, lse = seer.seer_block_sparse_attn_fwd(c["dq"], c["dk"], c["dv"], mask, out_dtype=torch.bfloat16,
+                                               want_lse=True)
+    torch.cuda.synchronize()
+    m = mask.cpu().numpy()
+    rows = sample_rows(1, shape.heads_q, shape.nb, 2, 77)
+    t0 = time.perf_counter()
+    o_ref, l_ref = oracle.attention_rows(c["q"], c["k"], c["v"], m, rows)
+    say(f"  oracle on {len(rows)} rows: {time.perf_counter() - t0:.1f} s")
+    o_gpu, l_gpu = host(out), host(lse)
+    got_o = np.concatenate([o_gpu[b, h, 64 * i:64 * i + 64] for (b, h, i) in rows])
+    got_l = np.concatenate([l_gpu[b, h, 64 * i:64 * i + 64] for (b, h, i) in rows])
+    check_close(got_o, np.concatenate(o_ref), "sampled O")
+    check_lse(got_l, np.concatenate(l_ref), "sampled LSE")
+
+
+def test_maxpool_gt_sampled_rows():
+    """Dense attention + 2D-maxpooled map at 32k: sampled rows of the map
+    (blocks 0, 1, nb/2, nb-1 and random ones, every head) within max-abs 1e-6
+    and relative 1e-4 of the oracle, zeros above the diagonal, gt[h, 0, 0] = 1,
+    and the same rows of O / LSE within the attention bounds."""
+    seer = _seer()
+    c = _inputs()
+    shape = c["shape"]
+    nb = shape.nb
+    say(f"[{WORKLOAD} maxpool gt] shape={shape}")
+    out, lse, gt = seer.seer_attn_maxpool_gt(c["dq"], c["dk"], c["dv"], out_dtype=torch.bfloat16, want_lse=True)
+    torch.cuda.synchronize()
+    g = host(gt)
+    rows = sample_rows(1, shape.heads_q, nb, 3, 78)
+    t0 = time.perf_counter()
+    gt_ref = oracle.maxpool_gt_rows(c["q"], c["k"], rows)
+    say(f"  oracle on {len(rows)} map rows: {time.perf_counter() - t0:.1f} s")
+    got = np.stack([g[b, h, i] for (b, h, i) in rows])
+    want = np.stack(gt_ref)
+    err = np.abs(got - want)
+    big = want > 1e-6
+    rel = err[big] / want[big]
+    say(f"  gt rows: max-abs {err.max():.3e}, max rel on entries > 1e-6 {rel.max():.3e}")
+    assert err.max() <= GT_MAX_ABS
+    assert rel.max() <= GT_MAX_REL
+    iu = np.triu_indices(nb, 1)
+    assert np.all(g[..., iu[0], iu[1]] == 0.0)
+    assert np.abs(g[:, :, 0, 0] - 1.0).max() <= GT_MAX_ABS      # token 0 sees one key
+    o_ref, l_ref = oracle.attention_rows(c["q"], c["k"], c["v"], None, rows[::3])
+    o_gpu, l_gpu = host(out), host(lse)
+    got_o = np.concatenate([o_gpu[b, h, 64 * i:64 * i + 64] for (b, h, i) in rows[::3]])
+    got_l = np.concatenate([l_gpu[b, h, 64 * i:64 * i + 64] for (b, h, i) in rows[::3]])
+    check_close(got_o, np.concatenate(o_ref), "gt-kernel O (sampled)")
+    check_lse(got_l, np.concatenate(l_ref), "gt-kernel LSE (sampled)")

@@ -34,10 +34,11 @@ def test_gt_matches_oracle(shape, dt):
     gt_ref = oracle.maxpool_gt(q, k)
     o_ref, l_ref = oracle.attention(q, k, v, None)
     g = host(gt)
-    check_close(g, gt_ref, "gt", max_abs=1e-4, mean_abs=1e-6)
+    # fp32 row statistics: the runs show max-abs ~1e-7 and relative ~1e-6
+    check_close(g, gt_ref, "gt", max_abs=1e-6, mean_abs=1e-7)
     rel = np.abs(g - gt_ref)[gt_ref > 1e-6] / gt_ref[gt_ref > 1e-6]
     say(f"  gt max relative error on entries > 1e-6: {rel.max():.3e}")
-    assert rel.max() < 2e-2
+    assert rel.max() < 1e-4
     assert np.all(g[..., np.triu_indices(shape.nb, 1)[0], np.triu_indices(shape.nb, 1)[1]] == 0.0)
     check_close(host(out), o_ref, "gt-kernel O")
     check_lse(host(lse), l_ref, "gt-kernel LSE")
