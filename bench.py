@@ -13,6 +13,11 @@ the attention consumes is the workload's seeded one, while the gate's full
 cost is in the step. The dense causal kernel runs on the same inputs for the
 speedup. Inputs are resident in HBM before timing starts.
 
+`--workload gate_gt_s32k` runs the full gate path instead: planted Q/K at 32k,
+random-init gate weights, the gate's threshold mask (T = 5e-4) feeding the
+block-sparse attention inside the step, and the ground-truth kernel (dense
+attention + 2D-maxpooled map) timed against the dense kernel.
+
 Prints one JSON line. `value` = executed-tile FLOP of the sparse attention
 (4*64*64*D per active causal tile) / step time, in TFLOP/s.
 """
@@ -253,6 +258,13 @@ def bench_varlen(seer, torch, dev, stream, seed, reps: int = 5):
             "sparse_attention_ms": round(ms, 4), "executed_tiles": tiles, "tflops": round(tflops, 2)}
 
 
+def mask_desc(sparsity) -> str:
+    if isinstance(sparsity, tuple):
+        lo, hi, mean = sparsity
+        return f"seeded diag+sink+4 stripes+random, per-head s in [{lo},{hi}] with mean {mean}"
+    return f"seeded diag+sink+4 stripes+random, s = {sparsity} for every head"
+
+
 def topk_for_sparsity(nb: int, s: float) -> int:
     """Smallest k whose top-k causal mask has sparsity <= s."""
     total = nb * (nb + 1) // 2
@@ -286,8 +298,28 @@ def cpu_baseline(q, k, v, mask, shape, seconds: float):
         rows_done += 1
     el = time.perf_counter() - t0
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{rows_done} random (head, query-block) rows of the same workload, fp64 NumPy, "
                       f"{el:.1f} s; rate = executed-tile FLOP / time"}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name as lscpu reports it (/proc/cpuinfo if lscpu is absent)."""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:                                          # pragma: no cover
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:                                            # pragma: no cover
+        pass
+    return "unknown"
 
 
 def main():
@@ -302,11 +334,14 @@ def main():
     import learned_block_sparse_attngate_amd as seer
 
     w = synth.WORKLOADS.get(args.workload)
-    if w is None or not isinstance(w["sparsity"], (float, tuple)):
-        usable = [k for k, v in synth.WORKLOADS.items() if isinstance(v["sparsity"], (float, tuple))]
-        print(f"bench.py needs a workload with a seeded block mask, one of {usable} (got {args.workload})",
-              file=sys.stderr)
+    if w is None or not (isinstance(w["sparsity"], (float, tuple)) or w["sparsity"] == "gate"):
+        usable = [k for k, v in synth.WORKLOADS.items() if isinstance(v["sparsity"], (float, tuple))
+                  or v["sparsity"] == "gate"]
+        print(f"bench.py needs a workload with a seeded or gate-made block mask, one of {usable} "
+              f"(got {args.workload})", file=sys.stderr)
         sys.exit(2)
+    # gate-made mask: planted Q/K, random-init weights, threshold mask from the gate feeds the attention
+    gate_made = w["sparsity"] == "gate"
     seer.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -317,35 +352,37 @@ def main():
     print(f"[bench] workload {args.workload}: B={B} Hq={Hq} Hkv={Hkv} S={S} D={D}; generating inputs",
           file=sys.stderr, flush=True)
 
-    qb, kb, vb = synth.gen_qkv(shape, w["seed"])
-    minfo = synth.workload_mask(args.workload)
-    mask_np = minfo.mask
-    wq_np, wk_np = synth.gen_gate_weights(Hq, D, 128, w["seed"] + 100)
+    dg = w.get("gate_dim", 128)
+    if gate_made:
+        qb, kb, vb, _ = synth.gen_planted_qk(shape, w["seed"])
+        mask_np = None                                  # the gate's mask, read back after the warm-up
+    else:
+        qb, kb, vb = synth.gen_qkv(shape, w["seed"])
+        mask_np = synth.workload_mask(args.workload).mask
+    wq_np, wk_np = synth.gen_gate_weights(Hq, D, dg, w["seed"] + 100)
+    rope_theta = 0.0 if gate_made else args.rope_theta
 
     def to_dev_bf16(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
     q, k, v = to_dev_bf16(qb), to_dev_bf16(kb), to_dev_bf16(vb)
-    mask = torch.from_numpy(mask_np).to(dev)
     wq, wk = torch.from_numpy(wq_np).to(dev), torch.from_numpy(wk_np).to(dev)
     out = torch.empty((B, Hq, S, D), dtype=torch.bfloat16, device=dev)
     gate_mask = torch.empty((B, Hq, nb, nb), dtype=torch.uint8, device=dev)
     gate_scores = torch.empty((B, Hq, nb, nb), dtype=torch.float32, device=dev)
-    gate_ws = torch.empty(seer.gate_workspace_bytes(B, Hq, Hkv, S, D, 128), dtype=torch.uint8, device=dev)
-    k_gate = topk_for_sparsity(nb, 0.9)
-
-    tiles = int(np.count_nonzero(np.tril(np.ones((nb, nb), dtype=bool)) & mask_np.astype(bool)))
-    causal_tiles = B * Hq * nb * (nb + 1) // 2
-    flop_tile = 4.0 * 64 * 64 * D
-    sparse_flop = tiles * flop_tile
-    dense_flop = causal_tiles * flop_tile
+    gate_ws = torch.empty(seer.gate_workspace_bytes(B, Hq, Hkv, S, D, dg), dtype=torch.uint8, device=dev)
+    k_gate = None if gate_made else topk_for_sparsity(nb, 0.9)
+    mask = gate_mask if gate_made else torch.from_numpy(mask_np).to(dev)
 
     stream = torch.cuda.current_stream(dev)
 
     def gate():
-        seer.seer_gate_fwd(q, k, wq, wk, mode="topk", topk=k_gate, rope_theta=args.rope_theta,
-                           scores=gate_scores, block_mask=gate_mask,
-                           workspace=gate_ws)
+        if gate_made:
+            seer.seer_gate_fwd(q, k, wq, wk, mode="threshold", threshold=w["threshold"], scores=gate_scores,
+                               block_mask=gate_mask, workspace=gate_ws)
+        else:
+            seer.seer_gate_fwd(q, k, wq, wk, mode="topk", topk=k_gate, rope_theta=rope_theta,
+                               scores=gate_scores, block_mask=gate_mask, workspace=gate_ws)
 
     attn_ws = torch.empty(max(seer.attn_workspace_bytes(B, Hq, Hkv, S, D), 16), dtype=torch.uint8, device=dev)
 
@@ -367,6 +404,16 @@ def main():
         gate()
         attn()
     torch.cuda.synchronize()
+    if gate_made:
+        gate()
+        torch.cuda.synchronize()
+        mask_np = gate_mask.cpu().numpy()
+
+    tiles = int(np.count_nonzero(np.tril(np.ones((nb, nb), dtype=bool)) & mask_np.astype(bool)))
+    causal_tiles = B * Hq * nb * (nb + 1) // 2
+    flop_tile = 4.0 * 64 * 64 * D
+    sparse_flop = tiles * flop_tile
+    dense_flop = causal_tiles * flop_tile
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -409,18 +456,23 @@ def main():
         print("[bench] ground-truth kernel and distillation step", file=sys.stderr, flush=True)
         gt = torch.empty((B, Hq, nb, nb), dtype=torch.float32, device=dev)
         gt_ws = torch.empty(seer.gt_workspace_bytes(B, Hq, Hkv, S, D), dtype=torch.uint8, device=dev)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
         seer.seer_attn_maxpool_gt(q, k, v, out=out, gt=gt, workspace=gt_ws)
-        e1.record(stream)
         torch.cuda.synchronize()
-        gt_ms = e0.elapsed_time(e1)
+        dts = []
+        for _ in range(args.dense_reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            seer.seer_attn_maxpool_gt(q, k, v, out=out, gt=gt, workspace=gt_ws)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            dts.append(e0.elapsed_time(e1))
+        gt_ms = float(np.median(dts))
         del gt_ws
-        d_ws = torch.empty(seer.distill_workspace_bytes(B, Hq, Hkv, S, D, 128), dtype=torch.uint8, device=dev)
+        d_ws = torch.empty(seer.distill_workspace_bytes(B, Hq, Hkv, S, D, dg), dtype=torch.uint8, device=dev)
         d_out = (torch.empty(1, dtype=torch.float32, device=dev), torch.empty_like(wq), torch.empty_like(wk))
 
         def distill():
-            seer.seer_gate_distill_bwd(q, k, wq, wk, gt, rope_theta=args.rope_theta, loss=d_out[0],
+            seer.seer_gate_distill_bwd(q, k, wq, wk, gt, rope_theta=rope_theta, loss=d_out[0],
                                        grad_wq=d_out[1], grad_wk=d_out[2], workspace=d_ws)
         distill()
         torch.cuda.synchronize()
@@ -470,9 +522,13 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "heads_q": Hq, "heads_kv": Hkv, "seq_len": S,
-                   "head_dim": D, "block": 64, "mask": "seeded diag+sink+4 stripes+random, per-head s in [0.8,0.97]",
-                   "realized_sparsity": round(s_real, 5), "executed_tiles": tiles, "gate_topk": k_gate,
-                   "gate_rope_theta": args.rope_theta},
+                   "head_dim": D, "block": 64, "gate_dim": dg,
+                   "mask": (f"the gate's threshold mask (T = {w['threshold']}) on planted Q/K, random-init weights"
+                            if gate_made else mask_desc(w["sparsity"])),
+                   "realized_sparsity": round(s_real, 5), "executed_tiles": tiles,
+                   "gate_mode": "threshold" if gate_made else "topk",
+                   "gate_threshold": w["threshold"] if gate_made else None, "gate_topk": k_gate,
+                   "gate_rope_theta": rope_theta},
         "breakdown_ms": {"gate": round(gate_avg, 4), "sparse_attention": round(attn_avg, 4),
                          "dense_attention": None if dense_ms is None else round(dense_ms, 4),
                          "dense_attention_with_gt_map": None if gt_ms is None else round(gt_ms, 4),
@@ -483,6 +539,12 @@ def main():
             "target_0.8/(1-s)": round(0.8 / (1.0 - s_real), 3),
             "ideal_1/(1-s)": round(1.0 / (1.0 - s_real), 3)},
         "dense_tflops": None if dense_ms is None else round(dense_flop / dense_ms / 1e9, 2),
+        "ground_truth": None if (gt_ms is None or dense_ms is None) else {
+            "kernel": "seer_attn_maxpool_gt (dense attention + 2D-maxpooled map)",
+            "ms": round(gt_ms, 4), "dense_ms": round(dense_ms, 4),
+            "overhead_vs_dense": round(gt_ms / dense_ms - 1.0, 4),
+            "map_shape": [B, Hq, nb, nb],
+            "pages_overhead_vs_flashattention": "< 0.05 (explainer section 3.4, customized training kernel)"},
         "roofline": {"kernel": "seer_block_sparse_attn_fwd (one call: main block-sparse kernel + merge of partial outputs)",
                      "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
