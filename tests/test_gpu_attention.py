@@ -27,7 +27,7 @@ def _run_full(shape, seed, mask, out_dtype, what):
                                                out_dtype=out_dtype, want_lse=True)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.attention(q, k, v, mask)
-    check_close(host(out), o_ref, f"{what} O")
+    check_close(host(out), o_ref, f"{what} O", out_dtype=out_dtype)
     check_lse(host(lse), l_ref, f"{what} LSE")
     return out, lse
 
@@ -84,7 +84,7 @@ def test_all_ones_mask_matches_dense():
     a, la = seer.seer_block_sparse_attn_fwd(q, k, v, ones, out_dtype=torch.float32, want_lse=True)
     b, lb = seer.seer_block_sparse_attn_fwd(q, k, v, None, out_dtype=torch.float32, want_lse=True)
     torch.cuda.synchronize()
-    check_close(host(a), host(b), "all-ones vs dense O", max_abs=2e-3, mean_abs=2e-5)
+    check_close(host(a), host(b), "all-ones vs dense O", max_abs=5e-4, mean_abs=2e-5)
     check_lse(host(la), host(lb), "all-ones vs dense LSE", tol=1e-4)
 
 
@@ -115,7 +115,7 @@ def test_llama8b_s8k_50_sampled():
     o_ref, l_ref = oracle.attention_rows(q, k, v, minfo.mask, rows)
     got = np.concatenate([out_h[b, h, 64 * i:64 * i + 64] for (b, h, i) in rows])
     got_l = np.concatenate([lse_h[b, h, 64 * i:64 * i + 64] for (b, h, i) in rows])
-    check_close(got, np.concatenate(o_ref), "8k O (sampled)")
+    check_close(got, np.concatenate(o_ref), "8k O (sampled)", out_dtype=torch.bfloat16)
     check_lse(got_l, np.concatenate(l_ref), "8k LSE (sampled)")
 
 
@@ -137,7 +137,7 @@ def _run_sampled(shape, seed, mask, out_dtype, rows, what):
     got_l = np.concatenate([host(lse[b, h, 64 * i:64 * i + 64]) for (b, h, i) in rows])
     del out, lse
     o_ref, l_ref = oracle.attention_rows(q, k, v, mask, rows)
-    check_close(got, np.concatenate(o_ref), f"{what} O (sampled)")
+    check_close(got, np.concatenate(o_ref), f"{what} O (sampled)", out_dtype=out_dtype)
     check_lse(got_l, np.concatenate(l_ref), f"{what} LSE (sampled)")
 
 
@@ -174,7 +174,7 @@ def test_sparse_multichunk_all_ones_matches_dense():
     a, la = seer.seer_block_sparse_attn_fwd(q, k, v, ones, out_dtype=torch.float32, want_lse=True)
     b, lb = seer.seer_block_sparse_attn_fwd(q, k, v, None, out_dtype=torch.float32, want_lse=True)
     torch.cuda.synchronize()
-    check_close(host(a), host(b), "all-ones vs dense O", max_abs=2e-3, mean_abs=2e-5)
+    check_close(host(a), host(b), "all-ones vs dense O", max_abs=5e-4, mean_abs=2e-5)
     check_lse(host(la), host(lb), "all-ones vs dense LSE", tol=1e-4)
 
 
@@ -222,7 +222,7 @@ def test_sparse_xcd_all_ones_matches_dense():
     a, la = seer.seer_block_sparse_attn_fwd(q, k, v, ones, out_dtype=torch.float32, want_lse=True)
     b, lb = seer.seer_block_sparse_attn_fwd(q, k, v, None, out_dtype=torch.float32, want_lse=True)
     torch.cuda.synchronize()
-    check_close(host(a), host(b), "xcd all-ones vs dense O", max_abs=2e-3, mean_abs=1e-4)
+    check_close(host(a), host(b), "xcd all-ones vs dense O", max_abs=1e-3, mean_abs=5e-5)
     check_lse(host(la), host(lb), "xcd all-ones vs dense LSE", tol=1e-4)
 
 

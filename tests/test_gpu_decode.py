@@ -140,7 +140,7 @@ def test_decode_attention_matches_oracle(name, shape, dens, dt):
     out, lse, _ = seer.seer_decode_attn_fwd(dev_bf16(qd), dev_bf16(k), dev_bf16(v), dev_u8(mask), out_dtype=dt,
                                             want_lse=True)
     torch.cuda.synchronize()
-    check_close(host(out), o_ref, f"{name} O")
+    check_close(host(out), o_ref, f"{name} O", out_dtype=dt)
     check_lse(host(lse), l_ref, f"{name} LSE")
 
 

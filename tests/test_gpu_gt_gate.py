@@ -40,7 +40,7 @@ def test_gt_matches_oracle(shape, dt):
     say(f"  gt max relative error on entries > 1e-6: {rel.max():.3e}")
     assert rel.max() < 1e-4
     assert np.all(g[..., np.triu_indices(shape.nb, 1)[0], np.triu_indices(shape.nb, 1)[1]] == 0.0)
-    check_close(host(out), o_ref, "gt-kernel O")
+    check_close(host(out), o_ref, "gt-kernel O", out_dtype=dt)
     check_lse(host(lse), l_ref, "gt-kernel LSE")
 
 

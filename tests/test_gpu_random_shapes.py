@@ -59,10 +59,10 @@ def test_random_shape_attention(name, shape, seed, p, dt):
     outd, lsed = seer.seer_block_sparse_attn_fwd(dq, dk, dv, None, out_dtype=dt, want_lse=True)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.attention(q, k, v, m)
-    check_close(host(out), o_ref, f"{name} sparse O")
+    check_close(host(out), o_ref, f"{name} sparse O", out_dtype=dt)
     check_lse(host(lse), l_ref, f"{name} sparse LSE")
     od_ref, ld_ref = oracle.attention(q, k, v, None)
-    check_close(host(outd), od_ref, f"{name} dense O")
+    check_close(host(outd), od_ref, f"{name} dense O", out_dtype=dt)
     check_lse(host(lsed), ld_ref, f"{name} dense LSE")
 
 

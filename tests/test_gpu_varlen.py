@@ -70,10 +70,10 @@ def test_varlen_sparse_and_dense_attention(D, dt):
         q, k, v = seqs[i]
         a, b = cu[i], cu[i + 1]
         o_ref, l_ref = oracle.attention(q, k, v, masks[i][None])
-        check_close(o_h[:, a:b][None], o_ref, f"seq {i} sparse O")
+        check_close(o_h[:, a:b][None], o_ref, f"seq {i} sparse O", out_dtype=dt)
         check_lse(l_h[:, a:b][None], l_ref, f"seq {i} sparse LSE")
         od_ref, ld_ref = oracle.attention(q, k, v, None)
-        check_close(od_h[:, a:b][None], od_ref, f"seq {i} dense O")
+        check_close(od_h[:, a:b][None], od_ref, f"seq {i} dense O", out_dtype=dt)
         # the batch-1 call on the sequence alone gives the same bits
         o1, l1 = seer.seer_block_sparse_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_u8(masks[i][None]),
                                                  out_dtype=dt, want_lse=True)
