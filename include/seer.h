@@ -248,6 +248,29 @@ seer_status seer_decode_attn_fwd(const seer_shape* shape, const void* q, const v
                                  size_t workspace_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * Allocation-free decode attention, for callers that cannot allocate device
+ * memory between calls: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * Computes exactly what seer_decode_attn_fwd computes (same kernels, same
+ * bits), with the same arguments minus the workspace. Its scratch (per-split
+ * partial results and the per-KV-group block lists) is a fixed array of
+ * SEER_NOALLOC_SCRATCH_BYTES in each device's copy of the library, held until
+ * the process ends; the call allocates nothing (no hipMalloc, no library
+ * routine that allocates). Shapes whose seer_decode_attn_workspace_size()
+ * exceeds SEER_NOALLOC_SCRATCH_BYTES are rejected with SEER_ERR_UNSUPPORTED
+ * before anything is enqueued (16 MiB covers, e.g., batch 64 of 32/8 heads
+ * at 128k cached tokens). Every call on one device shares that device's
+ * scratch and overwrites it: calls that can overlap on one device (other
+ * streams, other threads) race and must be serialized by the caller. No
+ * part of the scratch has to start at zero.
+ * ---------------------------------------------------------------------- */
+#define SEER_NOALLOC_SCRATCH_BYTES (16u << 20)
+seer_status seer_decode_attn_fwd_noalloc(const seer_shape* shape, const void* q, const void* k_cache,
+                                         const void* v_cache, const uint8_t* block_mask, void* out,
+                                         seer_dtype out_dtype, float* lse, float* gt, void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * Varlen (packed) prefill batches ([R], on batching: variable-length inputs
  * are packed along the sequence dimension, hiding the batch in the sequence
  * length).

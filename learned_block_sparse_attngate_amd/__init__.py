@@ -9,6 +9,7 @@ from ._binding import (  # noqa: F401
     BLOCK, EXPORTED, LIB_PATH, SeerError, SeerShape, load_library, make_shape, nblocks,
     seer_gate_fwd, seer_gate_distill_bwd, seer_block_sparse_attn_fwd, seer_attn_maxpool_gt,
     seer_decode_compress_k, seer_decode_gate_fwd, seer_decode_attn_fwd, decode_attn_workspace_bytes,
+    seer_decode_attn_fwd_noalloc, NOALLOC_SCRATCH_BYTES,
     SeerVarlen, make_varlen, varlen_map_offsets, seer_gate_varlen_fwd, seer_block_sparse_attn_varlen_fwd,
     seer_attn_maxpool_gt_varlen,
     gate_workspace_bytes, distill_workspace_bytes, gt_workspace_bytes, attn_workspace_bytes, version,

@@ -36,6 +36,7 @@ EXPORTED = (
     "seer_attn_workspace_size", "seer_block_sparse_attn_fwd",
     "seer_gt_workspace_size", "seer_attn_maxpool_gt",
     "seer_decode_compress_k", "seer_decode_gate_fwd", "seer_decode_attn_workspace_size", "seer_decode_attn_fwd",
+    "seer_decode_attn_fwd_noalloc",
     "seer_varlen_map_elements", "seer_gate_varlen_workspace_size", "seer_gate_varlen_fwd",
     "seer_attn_varlen_workspace_size", "seer_block_sparse_attn_varlen_fwd", "seer_gt_varlen_workspace_size",
     "seer_attn_maxpool_gt_varlen",
@@ -98,6 +99,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.seer_decode_attn_workspace_size.restype = sz
     lib.seer_decode_attn_fwd.argtypes = [shp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, sz, vp]
     lib.seer_decode_attn_fwd.restype = ctypes.c_int
+    lib.seer_decode_attn_fwd_noalloc.argtypes = [shp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp]
+    lib.seer_decode_attn_fwd_noalloc.restype = ctypes.c_int
     vlp = ctypes.POINTER(SeerVarlen)
     lib.seer_varlen_map_elements.argtypes = [vlp]
     lib.seer_varlen_map_elements.restype = sz
@@ -453,6 +456,43 @@ def seer_decode_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.seer_decode_attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_mask),
                                     _ptr(out), dt, _ptr(lse), _ptr(gt), _ptr(workspace), ws_bytes, _stream(dev)))
+    return out, lse, gt
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20    # SEER_NOALLOC_SCRATCH_BYTES
+
+
+def seer_decode_attn_fwd_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 block_mask: Optional[torch.Tensor], out: torch.Tensor, *,
+                                 lse: Optional[torch.Tensor] = None, gt: Optional[torch.Tensor] = None):
+    """Decode attention through the allocation-free entry point: the caller
+    passes every output, the library uses its own fixed device scratch, and
+    nothing is allocated. Same results as seer_decode_attn_fwd. Calls that
+    overlap on one device share that scratch and must be serialized."""
+    lib = load_library()
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a 3-D tensor [B, Hq, D]")
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{n} must be a 4-D tensor [B, Hkv, S, D]")
+    B, Hq, D = q.shape
+    Hkv, S = k_cache.shape[1], k_cache.shape[2]
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError(f"heads of q ({Hq}) must be a positive multiple of the cache's {Hkv} heads")
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, S, D))
+    _need(v_cache, "v_cache", torch.bfloat16, (B, Hkv, S, D))
+    nb = nblocks(S)
+    _opt(block_mask, "block_mask", torch.uint8, (B, Hq, nb))
+    if out is None:
+        raise ValueError("the allocation-free call needs a caller-provided out")
+    dt = _check_out(out, lse, out.dtype, (B, Hq, D), (B, Hq))
+    _opt(gt, "gt", torch.float32, (B, Hq, nb))
+    dev = q.device
+    _devices(dev, k_cache=k_cache, v_cache=v_cache, block_mask=block_mask, out=out, lse=lse, gt=gt)
+    shape = make_shape(B, Hq, Hkv, S, D)
+    _check(lib.seer_decode_attn_fwd_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(block_mask), _ptr(out), dt, _ptr(lse), _ptr(gt), _stream(dev)))
     return out, lse, gt
 
 

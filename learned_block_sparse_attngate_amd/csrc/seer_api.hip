@@ -192,6 +192,36 @@ seer_status check_rope(float rope_theta) {
 
 }  // namespace
 
+// Scratch of the allocation-free entry point (seer_decode_attn_fwd_noalloc):
+// one copy per device, held until the process ends.
+static __device__ __align__(256) unsigned char scratch[SEER_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[64];
+
+// Device address of the current device's `scratch`, looked up on the first
+// call on that device.
+seer_status scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SEER_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(SEER_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot]() { slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch)); });
+  if (slot.err != hipSuccess || slot.ptr == nullptr)
+    return fail(SEER_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(slot.err));
+  *ptr = slot.ptr;
+  return SEER_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* seer_status_string(seer_status s) {
@@ -363,9 +393,10 @@ size_t seer_decode_attn_workspace_size(const seer_shape* shape) {
                                       shape->head_dim);
 }
 
-seer_status seer_decode_attn_fwd(const seer_shape* shape, const void* q, const void* k_cache, const void* v_cache,
-                                 const uint8_t* block_mask, void* out, seer_dtype out_dtype, float* lse, float* gt,
-                                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+static seer_status decode_attn_impl(const seer_shape* shape, const void* q, const void* k_cache,
+                                    const void* v_cache, const uint8_t* block_mask, void* out, seer_dtype out_dtype,
+                                    float* lse, float* gt, void* workspace, size_t workspace_bytes,
+                                    void* hip_stream) {
   bool empty = false;
   seer_status st = check_shape(shape, &empty);
   if (st != SEER_OK) return st;
@@ -414,6 +445,38 @@ seer_status seer_decode_attn_fwd(const seer_shape* shape, const void* q, const v
   hipError_t e = seer::launch_decode_attn(a, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SEER_ERR_HIP, "decode attention launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+seer_status seer_decode_attn_fwd(const seer_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                                 const uint8_t* block_mask, void* out, seer_dtype out_dtype, float* lse, float* gt,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return decode_attn_impl(shape, q, k_cache, v_cache, block_mask, out, out_dtype, lse, gt, workspace,
+                          workspace_bytes, hip_stream);
+}
+
+// Allocation-free variant: the kernels' scratch (per-split partials and the
+// per-KV-group block lists) lives in `scratch`, a fixed array in each device's
+// copy of this library. Host code must not pass the array's name to a kernel:
+// on the host it only stands for the symbol. Its device address is looked up
+// once per device (with that device current) and kept.
+seer_status seer_decode_attn_fwd_noalloc(const seer_shape* shape, const void* q, const void* k_cache,
+                                         const void* v_cache, const uint8_t* block_mask, void* out,
+                                         seer_dtype out_dtype, float* lse, float* gt, void* hip_stream) {
+  bool empty = false;
+  seer_status st = check_shape(shape, &empty);
+  if (st != SEER_OK) return st;
+  if (empty) return decode_attn_impl(shape, q, k_cache, v_cache, block_mask, out, out_dtype, lse, gt, nullptr, 0,
+                                     hip_stream);
+  const size_t need = seer_decode_attn_workspace_size(shape);
+  if (need > SEER_NOALLOC_SCRATCH_BYTES)
+    return fail(SEER_ERR_UNSUPPORTED,
+                "decode attention of this shape needs %zu bytes of scratch, more than the %zu bytes the "
+                "allocation-free entry point holds; use seer_decode_attn_fwd with a workspace",
+                need, static_cast<size_t>(SEER_NOALLOC_SCRATCH_BYTES));
+  void* ptr = nullptr;
+  if ((st = scratch_address(&ptr)) != SEER_OK) return st;
+  return decode_attn_impl(shape, q, k_cache, v_cache, block_mask, out, out_dtype, lse, gt, ptr,
+                          SEER_NOALLOC_SCRATCH_BYTES, hip_stream);
 }
 
 // ---------------------------------------------------------------------------
