@@ -216,46 +216,52 @@ def bench_decode(seer, torch, q, k, v, shape, stream, seed, reps: int = 50):
 
 
 def bench_varlen(seer, torch, dev, stream, seed, reps: int = 5):
-    """A packed batch of 8 Llama-3.1-8B-shaped sequences of seeded lengths in
-    [4k, 32k] tokens (no padding), each with its own 90%-sparse seeded block
-    mask, through the varlen block-sparse attention; TFLOP/s on executed tiles."""
+    """Packed batches of Llama-3.1-8B-shaped sequences (no padding), each
+    sequence with its own 90%-sparse seeded block mask, through the varlen
+    block-sparse attention: 8 sequences of seeded lengths in [4k, 32k] tokens,
+    and 64 sequences of 2048 tokens; TFLOP/s on executed tiles."""
     import synth
     rng = np.random.Generator(np.random.PCG64(seed + 300))
-    lens = [int(x) for x in rng.integers(4096, 32769, size=8)]
-    cu = [0] + [int(x) for x in np.cumsum(lens)]
-    Hq, Hkv, D = 32, 8, 128
-    T = cu[-1]
-    g = torch.Generator(device=dev)
-    g.manual_seed(seed + 301)
-    q = torch.randn((Hq, T, D), generator=g, device=dev).to(torch.bfloat16)
-    k = torch.randn((Hkv, T, D), generator=g, device=dev).to(torch.bfloat16)
-    v = torch.randn((Hkv, T, D), generator=g, device=dev).to(torch.bfloat16)
-    masks, tiles = [], 0
-    for i, n in enumerate(lens):
-        sh = synth.Shape(1, Hq, Hkv, n, D)
-        m = synth.gen_block_mask(sh, seed + 310 + i, 0.9).mask[0]
-        nb = sh.nb
-        tiles += int(np.count_nonzero(np.tril(np.ones((nb, nb), dtype=bool))[None] & m.astype(bool)))
-        masks.append(m.reshape(-1))
-    mask = torch.from_numpy(np.concatenate(masks)).to(dev)
-    out = torch.empty((Hq, T, D), dtype=torch.bfloat16, device=dev)
+    batches = {"mixed_8x4k-32k": [int(x) for x in rng.integers(4096, 32769, size=8)],
+               "uniform_64x2k": [2048] * 64}
+    res = {}
+    for bi, (name, lens) in enumerate(batches.items()):
+        cu = [0] + [int(x) for x in np.cumsum(lens)]
+        Hq, Hkv, D = 32, 8, 128
+        T = cu[-1]
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed + 301 + bi)
+        q = torch.randn((Hq, T, D), generator=g, device=dev).to(torch.bfloat16)
+        k = torch.randn((Hkv, T, D), generator=g, device=dev).to(torch.bfloat16)
+        v = torch.randn((Hkv, T, D), generator=g, device=dev).to(torch.bfloat16)
+        masks, tiles = [], 0
+        for i, n in enumerate(lens):
+            sh = synth.Shape(1, Hq, Hkv, n, D)
+            m = synth.gen_block_mask(sh, seed + 310 + 100 * bi + i, 0.9).mask[0]
+            nb = sh.nb
+            tiles += int(np.count_nonzero(np.tril(np.ones((nb, nb), dtype=bool))[None] & m.astype(bool)))
+            masks.append(m.reshape(-1))
+        mask = torch.from_numpy(np.concatenate(masks)).to(dev)
+        out = torch.empty((Hq, T, D), dtype=torch.bfloat16, device=dev)
 
-    def run():
-        seer.seer_block_sparse_attn_varlen_fwd(q, k, v, cu, mask, out=out)
-    run()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
+        def run():
+            seer.seer_block_sparse_attn_varlen_fwd(q, k, v, cu, mask, out=out)
         run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    tflops = tiles * 4.0 * 64 * 64 * D / ms / 1e9
-    print(f"[bench] varlen: {len(lens)} sequences, {T} tokens, block-sparse attention {ms:.3f} ms "
-          f"({tflops:.1f} TFLOP/s on executed tiles)", file=sys.stderr, flush=True)
-    return {"workload": f"packed batch of 8 sequences, lengths {lens}, 90% sparse masks", "tokens": T,
-            "sparse_attention_ms": round(ms, 4), "executed_tiles": tiles, "tflops": round(tflops, 2)}
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tflops = tiles * 4.0 * 64 * 64 * D / ms / 1e9
+        print(f"[bench] varlen {name}: {len(lens)} sequences, {T} tokens, block-sparse attention {ms:.3f} ms "
+              f"({tflops:.1f} TFLOP/s on executed tiles)", file=sys.stderr, flush=True)
+        res[name] = {"lengths": lens if len(set(lens)) > 1 else f"{len(lens)} x {lens[0]}", "tokens": T,
+                     "sparse_attention_ms": round(ms, 4), "executed_tiles": tiles, "tflops": round(tflops, 2)}
+        del q, k, v, mask, out
+    return res
 
 
 def mask_desc(sparsity) -> str:

@@ -284,9 +284,15 @@ seer_status seer_decode_attn_fwd_noalloc(const seer_shape* shape, const void* q,
  * nb_i = ceil(len_i / 64), stored one after another: sequence i's map starts
  * at element sum_{i'<i} Hq * nb_i'^2 (seer_varlen_map_elements() gives the
  * total). Every call computes exactly what the batch-1 call computes on each
- * sequence alone. The sequences run one after another on hip_stream and share
- * the workspace, whose size is the largest any sequence needs. All sequences
- * are validated before anything is enqueued. Empty sequences are allowed.
+ * sequence alone, bit for bit. Attention and the ground-truth map run the
+ * sequences together: up to 64 sequences per launch, longest first, each row
+ * of each sequence one workgroup of a single grid (in block-sparse mode,
+ * sequences of more than 1024 blocks run on their own launches, key-chunked,
+ * and share the workspace). The gate runs the sequences one after another
+ * and shares the workspace. seer_gt_varlen_workspace_size() covers the
+ * scratch of every sequence of the largest shared launch; the other
+ * workspace sizes are the largest any sequence needs. All sequences are
+ * validated before anything is enqueued. Empty sequences are allowed.
  * ---------------------------------------------------------------------- */
 typedef struct seer_varlen {
   int32_t num_seqs;

@@ -169,8 +169,12 @@ __device__ __forceinline__ void tile_update(const f32x16_t (&sacc)[2], const u32
     }
 }
 
+// One (batch, query head, query block) row -- or one key chunk of it -- of
+// the tile loop below. `w` is the row's workgroup index in the launch the
+// block-sparse circular sweep is phased by (see the sweep below).
 template <int D, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
+__device__ __forceinline__ void attn_row(const AttnArgs& p, const int w, const int qb, const int bh,
+                                         const int chunk) {
   constexpr int CPR = D / 8;               // 16-byte chunks per K/V row
   constexpr int KS = D / 16;               // MFMA k-steps for S^T
   constexpr int MT = D / 32;               // MFMA m-tiles for O^T
@@ -189,52 +193,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
-  // ---- which row ---------------------------------------------------------
-  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-  // L2); all orders below launch the heaviest rows (last query blocks) first.
-  //  0: heads interleaved, all KV groups at once;
-  //  1: the query heads of one KV group on one XCD;
-  //  2: KV-group major: every XCD works on the same KV group at a time, so
-  //     the K/V working set is one group;
-  //  3: KV-group major, then head major inside the group.
-  const int BH = p.B * p.Hq;
-  const int w = blockIdx.x;
-  int qb, bh;
-  int chunk = 0;                                  // block-sparse: key chunk of this work item
-  if constexpr (MODE == kSparse) {
-    // Key-chunked items: (batch, KV group) major, then chunk c ascending, then
-    // head, then query block descending. Consecutive items go round-robin over
-    // the XCDs, so all of them work on one C-block K/V chunk of one group at a
-    // time and that chunk stays in each XCD's L2.
-    const int gi = static_cast<int>(w / p.items_per_group);
-    long long r = w - gi * p.items_per_group;
-    int c = 0;
-    while (true) {
-      const long long n = static_cast<long long>(p.group) * (p.nb - c * p.chunk);   // items of chunk c
-      if (r < n) break;
-      r -= n;
-      ++c;
-    }
-    const int rows = p.nb - c * p.chunk;            // query blocks qb >= c*C
-    const int hig = static_cast<int>(r / rows);
-    qb = p.nb - 1 - static_cast<int>(r % rows);
-    chunk = c;
-    const int bb = gi / p.Hkv, gg = gi - bb * p.Hkv;
-    bh = bb * p.Hq + gg * p.group + hig;
-  } else if (p.sched >= 2) {
-    const int R = p.group * p.nb;                 // rows per (batch, KV group)
-    const int gi = w / R, r = w - gi * R;         // gi = b * Hkv + g
-    int hig;
-    if (p.sched == 2) { qb = p.nb - 1 - r / p.group; hig = r % p.group; }
-    else { hig = r / p.nb; qb = p.nb - 1 - r % p.nb; }
-    const int bb = gi / p.Hkv, gg = gi - bb * p.Hkv;
-    bh = bb * p.Hq + gg * p.group + hig;
-  } else {
-    qb = p.nb - 1 - w / BH;
-    int local = w % BH;
-    if (p.sched == 1) local = (local & 7) * (BH >> 3) + (local >> 3);
-    bh = local;
-  }
   const int b = bh / p.Hq;
   const int h = bh - b * p.Hq;
   const int g = h / p.group;
@@ -507,6 +465,109 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
       gtrow[kb] = best;
     }
   }
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
+  // ---- which row ---------------------------------------------------------
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+  // L2); all orders below launch the heaviest rows (last query blocks) first.
+  //  0: heads interleaved, all KV groups at once;
+  //  1: the query heads of one KV group on one XCD;
+  //  2: KV-group major: every XCD works on the same KV group at a time, so
+  //     the K/V working set is one group;
+  //  3: KV-group major, then head major inside the group.
+  const int BH = p.B * p.Hq;
+  const int w = blockIdx.x;
+  int qb, bh;
+  int chunk = 0;                                  // block-sparse: key chunk of this work item
+  if constexpr (MODE == kSparse) {
+    // Key-chunked items: (batch, KV group) major, then chunk c ascending, then
+    // head, then query block descending. Consecutive items go round-robin over
+    // the XCDs, so all of them work on one C-block K/V chunk of one group at a
+    // time and that chunk stays in each XCD's L2.
+    const int gi = static_cast<int>(w / p.items_per_group);
+    long long r = w - gi * p.items_per_group;
+    int c = 0;
+    while (true) {
+      const long long n = static_cast<long long>(p.group) * (p.nb - c * p.chunk);   // items of chunk c
+      if (r < n) break;
+      r -= n;
+      ++c;
+    }
+    const int rows = p.nb - c * p.chunk;            // query blocks qb >= c*C
+    const int hig = static_cast<int>(r / rows);
+    qb = p.nb - 1 - static_cast<int>(r % rows);
+    chunk = c;
+    const int bb = gi / p.Hkv, gg = gi - bb * p.Hkv;
+    bh = bb * p.Hq + gg * p.group + hig;
+  } else if (p.sched >= 2) {
+    const int R = p.group * p.nb;                 // rows per (batch, KV group)
+    const int gi = w / R, r = w - gi * R;         // gi = b * Hkv + g
+    int hig;
+    if (p.sched == 2) { qb = p.nb - 1 - r / p.group; hig = r % p.group; }
+    else { hig = r / p.nb; qb = p.nb - 1 - r % p.nb; }
+    const int bb = gi / p.Hkv, gg = gi - bb * p.Hkv;
+    bh = bb * p.Hq + gg * p.group + hig;
+  } else {
+    qb = p.nb - 1 - w / BH;
+    int local = w % BH;
+    if (p.sched == 1) local = (local & 7) * (BH >> 3) + (local >> 3);
+    bh = local;
+  }
+  attn_row<D, MODE>(p, w, qb, bh, chunk);
+}
+
+// Packed (varlen) batch in one launch: workgroup w takes a row of the sequence
+// whose row range holds w. Each sequence is the batch-1 problem at its token
+// offset with the packed length as head stride, and every row runs exactly
+// what the batch-1 call on that sequence runs for it (the block-sparse sweep
+// is phased by the row's workgroup index in that call), so the results are
+// bitwise those of the batch-1 calls. Rows of a sequence go in the batch-1
+// order; sequences in table order (longest first).
+template <int D, int MODE>
+__global__ __launch_bounds__(kThreads, 2) void attn_varlen_kernel(AttnArgs p, VarlenTable t) {
+  const int w = blockIdx.x;
+  int lo = 0, hi = t.n - 1;                       // last sequence i with row_start[i] <= w
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (t.row_start[mid] <= w) lo = mid;
+    else hi = mid - 1;
+  }
+  AttnArgs a = p;
+  const size_t tok = static_cast<size_t>(t.tok[lo]);
+  a.q += tok * D;
+  a.k += tok * D;
+  a.v += tok * D;
+  a.out = a.out_bf16 ? static_cast<void*>(static_cast<uint16_t*>(p.out) + tok * D)
+                     : static_cast<void*>(static_cast<float*>(p.out) + tok * D);
+  if (a.lse != nullptr) a.lse += tok;
+  a.S = t.len[lo];
+  a.nb = (a.S + kBlock - 1) / kBlock;
+  a.ntri = static_cast<long long>(a.nb) * (a.nb + 1) / 2;
+  if constexpr (MODE == kSparse) {
+    a.mask += t.map_off[lo];
+    a.items_per_group = static_cast<long long>(a.group) * a.nb;
+  }
+  if constexpr (MODE == kDenseGt) {
+    a.gt += t.map_off[lo];
+    a.rmax += t.rmax_off[lo];
+  }
+  // the row's place in the batch-1 launch order: KV-group major (one group's
+  // K/V hot at a time), then head-major for block-sparse rows, query-block
+  // major for dense ones, heaviest rows first
+  const int local = w - t.row_start[lo];
+  const int per_group = a.group * a.nb;
+  const int g = local / per_group, r = local - g * per_group;
+  int qb, hig;
+  if constexpr (MODE == kSparse) {
+    hig = r / a.nb;
+    qb = a.nb - 1 - (r - hig * a.nb);
+  } else {
+    qb = a.nb - 1 - r / a.group;
+    hig = r - (a.nb - 1 - qb) * a.group;
+  }
+  attn_row<D, MODE>(a, local, qb, g * a.group + hig, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1095,6 +1156,22 @@ SparsePlan sparse_plan(int B, int Hkv, int group, int nb, int D) {
 hipError_t launch_attn(const AttnArgs& a, int mode, hipStream_t st) {
   if (a.D == 64) return launch_d<64>(a, mode, st);
   return launch_d<128>(a, mode, st);
+}
+
+int varlen_chunk_blocks() { return kListCap; }
+
+hipError_t launch_attn_varlen(const AttnArgs& a, const VarlenTable& t, int mode, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(t.row_start[t.n])), block(kThreads);
+  if (a.D == 64) {
+    if (mode == kSparse) hipLaunchKernelGGL((attn_varlen_kernel<64, kSparse>), grid, block, 0, st, a, t);
+    else if (mode == kDense) hipLaunchKernelGGL((attn_varlen_kernel<64, kDense>), grid, block, 0, st, a, t);
+    else hipLaunchKernelGGL((attn_varlen_kernel<64, kDenseGt>), grid, block, 0, st, a, t);
+  } else {
+    if (mode == kSparse) hipLaunchKernelGGL((attn_varlen_kernel<128, kSparse>), grid, block, 0, st, a, t);
+    else if (mode == kDense) hipLaunchKernelGGL((attn_varlen_kernel<128, kDense>), grid, block, 0, st, a, t);
+    else hipLaunchKernelGGL((attn_varlen_kernel<128, kDenseGt>), grid, block, 0, st, a, t);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace seer

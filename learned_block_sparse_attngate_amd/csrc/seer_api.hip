@@ -7,7 +7,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
+#include <vector>
 #include <string>
 
 #include "seer.h"
@@ -687,6 +689,70 @@ static seer_shape varlen_shape(const seer_varlen* vl, int i) {
   return s;
 }
 
+// Sequences of a packed batch that share launches: non-empty, at most max_nb
+// blocks, longest first (stable), cut into batches of kVarlenMaxSeqs.
+static std::vector<int> varlen_shared(const seer_varlen* vl, long long max_nb) {
+  std::vector<int> idx;
+  for (int i = 0; i < vl->num_seqs; ++i) {
+    const long long len = static_cast<long long>(vl->cu_seqlens[i + 1]) - vl->cu_seqlens[i];
+    if (len > 0 && (len + kBlock - 1) / kBlock <= max_nb) idx.push_back(i);
+  }
+  std::stable_sort(idx.begin(), idx.end(), [vl](int a, int b) {
+    return vl->cu_seqlens[a + 1] - vl->cu_seqlens[a] > vl->cu_seqlens[b + 1] - vl->cu_seqlens[b];
+  });
+  return idx;
+}
+
+// Element offset of each sequence's [Hq, nb_i, nb_i] block map.
+static std::vector<long long> varlen_map_offsets(const seer_varlen* vl) {
+  std::vector<long long> off(static_cast<size_t>(vl->num_seqs) + 1, 0);
+  for (int i = 0; i < vl->num_seqs; ++i) {
+    const long long nb = (static_cast<long long>(vl->cu_seqlens[i + 1]) - vl->cu_seqlens[i] + kBlock - 1) / kBlock;
+    off[i + 1] = off[i] + static_cast<long long>(vl->heads_q) * nb * nb;
+  }
+  return off;
+}
+
+// Launch table of sequences idx[from .. from+n-1]; *rmax_floats receives the
+// ground-truth scratch those sequences need (floats). False if the rows
+// exceed the launch limit.
+static bool varlen_table(const seer_varlen* vl, const std::vector<int>& idx, size_t from, int n,
+                         const std::vector<long long>& moff, seer::VarlenTable* t, long long* rmax_floats) {
+  long long rows = 0, rmax = 0;
+  t->n = n;
+  for (int k = 0; k < n; ++k) {
+    const int i = idx[from + k];
+    const long long len = static_cast<long long>(vl->cu_seqlens[i + 1]) - vl->cu_seqlens[i];
+    const long long nb = (len + kBlock - 1) / kBlock;
+    t->row_start[k] = static_cast<int>(rows);
+    t->tok[k] = vl->cu_seqlens[i];
+    t->len[k] = static_cast<int>(len);
+    t->map_off[k] = moff[i];
+    t->rmax_off[k] = rmax;
+    rows += static_cast<long long>(vl->heads_q) * nb;
+    rmax += static_cast<long long>(vl->heads_q) * (nb * (nb + 1) / 2) * kBlock;
+    if (rows > 0x7fffffffLL) return false;
+  }
+  t->row_start[n] = static_cast<int>(rows);
+  *rmax_floats = rmax;
+  return true;
+}
+
+// Ground-truth scratch (bytes) of the largest shared launch of a packed batch.
+static size_t varlen_gt_batch_bytes(const seer_varlen* vl) {
+  const std::vector<int> idx = varlen_shared(vl, 1LL << 40);
+  const std::vector<long long> moff = varlen_map_offsets(vl);
+  size_t need = 0;
+  for (size_t from = 0; from < idx.size(); from += seer::kVarlenMaxSeqs) {
+    const int n = static_cast<int>(std::min<size_t>(seer::kVarlenMaxSeqs, idx.size() - from));
+    seer::VarlenTable t{};
+    long long rmax = 0;
+    varlen_table(vl, idx, from, n, moff, &t, &rmax);
+    need = std::max(need, align_up(static_cast<size_t>(rmax) * sizeof(float)));
+  }
+  return need;
+}
+
 size_t seer_varlen_map_elements(const seer_varlen* vl) {
   long long total = 0;
   if (check_varlen(vl, &total) != SEER_OK) return 0;
@@ -726,13 +792,7 @@ size_t seer_attn_varlen_workspace_size(const seer_varlen* vl) {
 size_t seer_gt_varlen_workspace_size(const seer_varlen* vl) {
   long long total = 0;
   if (check_varlen(vl, &total) != SEER_OK) return 0;
-  size_t need = 0;
-  for (int i = 0; i < vl->num_seqs; ++i) {
-    const seer_shape s = varlen_shape(vl, i);
-    const size_t n = seer_gt_workspace_size(&s);
-    need = n > need ? n : need;
-  }
-  return need;
+  return varlen_gt_batch_bytes(vl);
 }
 
 seer_status seer_gate_varlen_fwd(const seer_varlen* vl, int32_t gate_dim, int32_t wk_per_kv_head, float rope_theta,
@@ -770,22 +830,46 @@ seer_status seer_block_sparse_attn_varlen_fwd(const seer_varlen* vl, const void*
   seer_status st = check_varlen(vl, &total);
   if (st != SEER_OK) return st;
   const size_t esize = out_dtype == SEER_BF16 ? 2 : 4;
+  // Sequences whose rows are one work item each (all of them in dense mode,
+  // up to 1024 blocks in block-sparse mode) share launches; longer ones run
+  // on their own (key-chunked or XCD-owned paths).
+  const long long max_shared = block_mask != nullptr ? 1024 : (1LL << 40);
+  const std::vector<int> shared = varlen_shared(vl, max_shared);
+  const std::vector<long long> moff = varlen_map_offsets(vl);
+  std::vector<char> is_shared(static_cast<size_t>(vl->num_seqs), 0);
+  for (int i : shared) is_shared[i] = 1;
   for (int pass = 0; pass < 2; ++pass) {
-    size_t moff = 0;
     for (int i = 0; i < vl->num_seqs; ++i) {
       const seer_shape s = varlen_shape(vl, i);
       const size_t tok = static_cast<size_t>(vl->cu_seqlens[i]);
       const size_t t0 = tok * vl->head_dim;
-      const size_t nb = nblocks(&s);
-      if (s.seq_len > 0) {
-        st = attn_impl(&s, total, q ? static_cast<const uint16_t*>(q) + t0 : nullptr,
-                       k ? static_cast<const uint16_t*>(k) + t0 : nullptr,
-                       v ? static_cast<const uint16_t*>(v) + t0 : nullptr, block_mask ? block_mask + moff : nullptr,
-                       out ? static_cast<char*>(out) + t0 * esize : nullptr, out_dtype, lse ? lse + tok : nullptr,
-                       workspace, workspace_bytes, hip_stream, pass == 1);
-        if (st != SEER_OK) return st;
-      }
-      moff += static_cast<size_t>(vl->heads_q) * nb * nb;
+      if (s.seq_len == 0 || (pass == 1 && is_shared[i])) continue;
+      st = attn_impl(&s, total, q ? static_cast<const uint16_t*>(q) + t0 : nullptr,
+                     k ? static_cast<const uint16_t*>(k) + t0 : nullptr,
+                     v ? static_cast<const uint16_t*>(v) + t0 : nullptr, block_mask ? block_mask + moff[i] : nullptr,
+                     out ? static_cast<char*>(out) + t0 * esize : nullptr, out_dtype, lse ? lse + tok : nullptr,
+                     workspace, workspace_bytes, hip_stream, pass == 1);
+      if (st != SEER_OK) return st;
+    }
+    for (size_t from = 0; from < shared.size(); from += seer::kVarlenMaxSeqs) {
+      const int n = static_cast<int>(std::min<size_t>(seer::kVarlenMaxSeqs, shared.size() - from));
+      seer::VarlenTable t{};
+      long long rmax = 0;
+      if (!varlen_table(vl, shared, from, n, moff, &t, &rmax))
+        return fail(SEER_ERR_SHAPE, "the rows of a shared varlen launch exceed the launch limit");
+      if (pass == 0) continue;
+      const seer_shape s = varlen_shape(vl, shared[from]);
+      seer::AttnArgs a = attn_args(&s, q, k, v, block_mask ? 0 : 1);
+      a.hs = total;
+      a.mask = block_mask;
+      a.out = out;
+      a.lse = lse;
+      a.out_bf16 = out_dtype == SEER_BF16;
+      a.chunk = seer::varlen_chunk_blocks();
+      a.nchunk = 1;
+      a.rotate = 1;
+      hipError_t e = seer::launch_attn_varlen(a, t, block_mask ? 0 : 1, static_cast<hipStream_t>(hip_stream));
+      if (e != hipSuccess) return fail(SEER_ERR_HIP, "varlen attention launch failed: %s", hipGetErrorString(e));
     }
   }
   return ok();
@@ -798,26 +882,48 @@ seer_status seer_attn_maxpool_gt_varlen(const seer_varlen* vl, const void* q, co
   seer_status st = check_varlen(vl, &total);
   if (st != SEER_OK) return st;
   const size_t esize = out_dtype == SEER_BF16 ? 2 : 4;
-  for (int pass = 0; pass < 2; ++pass) {
-    size_t moff = 0;
-    for (int i = 0; i < vl->num_seqs; ++i) {
-      const seer_shape s = varlen_shape(vl, i);
-      const size_t tok = static_cast<size_t>(vl->cu_seqlens[i]);
-      const size_t t0 = tok * vl->head_dim;
-      const size_t nb = nblocks(&s);
-      if (s.seq_len > 0) {
-        st = gt_impl(&s, total, q ? static_cast<const uint16_t*>(q) + t0 : nullptr,
-                     k ? static_cast<const uint16_t*>(k) + t0 : nullptr,
-                     v ? static_cast<const uint16_t*>(v) + t0 : nullptr,
-                     out ? static_cast<char*>(out) + t0 * esize : nullptr, out_dtype, lse ? lse + tok : nullptr,
-                     gt ? gt + moff : nullptr, workspace, workspace_bytes, hip_stream, pass == 1);
-        if (st != SEER_OK) return st;
-      }
-      moff += static_cast<size_t>(vl->heads_q) * nb * nb;
-    }
+  const std::vector<long long> moff = varlen_map_offsets(vl);
+  // every sequence is validated as the batch-1 call, then all run in shared launches
+  for (int i = 0; i < vl->num_seqs; ++i) {
+    const seer_shape s = varlen_shape(vl, i);
+    const size_t tok = static_cast<size_t>(vl->cu_seqlens[i]);
+    const size_t t0 = tok * vl->head_dim;
+    if (s.seq_len == 0) continue;
+    st = gt_impl(&s, total, q ? static_cast<const uint16_t*>(q) + t0 : nullptr,
+                 k ? static_cast<const uint16_t*>(k) + t0 : nullptr, v ? static_cast<const uint16_t*>(v) + t0 : nullptr,
+                 out ? static_cast<char*>(out) + t0 * esize : nullptr, out_dtype, lse ? lse + tok : nullptr,
+                 gt ? gt + moff[i] : nullptr, workspace, workspace_bytes, hip_stream, false);
+    if (st != SEER_OK) return st;
+  }
+  const size_t need = varlen_gt_batch_bytes(vl);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+    return fail(SEER_ERR_WORKSPACE, "workspace must be %zu bytes, 16-byte aligned (got %zu at %p)", need,
+                workspace_bytes, workspace);
+  const std::vector<int> shared = varlen_shared(vl, 1LL << 40);
+  for (size_t from = 0; from < shared.size(); from += seer::kVarlenMaxSeqs) {
+    const int n = static_cast<int>(std::min<size_t>(seer::kVarlenMaxSeqs, shared.size() - from));
+    seer::VarlenTable t{};
+    long long rmax = 0;
+    if (!varlen_table(vl, shared, from, n, moff, &t, &rmax))
+      return fail(SEER_ERR_SHAPE, "the rows of a shared varlen launch exceed the launch limit");
+  }
+  for (size_t from = 0; from < shared.size(); from += seer::kVarlenMaxSeqs) {
+    const int n = static_cast<int>(std::min<size_t>(seer::kVarlenMaxSeqs, shared.size() - from));
+    seer::VarlenTable t{};
+    long long rmax = 0;
+    varlen_table(vl, shared, from, n, moff, &t, &rmax);
+    const seer_shape s = varlen_shape(vl, shared[from]);
+    seer::AttnArgs a = attn_args(&s, q, k, v, 2);
+    a.hs = total;
+    a.out = out;
+    a.lse = lse;
+    a.out_bf16 = out_dtype == SEER_BF16;
+    a.rmax = static_cast<float*>(workspace);
+    a.gt = gt;
+    hipError_t e = seer::launch_attn_varlen(a, t, 2, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SEER_ERR_HIP, "varlen ground-truth launch failed: %s", hipGetErrorString(e));
   }
   return ok();
 }
-
 
 }  // extern "C"

@@ -41,6 +41,24 @@ struct AttnArgs {
 // mode: 0 block-sparse (mask), 1 dense causal, 2 dense causal + ground-truth maxima
 hipError_t launch_attn(const AttnArgs& a, int mode, hipStream_t st);
 
+// Sequences of a packed batch that run in one launch (see attn_varlen_kernel):
+// sequence i has t.len[i] > 0 tokens from packed token t.tok[i], its rows are
+// workgroups row_start[i] .. row_start[i+1]-1 (Hq * nb_i of them), its
+// [Hq, nb_i, nb_i] block map starts at element map_off[i] and its
+// ground-truth scratch at float rmax_off[i].
+constexpr int kVarlenMaxSeqs = 64;
+struct VarlenTable {
+  int n;
+  int row_start[kVarlenMaxSeqs + 1];
+  int tok[kVarlenMaxSeqs];
+  int len[kVarlenMaxSeqs];
+  long long map_off[kVarlenMaxSeqs];
+  long long rmax_off[kVarlenMaxSeqs];
+};
+hipError_t launch_attn_varlen(const AttnArgs& a, const VarlenTable& t, int mode, hipStream_t st);
+// key blocks per sweep chunk on the one-item-per-row block-sparse path (rows up to 1024 blocks)
+int varlen_chunk_blocks();
+
 // Work plan of the block-sparse kernel for one shape: which path, key chunks,
 // item / slot counts and the workspace it needs.
 struct SparsePlan {

@@ -174,3 +174,55 @@ def test_varlen_gate_and_gt():
         err = np.abs(g_h[sl].reshape(HQ, nb, nb) - gt_ref).max()
         say(f"  seq {i}: gt max-abs {err:.3e}")
         assert err <= 1e-6
+
+
+def test_varlen_many_sequences_shared_launches():
+    """70 packed sequences (more than one shared launch of 64; lengths from 0 to
+    ~3k tokens in scrambled order): block-sparse, dense and the 2D map, every
+    sequence bitwise equal to its batch-1 call, and a few against the oracle."""
+    seer = _seer()
+    rng = np.random.default_rng(320)
+    lens = [int(x) for x in rng.integers(1, 3200, size=70)]
+    lens[3] = 0
+    lens[10] = 1
+    lens[11] = 64
+    lens[40] = 65
+    D = 64
+    seqs, qp, kp, vp, cu = _pack(lens, D, 330)
+    say(f"[varlen many] {len(lens)} sequences, {cu[-1]} tokens")
+    masks = [synth.gen_tiny_mask(Shape(1, HQ, HKV, max(n, 1), D), 340 + i, p_keep=0.3).mask[0] if n else
+             np.zeros((HQ, 0, 0), np.uint8) for i, n in enumerate(lens)]
+    flat = np.concatenate([m.reshape(-1) for m in masks])
+    dq, dk, dv = dev_bf16(qp), dev_bf16(kp), dev_bf16(vp)
+    out, lse = seer.seer_block_sparse_attn_varlen_fwd(dq, dk, dv, cu, dev_u8(flat), out_dtype=torch.float32,
+                                                      want_lse=True)
+    outd, lsed = seer.seer_block_sparse_attn_varlen_fwd(dq, dk, dv, cu, None, out_dtype=torch.bfloat16,
+                                                        want_lse=True)
+    og, lg, gt = seer.seer_attn_maxpool_gt_varlen(dq, dk, dv, cu, out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    offs, _ = seer.varlen_map_offsets(cu, HQ)
+    for i, n in enumerate(lens):
+        if n == 0:
+            continue
+        q, k, v = seqs[i]
+        a, b = cu[i], cu[i + 1]
+        nb = (n + 63) // 64
+        q1, k1, v1 = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+        o1, l1 = seer.seer_block_sparse_attn_fwd(q1, k1, v1, dev_u8(masks[i][None]), out_dtype=torch.float32,
+                                                 want_lse=True)
+        od1, ld1 = seer.seer_block_sparse_attn_fwd(q1, k1, v1, None, out_dtype=torch.bfloat16, want_lse=True)
+        og1, lg1, g1 = seer.seer_attn_maxpool_gt(q1, k1, v1, out_dtype=torch.float32, want_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], out[:, a:b]) and torch.equal(l1[0], lse[:, a:b]), f"seq {i} sparse"
+        assert torch.equal(od1[0], outd[:, a:b]) and torch.equal(ld1[0], lsed[:, a:b]), f"seq {i} dense"
+        assert torch.equal(og1[0], og[:, a:b]) and torch.equal(lg1[0], lg[:, a:b]), f"seq {i} gt-kernel O"
+        assert torch.equal(g1.reshape(-1), gt[offs[i]:offs[i] + HQ * nb * nb]), f"seq {i} map"
+        if i % 17 == 0:
+            o_ref, l_ref = oracle.attention(q, k, v, masks[i][None])
+            check_close(host(out[:, a:b])[None], o_ref, f"seq {i} sparse O")
+            check_lse(host(lse[:, a:b])[None], l_ref, f"seq {i} sparse LSE")
+            g_ref = oracle.maxpool_gt(q, k)[0]
+            err = np.abs(host(gt[offs[i]:offs[i] + HQ * nb * nb]).reshape(HQ, nb, nb) - g_ref).max()
+            say(f"  seq {i}: gt max-abs {err:.3e}")
+            assert err <= 1e-6
+    say("  every sequence bitwise equal to its batch-1 call (sparse, dense, map)")
