@@ -518,6 +518,226 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   attn_row<D, MODE>(p, w, qb, bh, chunk);
 }
 
+// ---------------------------------------------------------------------------
+// Dense causal attention (and its ground-truth variant) for GQA groups of a
+// multiple of four query heads: one workgroup = four query heads of one KV
+// group at one query block, 8 wavefronts (head-major, two 32-query halves
+// per head). The four heads read the same K/V tiles, so each tile is copied
+// HBM -> LDS once for 256 queries instead of once per 64, and the LDS that
+// four row-workgroups would use holds a ring of kRing tiles: the copies run
+// kRing - 1 tiles ahead, and one workgroup barrier per tile both publishes
+// the tile every wave copied a part of and frees the slot of the tile before.
+// Each wavefront does exactly what a wavefront of attn_fwd_kernel does for
+// its 32 queries (same tile order, same tile arithmetic), so results are
+// bitwise those of attn_fwd_kernel.
+constexpr int kGqaHeads = 4;                 // query heads per workgroup
+constexpr int kGqaWaves = 2 * kGqaHeads;
+constexpr int kGqaThreads = kGqaWaves * kWave;
+constexpr int kRing = 4;                     // K/V tiles in flight per workgroup
+
+template <int D, int MODE>
+__device__ __forceinline__ void attn_dense_gqa_body(const AttnArgs& p) {
+  static_assert(MODE != kSparse, "dense modes only");
+  constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
+  constexpr int KS = D / 16;
+  constexpr int MT = D / 32;
+  constexpr int RPI = 64 / CPR;              // tile rows per copy instruction
+  constexpr int NCW = (kBlock / kGqaWaves) / RPI;   // copy instructions per wave per operand and tile
+  constexpr int TILE_BYTES = kBlock * CPR * 16;     // one K or V tile
+  static_assert(NCW >= 1 && (kBlock / kGqaWaves) % RPI == 0, "copy split");
+
+  __shared__ uint4 Kr[kRing * kBlock * CPR];
+  __shared__ uint4 Vr[kRing * kBlock * CPR];
+  __shared__ float lse_s[MODE == kDenseGt ? kGqaHeads * kBlock : 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+  const int hloc = wave >> 1;                // head within the workgroup
+  const int q_local = (wave & 1) * 32 + l32; // query row within the block
+
+  // workgroups: (batch, KV group, 4-head quarter) major, query block descending
+  const int quarters = p.group / kGqaHeads;
+  const int per_q = p.nb;
+  const int w = blockIdx.x;
+  const int gq = w / per_q;                  // (b * Hkv + g) * quarters + quarter
+  const int qb = p.nb - 1 - (w - gq * per_q);
+  const int bg = gq / quarters;
+  const int b = bg / p.Hkv;
+  const int g = bg - b * p.Hkv;
+  const int h = g * p.group + (gq - bg * quarters) * kGqaHeads + hloc;
+  const int bh = b * p.Hq + h;
+  const size_t kv_off = (static_cast<size_t>(b) * p.Hkv + g) * p.hs * D;
+  const uint16_t* __restrict__ Kg = p.k + kv_off;
+  const uint16_t* __restrict__ Vg = p.v + kv_off;
+
+  // this wave copies rows 8 wave .. 8 wave + 7 of every tile: instruction i,
+  // lane l moves tile row r = 8 wave + RPI i + l / CPR, physical chunk l % CPR
+  // holding logical chunk (l % CPR) ^ swz(r), to LDS byte 1024 (NCW wave + i) + 16 l
+  uint32_t kofs[NCW], vofs[NCW];
+#pragma unroll
+  for (int i = 0; i < NCW; ++i) {
+    const int r = 8 * wave + RPI * i + lane / CPR;
+    const int pc = lane % CPR;
+    kofs[i] = static_cast<uint32_t>(r * 2 * D + 16 * (pc ^ swz_k<D>(r)));
+    vofs[i] = static_cast<uint32_t>(r * 2 * D + 16 * (pc ^ swz_v<D>(r)));
+  }
+  auto issue = [&](int kb, int slot) {
+    const int key0 = kb * kBlock;
+    const uint32_t bytes = static_cast<uint32_t>((p.S - key0) * 2 * D);
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kg + static_cast<size_t>(key0) * D), 0,
+                                                      bytes, kBufferWord3);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Vg + static_cast<size_t>(key0) * D), 0,
+                                                      bytes, kBufferWord3);
+    char* kd = reinterpret_cast<char*>(Kr) + slot * TILE_BYTES + 1024 * NCW * wave;
+    char* vd = reinterpret_cast<char*>(Vr) + slot * TILE_BYTES + 1024 * NCW * wave;
+#pragma unroll
+    for (int i = 0; i < NCW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kd + 1024 * i), 16, kofs[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NCW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vd + 1024 * i), 16, vofs[i], 0, 0, 0);
+  };
+
+  // operand read addresses in slot 0 (the swizzles of attn_fwd_kernel)
+  uint32_t kaddr0[KS], vaddr0[MT];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    kaddr0[ks] = lds_addr(Kr) + l32 * 2 * D + 16 * ((2 * ks + hl) ^ swz_k<D>(l32));
+  {
+    const int G = lane >> 4, jj = (lane >> 2) & 3, a = lane & 3;
+    const int key = 4 * (G >> 1) + jj;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      vaddr0[mt] = lds_addr(Vr) + key * 2 * D + 16 * ((4 * mt + 2 * (G & 1) + (a >> 1)) ^ swz_v<D>(key)) + 8 * (a & 1);
+  }
+
+  // tiles in the order of attn_fwd_kernel: the diagonal first, then 0 .. qb - 1
+  const int ntiles = qb + 1;
+  auto tile_kb = [&](int t) { return t == 0 ? qb : t - 1; };
+  // Vector-memory operations of this wave, in issue order: the copies of
+  // tiles 0 .. pro-1 (kPerTile each), the KS Q loads, then per tile t: the
+  // copies of tile t + kRing - 1 (while that tile exists) and, for the ground
+  // truth, one store. Before tile t is read the wave waits until at most
+  // issued(t) - after(t) operations are outstanding: issued(t) counts all it
+  // issued before tile t, after(t) those up to and including tile t's copies.
+  constexpr int kPerTile = 2 * NCW;          // copy instructions per wave and tile
+  constexpr int kStore = MODE == kDenseGt ? 1 : 0;
+  const int pro = ntiles < kRing - 1 ? ntiles : kRing - 1;
+  const int late = ntiles - (kRing - 1) > 0 ? ntiles - (kRing - 1) : 0;   // tiles copied inside the loop
+  auto issued_before = [&](int t) { return (pro + (t < late ? t : late)) * kPerTile + KS + t * kStore; };
+  auto through_copies = [&](int t) {
+    if (t < pro) return (t + 1) * kPerTile;
+    const int i = t - (kRing - 1);           // the tile whose step issued these copies
+    return (pro + i + 1) * kPerTile + KS + i * kStore;
+  };
+  for (int t = 0; t < pro; ++t) issue(tile_kb(t), t);
+
+  // Q fragment of this wave's 32 queries
+  const int t_q = qb * kBlock + q_local;
+  const bool t_ok = t_q < p.S;
+  uint4 qreg[KS];
+  {
+    const uint16_t* qrow = p.q + (static_cast<size_t>(bh) * p.hs + (t_ok ? t_q : 0)) * D + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qreg[ks] = t_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * ks) : make_uint4(0, 0, 0, 0);
+  }
+
+  const float c = p.scale_log2;
+  float m = -INFINITY, lsum = 0.f;
+  f32x16_t oacc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) oacc[i] = f32x16_t{};
+  const long long ntri_off = static_cast<long long>(qb) * (qb + 1) / 2;
+
+  auto step = [&](auto diag_tag, int t) {
+    constexpr bool kDiag = decltype(diag_tag)::value;
+    const int slot = t % kRing;
+    const int kb = tile_kb(t);
+    wait_vm_upto(issued_before(t) - through_copies(t));   // this wave's part of tile t landed
+    wg_barrier();                            // every part landed; every wave is done with tile t - 1
+    if (t + kRing - 1 < ntiles) {            // refill the slot of tile t - 1
+      const int tn = t + kRing - 1;
+      issue(tile_kb(tn), tn % kRing);
+    }
+    const uint32_t off = static_cast<uint32_t>(slot * TILE_BYTES);
+    uint32_t kaddr[KS], vaddr[MT];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kaddr[ks] = kaddr0[ks] + off;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) vaddr[mt] = vaddr0[mt] + off;
+    u32x4_t kr[2 * KS];
+    read_k_tile<D>(kaddr, kr);
+    f32x16_t sacc[2];
+    const float mx = tile_scores<D, kDiag>(kr, qreg, sacc, q_local, hl, c);
+    if constexpr (MODE == kDenseGt) {
+      if (hl == 0) p.rmax[((static_cast<size_t>(bh) * p.ntri + ntri_off + kb) << 6) + q_local] = mx;
+    }
+    u32x2_t vr[8 * MT];
+    read_v_tile<D>(vaddr, vr);
+    tile_update<D>(sacc, vr, mx, c, m, lsum, oacc);
+  };
+  step(std::true_type{}, 0);
+  for (int t = 1; t < ntiles; ++t) step(std::false_type{}, t);
+
+  // ---- epilogue: normalize, store O and LSE (as attn_fwd_kernel)
+  const float ltot = pair_sum(lsum);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  const float lse2 = ltot > 0.f ? m + __log2f(ltot) : -INFINITY;
+  if (t_ok) {
+    const size_t obase = (static_cast<size_t>(bh) * p.hs + t_q) * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dim = 32 * mt + 8 * r4 + 4 * hl;
+        const float o0 = oacc[mt][4 * r4 + 0] * inv, o1 = oacc[mt][4 * r4 + 1] * inv;
+        const float o2 = oacc[mt][4 * r4 + 2] * inv, o3 = oacc[mt][4 * r4 + 3] * inv;
+        if (p.out_bf16) {
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + obase + dim) =
+              make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + obase + dim) = make_float4(o0, o1, o2, o3);
+        }
+      }
+    }
+    if (p.lse != nullptr && hl == 0) p.lse[static_cast<size_t>(bh) * p.hs + t_q] = lse2 * kLn2;
+  }
+
+  if constexpr (MODE == kDenseGt) {
+    // gt[qb, kb] = max over the block's queries of exp2(r - lse2) per head; 0 above the diagonal
+    if (hl == 0) lse_s[hloc * kBlock + q_local] = t_ok ? lse2 : INFINITY;
+    __syncthreads();                         // lse_s and the heads' r writes visible to the workgroup
+    const int bh0 = bh - hloc;               // first head of the workgroup
+    for (int e = tid; e < kGqaHeads * p.nb; e += kGqaThreads) {
+      const int hh = e / p.nb, kb = e - hh * p.nb;
+      float best = 0.f;
+      if (kb <= qb) {
+        const float4* rr = reinterpret_cast<const float4*>(
+            p.rmax + ((static_cast<size_t>(bh0 + hh) * p.ntri + ntri_off + kb) << 6));
+        const float* ls = lse_s + hh * kBlock;
+#pragma unroll 4
+        for (int q4 = 0; q4 < 16; ++q4) {
+          const float4 v = rr[q4];
+          best = fmaxf(best, exp2f(v.x - ls[4 * q4 + 0]));
+          best = fmaxf(best, exp2f(v.y - ls[4 * q4 + 1]));
+          best = fmaxf(best, exp2f(v.z - ls[4 * q4 + 2]));
+          best = fmaxf(best, exp2f(v.w - ls[4 * q4 + 3]));
+        }
+      }
+      p.gt[(static_cast<size_t>(bh0 + hh) * p.nb + qb) * p.nb + kb] = best;
+    }
+  }
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(kGqaThreads, 1) void attn_dense_gqa_kernel(AttnArgs p) {
+  attn_dense_gqa_body<D, MODE>(p);
+}
+
 // Packed (varlen) batch in one launch: workgroup w takes a row of the sequence
 // whose row range holds w. Each sequence is the batch-1 problem at its token
 // offset with the packed length as head stride, and every row runs exactly
@@ -656,7 +876,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
   constexpr int MT = D / 32;               // MFMA m-tiles for O^T
   constexpr int RPI = 64 / CPR;            // tile rows per copy instruction
   constexpr int NDMA = 32 / RPI;           // copy instructions per wave per operand
-  constexpr int HALF = D / 2;              // output values per thread
 
   __shared__ uint4 Ks[kBlock * CPR];
   __shared__ uint4 Vs[kBlock * CPR];
@@ -1103,6 +1322,13 @@ hipError_t launch_d(const AttnArgs& a, int mode, hipStream_t st) {
       const dim3 cgrid(static_cast<unsigned>(a.B) * a.Hq * (a.nb - a.chunk));
       hipLaunchKernelGGL((attn_combine_kernel<D>), cgrid, dim3(256), 0, st, a);
     }
+    return hipGetLastError();
+  }
+  if (a.group % kGqaHeads == 0) {
+    // the query heads of a KV group four at a time, sharing K/V tile copies
+    const dim3 grid(static_cast<unsigned>(a.B) * a.Hq / kGqaHeads * a.nb), gblock(kGqaThreads);
+    if (mode == kDense) hipLaunchKernelGGL((attn_dense_gqa_kernel<D, kDense>), grid, gblock, 0, st, a);
+    else hipLaunchKernelGGL((attn_dense_gqa_kernel<D, kDenseGt>), grid, gblock, 0, st, a);
     return hipGetLastError();
   }
   const dim3 grid(static_cast<unsigned>(a.B) * a.Hq * a.nb);

@@ -165,4 +165,27 @@ __device__ __forceinline__ void wait_vm(int n) {
   }
 }
 
+// s_waitcnt vmcnt(n) for 0 <= n: counts up to 15 have their own instruction,
+// larger ones wait until 15 remain (more than needed, always safe)
+__device__ __forceinline__ void wait_vm_upto(int n) {
+  switch (n) {
+    case 0: wait_vm_le<0>(); break;
+    case 1: wait_vm_le<1>(); break;
+    case 2: wait_vm_le<2>(); break;
+    case 3: wait_vm_le<3>(); break;
+    case 4: wait_vm_le<4>(); break;
+    case 5: wait_vm_le<5>(); break;
+    case 6: wait_vm_le<6>(); break;
+    case 7: wait_vm_le<7>(); break;
+    case 8: wait_vm_le<8>(); break;
+    case 9: wait_vm_le<9>(); break;
+    case 10: wait_vm_le<10>(); break;
+    case 11: wait_vm_le<11>(); break;
+    case 12: wait_vm_le<12>(); break;
+    case 13: wait_vm_le<13>(); break;
+    case 14: wait_vm_le<14>(); break;
+    default: wait_vm_le<15>(); break;
+  }
+}
+
 }  // namespace seer
