@@ -808,8 +808,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_varlen_kernel(AttnArgs p, Va
 // per-XCD counter, so the items resident on an XCD stay a contiguous window of
 // its sequence (a fixed stride per workgroup lets them drift over several
 // chunks). Nothing drains between items: item indices are fetched two items
-// ahead, the next item's mask flags one item ahead, and its Q rows and first
-// K/V tile are issued during the current item's last tile. An item of a row
+// ahead, the next item's mask flags one item ahead, and its Q rows and the K
+// of its first tile are issued during the current item's last tile. An item of a row
 // that spans several chunks writes a bf16 partial output (normalized by its
 // own sum) and its log2-sum-exp; attn_xcd_combine_kernel merges them. Rows
 // inside the first chunk are one item and are written directly.
@@ -828,38 +828,57 @@ __device__ __forceinline__ int xcd_job(int x, int t, int njobs) {
 }
 
 struct XcdItem {
-  int bh;      // batch * Hq + head; -1: past the end of the sequence
-  int qb;      // query block
-  int c;       // key chunk
+  int bh;          // batch * Hq + head; -1: past the end of the sequence
+  int qb;          // query block
+  int c;           // key chunk
+  long long kvo;   // element offset of the item's K/V head
 };
 
-// Walks one XCD's item sequence; queried with increasing item indices (the
-// host keeps every index within 32 bits).
+// Walks one XCD's item sequence; queried with non-decreasing item indices
+// (the host keeps every index within 32 bits). What depends only on the job
+// is computed once, when the walk enters the job; within a job the head
+// advances incrementally, so an item costs no integer division (the scalar
+// arithmetic of an item start issues at one instruction per four cycles).
 struct XcdCursor {
-  int t = 0;
+  int t = 0;               // position in the XCD's job sequence
   int job = -1;
   int begin = 0;           // sequence index of the job's first item
   int count = 0;           // items in the job
+  int c = 0;               // the job's key chunk
+  int rows = 0;            // query blocks per head that reach the chunk
+  int bh0 = 0;             // batch * Hq + first query head of the job's KV group
+  int hig = 0;             // head within the group of the last item returned
+  int hbase = 0;           // job-relative index of that head's first item
+  long long kvo = 0;       // element offset of the job's K/V head
 };
 
+template <int D>
 __device__ __forceinline__ XcdItem xcd_item(const AttnArgs& p, int x, int j, XcdCursor& cur) {
   while (true) {
     if (cur.job < 0) {
       cur.job = xcd_job(x, cur.t, p.njobs);
-      if (cur.job < 0) return XcdItem{-1, 0, 0};
-      cur.count = p.group * (p.nb - (cur.job % p.nchunk) * p.chunk);
+      if (cur.job < 0) return XcdItem{-1, 0, 0, 0};
+      cur.c = cur.job % p.nchunk;
+      const int gi = cur.job / p.nchunk;
+      const int bb = gi / p.Hkv, gg = gi - bb * p.Hkv;
+      cur.rows = p.nb - cur.c * kXcdDefaultChunk;
+      cur.count = p.group * cur.rows;
+      cur.bh0 = bb * p.Hq + gg * p.group;
+      cur.kvo = (static_cast<long long>(bb) * p.Hkv + gg) * p.hs * D;
+      cur.hig = 0;
+      cur.hbase = 0;
     }
     if (j < cur.begin + cur.count) break;
     cur.begin += cur.count;
     ++cur.t;
     cur.job = -1;
   }
-  const int c = cur.job % p.nchunk, gi = cur.job / p.nchunk;
-  const int rows = p.nb - c * p.chunk;
   const int mi = j - cur.begin;
-  const int hig = mi / rows;
-  const int bb = gi / p.Hkv, gg = gi - bb * p.Hkv;
-  return XcdItem{bb * p.Hq + gg * p.group + hig, p.nb - 1 - (mi - hig * rows), c};
+  while (mi >= cur.hbase + cur.rows) {
+    cur.hbase += cur.rows;
+    ++cur.hig;
+  }
+  return XcdItem{cur.bh0 + cur.hig, p.nb - 1 - (mi - cur.hbase), cur.c, cur.kvo};
 }
 
 // Partial-output slots before query block qb of one head: rows qb' >= C own
@@ -937,19 +956,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
       vaddr[mt] = lds_addr(Vs) + key * 2 * D + 16 * ((4 * mt + 2 * (G & 1) + (a >> 1)) ^ swz_v<D>(key)) + 8 * (a & 1);
   }
 
-  auto kv_head = [&](const XcdItem& it) -> size_t {
-    const int b = it.bh / p.Hq;
-    const int g = (it.bh - b * p.Hq) / p.group;
-    return (static_cast<size_t>(b) * p.Hkv + g) * p.hs * D;
-  };
   // this lane's mask bytes of an item's chunk: keys c0 + lane and c0 + 64 +
   // lane (0 past the causal end, the diagonal included)
   auto load_flags = [&](const XcdItem& it, uint32_t& f0, uint32_t& f1) {
     f0 = 0;
     f1 = 0;
     if (it.bh < 0) return;
-    const int c0 = it.c * p.chunk;
-    const int kend = min(it.qb + 1, c0 + p.chunk);
+    const int c0 = it.c * kXcdDefaultChunk;
+    const int kend = min(it.qb + 1, c0 + kXcdDefaultChunk);
     const uint8_t* mrow = p.mask + (static_cast<size_t>(it.bh) * p.nb + it.qb) * p.nb;
     if (c0 + lane < kend) f0 = mrow[c0 + lane];
     if (c0 + 64 + lane < kend) f1 = mrow[c0 + 64 + lane];
@@ -964,9 +978,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
   };
   // first tile of an item: the diagonal if it is active, else the lowest active block
   auto first_tile = [&](const XcdItem& it, uint64_t f0, uint64_t f1) -> int {
-    const int c0 = it.c * p.chunk;
+    const int c0 = it.c * kXcdDefaultChunk;
     const int d = it.qb - c0;
-    if (d < p.chunk && ((d < 64 ? (f0 >> d) : (f1 >> (d - 64))) & 1)) return it.qb;
+    if (d < kXcdDefaultChunk && ((d < 64 ? (f0 >> d) : (f1 >> (d - 64))) & 1)) return it.qb;
     if (f0) return c0 + static_cast<int>(__builtin_ctzll(f0));
     if (f1) return c0 + 64 + static_cast<int>(__builtin_ctzll(f1));
     return -1;
@@ -994,9 +1008,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
   __syncthreads();
   const int j0 = claim;
   XcdCursor cur;
-  XcdItem it = xcd_item(p, x, j0, cur);            // this item
+  XcdItem it = xcd_item<D>(p, x, j0, cur);            // this item
   if (it.bh < 0) return;
-  XcdItem it1 = xcd_item(p, x, j0 + 1, cur);       // the next one
+  XcdItem it1 = xcd_item<D>(p, x, j0 + 1, cur);       // the next one
   int j2 = j0 + 2;                                 // the one after
   int pend = 0;                                    // wave 0 lane 0: claim in flight (the item after j2)
   bool claimed = false;
@@ -1008,26 +1022,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
 #pragma unroll
   for (int i = 0; i < MT; ++i) oacc[i] = f32x16_t{};
 
-  // One tile; its copies were issued before. `tile0`: the item's first tile,
-  // whose copies (and everything else issued earlier) have landed. `nkv`:
-  // offset of the K/V head of the next tile `next` (-1: none). `qn`: load the
-  // next item's Q rows into qreg once this tile's scores are computed.
-  auto compute = [&](bool diag, bool tile0, size_t nkv, int next, bool qn) {
-    if (!tile0) wait_vm(NDMA);                     // this tile's K landed (its V may be in flight)
+  // One tile kb_t of the K/V head at kvo_t; its K copies were issued before.
+  // Two workgroup barriers per tile: the one that publishes K(t) also frees
+  // the V buffer (both waves have read V(t-1)), so V(t) is copied from there
+  // on; the one that publishes V(t) frees the K buffer, so the next tile's K
+  // (`next` of the head at `nkv`; -1: none) is copied from there on. Each
+  // batch of copies is issued while the wave's operand reads from LDS are in
+  // flight, which hides the time the copy instructions take to issue. `qn`:
+  // load the next item's Q rows into qreg once this tile's scores are issued.
+  auto compute = [&](bool diag, size_t kvo_t, int kb_t, size_t nkv, int next, bool qn) {
+    wait_vm(0);                                    // this tile's K landed (and everything before it)
     wg_barrier();
     u32x4_t kr[2 * KS];
-    read_k_tile<D>(kaddr, kr);
-    wg_barrier();                                  // both waves hold K: refill the K buffer
-    if (next >= 0) issue_k(p.k + nkv, next);
+    read_k_issue<D>(kaddr, kr);
+    issue_v(p.v + kvo_t, kb_t);
+    read_k_wait<D>(kr);
     f32x16_t sacc[2];
     const float mx = tile_scores_rt<D>(kr, qreg, sacc, q_local, hl, c, diag);
     if (qn) load_q(it1, qreg);                     // qreg is free once the scores are issued
-    if (!tile0) wait_vm((next >= 0 ? NDMA : 0) + (qn ? KS : 0));   // this tile's V landed
+    wait_vm(qn ? KS : 0);                          // this tile's V landed
     wg_barrier();
     u32x2_t vr[8 * MT];
-    read_v_tile<D>(vaddr, vr);
-    wg_barrier();                                  // both waves hold V: refill the V buffer
-    if (next >= 0) issue_v(p.v + nkv, next);
+    read_v_issue<D>(vaddr, vr);
+    if (next >= 0) issue_k(p.k + nkv, next);
+    read_v_wait<D>(vr);
     tile_update<D>(sacc, vr, mx, c, m, lsum, oacc);
   };
 
@@ -1041,8 +1059,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
 
   while (true) {
     // ---- item start ------------------------------------------------------
-    const int c0 = it.c * p.chunk;
-    const size_t kvo = kv_head(it);
+    const int c0 = it.c * kXcdDefaultChunk;
+    const size_t kvo = static_cast<size_t>(it.kvo);
     int kb = first_tile(it, f0, f1);
     if (kb >= 0) {
       const int d = kb - c0;
@@ -1051,10 +1069,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
     }
     if (!warm) {
       load_q(it, qreg);
-      if (kb >= 0) {
-        issue_k(p.k + kvo, kb);
-        issue_v(p.v + kvo, kb);
-      }
+      if (kb >= 0) issue_k(p.k + kvo, kb);
     }
     wait_vm(0);                                    // everything issued so far has landed
     const uint64_t g0 = __builtin_amdgcn_ballot_w64(fb0 != 0), g1 = __builtin_amdgcn_ballot_w64(fb1 != 0);
@@ -1066,50 +1081,60 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       wg_barrier();                                // both waves hold it before the LDS word is reused
     }
-    const XcdItem it2 = xcd_item(p, x, j2, cur);
+    const XcdItem it2 = xcd_item<D>(p, x, j2, cur);
     load_flags(it2, fb0, fb1);                     // the item after next; read at the next item's start
     claimed = it2.bh >= 0;
-    if (claimed && tid == 0) pend = atomicAdd(ctr, 1);
+    if (claimed && tid == 0) {
+      // an address the compiler cannot prove uniform: a uniform one makes it
+      // read the result back at once (a wait for the atomic's round trip
+      // here); this way the result is waited for only where it is used
+      int off = 0;
+      asm volatile("" : "+v"(off));
+      pend = atomicAdd(ctr + off, 1);
+    }
     const int kb1 = it1.bh >= 0 ? first_tile(it1, g0, g1) : -1;
-    const size_t kvo1 = it1.bh >= 0 ? kv_head(it1) : 0;
+    const size_t kvo1 = static_cast<size_t>(it1.kvo);
 
     // ---- tiles: the diagonal first, then ascending; the last one hands over
     // to the next item (its first tile's copies and its Q rows)
     warm = false;
     if (kb >= 0) {
-      bool tile0 = true;
       bool diag = kb == it.qb;
+      int cur_kb = kb;
       int next = pop_flag(f0, f1, c0);
       while (next >= 0) {
-        compute(diag, tile0, kvo, next, false);
-        tile0 = false;
+        compute(diag, kvo, cur_kb, kvo, next, false);
         diag = false;
+        cur_kb = next;
         next = pop_flag(f0, f1, c0);
       }
       warm = it1.bh >= 0;
-      compute(diag, tile0, warm ? kvo1 : kvo, warm ? kb1 : -1, warm);
+      compute(diag, kvo, cur_kb, warm ? kvo1 : kvo, warm ? kb1 : -1, warm);
     }
 
     // ---- epilogue ----------------------------------------------------------
     const float ltot = pair_sum(lsum);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     const float lse2 = ltot > 0.f ? m + __log2f(ltot) : -INFINITY;
-    if (it.qb >= p.chunk) {
+    if (it.qb >= kXcdDefaultChunk) {
       // normalized bf16 partial: the thread's 8-value group g (oacc[g / 2]
       // values 8 (g % 2) ..) is 16 bytes at uint4 index g * kThreads + tid of
-      // the slot, so each store instruction writes 1 KiB contiguous
+      // the slot, so each store instruction writes 1 KiB contiguous. The
+      // stores are non-temporal: the partials are read once, by the merge, and
+      // would otherwise push the chunk's K/V out of the XCD's L2
       const long long slot = static_cast<long long>(it.bh) * p.slots_per_head +
-                             xcd_slot_base(it.qb, p.chunk) + it.c;
+                             xcd_slot_base(it.qb, kXcdDefaultChunk) + it.c;
       uint4* po = reinterpret_cast<uint4*>(p.part_o16 + slot * kBlock * D) + tid;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
-          po[(2 * mt + h2) * kThreads] =
-              make_uint4(pack_bf16x2(oacc[mt][8 * h2 + 0] * inv, oacc[mt][8 * h2 + 1] * inv),
-                         pack_bf16x2(oacc[mt][8 * h2 + 2] * inv, oacc[mt][8 * h2 + 3] * inv),
-                         pack_bf16x2(oacc[mt][8 * h2 + 4] * inv, oacc[mt][8 * h2 + 5] * inv),
-                         pack_bf16x2(oacc[mt][8 * h2 + 6] * inv, oacc[mt][8 * h2 + 7] * inv));
+          __builtin_nontemporal_store(
+              u32x4_t{pack_bf16x2(oacc[mt][8 * h2 + 0] * inv, oacc[mt][8 * h2 + 1] * inv),
+                      pack_bf16x2(oacc[mt][8 * h2 + 2] * inv, oacc[mt][8 * h2 + 3] * inv),
+                      pack_bf16x2(oacc[mt][8 * h2 + 4] * inv, oacc[mt][8 * h2 + 5] * inv),
+                      pack_bf16x2(oacc[mt][8 * h2 + 6] * inv, oacc[mt][8 * h2 + 7] * inv)},
+              reinterpret_cast<u32x4_t*>(po + (2 * mt + h2) * kThreads));
       if (hl == 0) p.part_l[slot * kBlock + q_local] = lse2;
     } else {
       const int t = it.qb * kBlock + q_local;
@@ -1359,7 +1384,7 @@ SparsePlan sparse_plan(int B, int Hkv, int group, int nb, int D) {
   const long long jobs = static_cast<long long>(B) * Hkv * nch;
   pl.xcd = nb >= kXcdMinBlocks && jobs >= 64;
   if (pl.xcd) {
-    pl.chunk = C;
+    pl.chunk = C;                                  // attn_sparse_xcd_kernel assumes this chunk size
     pl.nchunk = static_cast<int>(nch);
     pl.njobs = static_cast<int>(jobs);
     pl.slots_per_head = xcd_slot_base(nb, C);
