@@ -254,12 +254,10 @@ __device__ __forceinline__ void attn_row(const AttnArgs& p, const int w, const i
       vaddr[mt] = lds_addr(Vs) + key * 2 * D + 16 * ((4 * mt + 2 * (G & 1) + (a >> 1)) ^ swz_v<D>(key)) + 8 * (a & 1);
   }
 
-  // the diagonal tile is processed first; start its copy before anything else
-  // (in block-sparse mode only the item whose chunk holds the diagonal has it)
-  if (MODE != kSparse || qb < (chunk + 1) * p.chunk) {
-    issue_k(qb);
-    issue_v(qb);
-  }
+  // the diagonal tile is processed first; start its K copy before anything
+  // else (in block-sparse mode only the item whose chunk holds the diagonal
+  // has it)
+  if (MODE != kSparse || qb < (chunk + 1) * p.chunk) issue_k(qb);
 
   // ---- Q fragment (B operand of S^T = K Q^T), resident for the row ------
   const int q_local = wave * 32 + l32;            // query row within the block
@@ -282,36 +280,35 @@ __device__ __forceinline__ void attn_row(const AttnArgs& p, const int w, const i
 
   const long long ntri_off = static_cast<long long>(qb) * (qb + 1) / 2;  // ground-truth scratch offset of this row
 
-  // One tile. On entry the copies of tile kb are in flight or landed, K issued
-  // before V. `first`: nothing but this tile's V copy was issued after its K
-  // copy. `stores_pending`: ground-truth stores issued after the last V copy.
-  int stores_pending = 0;
-  auto compute = [&](auto diag_tag, int kb, int next, bool first) {
+  // One tile kb. On entry its K copy is in flight or landed and its V copy is
+  // not issued yet. Two workgroup barriers per tile: the one that publishes
+  // K(kb) also frees the V buffer (both waves have read the previous tile's
+  // V), so V(kb) is copied from there on; the one that publishes V(kb) frees
+  // the K buffer, so K(next) is copied from there on. Each batch of copies is
+  // issued while the wave's operand reads from LDS are in flight. Both waits
+  // are for everything outstanding: the ground-truth row-max store of a tile
+  // is issued after the second one, so the next tile's first wait covers it.
+  auto compute = [&](auto diag_tag, int kb, int next) {
     constexpr bool kDiag = decltype(diag_tag)::value;   // the diagonal tile needs element causality
-    // ---- K: wait for the copy (only V of this tile and newer stores may be outstanding)
-    wait_vm(first ? NDMA : NDMA + stores_pending);
+    wait_vm(0);                                    // K(kb) landed, and every copy and store before it
     wg_barrier();
     u32x4_t kr[2 * KS];                           // kr[2 ks + mt]: keys 32 mt + l32, dims 16 ks + 8 hl ..
-    read_k_tile<D>(kaddr, kr);
-    wg_barrier();                                  // both waves hold K: refill the K buffer
-    if (next >= 0) issue_k(next);
+    read_k_issue<D>(kaddr, kr);
+    issue_v(kb);
+    read_k_wait<D>(kr);
 
     f32x16_t sacc[2];
-    float mx = tile_scores<D, kDiag>(kr, qreg, sacc, q_local, hl, c);
-    int stores_now = 0;
+    const float mx = tile_scores<D, kDiag>(kr, qreg, sacc, q_local, hl, c);
+
+    wait_vm(0);                                    // V(kb) landed
+    wg_barrier();
     if constexpr (MODE == kDenseGt) {
       if (hl == 0) p.rmax[((static_cast<size_t>(bh) * p.ntri + ntri_off + kb) << 6) + q_local] = mx;
-      stores_now = 1;
     }
-
-    // ---- V: wait for the copy (the K copy of `next` and this tile's store may be newer)
-    wait_vm((next >= 0 ? NDMA : 0) + stores_now);
-    wg_barrier();
     u32x2_t vr[8 * MT];                            // vr[(ks MT + mt) 2 + u]: dims 32 mt + .., keys 16 ks + 8 u + ..
-    read_v_tile<D>(vaddr, vr);
-    wg_barrier();                                  // both waves hold V: refill the V buffer
-    if (next >= 0) issue_v(next);
-    stores_pending = stores_now;
+    read_v_issue<D>(vaddr, vr);
+    if (next >= 0) issue_k(next);
+    read_v_wait<D>(vr);
 
     tile_update<D>(sacc, vr, mx, c, m, lsum, oacc);
   };
@@ -382,7 +379,7 @@ __device__ __forceinline__ void attn_row(const AttnArgs& p, const int w, const i
     bool issued = false;                        // the sweep's first tile already in flight
     if (diag_on) {
       const int nxt = cnt > 0 ? entry(0) : -1;
-      compute(std::true_type{}, qb, nxt, true);
+      compute(std::true_type{}, qb, nxt);
       issued = cnt > 0;
     } else if (has_diag) {
       wait_vm(0);                            // the early copy of the diagonal tile is not used
@@ -390,18 +387,16 @@ __device__ __forceinline__ void attn_row(const AttnArgs& p, const int w, const i
     }
     if (cnt > 0) {
       int kb = entry(0);
-      bool first = !issued;
-      if (!issued) { issue_k(kb); issue_v(kb); }
+      if (!issued) issue_k(kb);
       for (int n = 0; n < cnt; ++n) {
         const int next = n + 1 < cnt ? entry(n + 1) : -1;
-        compute(std::false_type{}, kb, next, first);
-        first = false;
+        compute(std::false_type{}, kb, next);
         kb = next;
       }
     }
   } else {
-    compute(std::true_type{}, qb, qb > 0 ? 0 : -1, true);
-    for (int kb = 0; kb < qb; ++kb) compute(std::false_type{}, kb, kb + 1 < qb ? kb + 1 : -1, false);
+    compute(std::true_type{}, qb, qb > 0 ? 0 : -1);
+    for (int kb = 0; kb < qb; ++kb) compute(std::false_type{}, kb, kb + 1 < qb ? kb + 1 : -1);
   }
 
   // ---- epilogue: normalize, store O and LSE --------------------------------

@@ -1,12 +1,12 @@
-"""The persistent block-sparse kernel issues its LDS operand reads in one
-inline-asm block and waits for them in a second one, with the tile copies in
+"""The prefill attention kernels issue their LDS operand reads in one
+inline-asm block and wait for them in a second one, with the tile copies in
 between (tile_ops.h: read_k_issue / read_k_wait, read_v_issue / read_v_wait).
 That is correct only while no instruction between the two blocks reads or
 writes a destination register of the reads: such an instruction would see the
 register before the LDS data has arrived. The compiler schedules other
 independent work into that gap, so this test compiles attn_kernels.hip to
 gfx950 assembly with the library's own flags (cross-compiled, no GPU) and checks
-every split read of every instantiation of the kernel.
+every split read of every kernel instantiation.
 """
 import os
 import re
@@ -54,27 +54,35 @@ def kernel_asm(tmp_path_factory):
     return out.read_text()
 
 
+def _check_kernel(name, kernel_asm):
+    """Number of split reads in kernel `name`; fails on a violation."""
+    body = kernel_asm[kernel_asm.index(name + ":"):]
+    lines = body[:body.index("s_endpgm")].split("\n")
+    blocks = list(_asm_blocks(lines))
+    splits = 0
+    for n, (start, end, text) in enumerate(blocks):
+        reads = [t for t in text if t.startswith("ds_read")]
+        if not reads or any(t.startswith("s_waitcnt") for t in text):
+            continue
+        splits += 1
+        dst = set()
+        for t in reads:
+            dst |= _vregs(t.split(",")[0])
+        nxt_start, _, nxt_text = blocks[n + 1]
+        assert nxt_text == ["s_waitcnt lgkmcnt(0)"], (name, nxt_text)
+        for ln in lines[end + 1:nxt_start]:
+            ins = ln.split(";")[0].strip()
+            if ins and not ins.endswith(":"):
+                assert not (_vregs(ins) & dst), f"{name}: '{ins}' touches a register the LDS reads are filling"
+    return splits
+
+
 def test_no_instruction_touches_a_split_read_destination(kernel_asm):
-    names = re.findall(r"^(_ZN4seer\S*attn_sparse_xcd_kernel\S*):", kernel_asm, re.M)
-    assert len(names) == 2, names                       # D = 64 and D = 128
+    names = re.findall(r"^(_ZN4seer\S*(?:attn_sparse_xcd_kernel|attn_fwd_kernel|attn_varlen_kernel)\S*):",
+                       kernel_asm, re.M)
+    # D = 64 and 128; the row kernels in block-sparse, dense and ground-truth mode
+    assert len(names) == 2 + 6 + 6, names
     for name in names:
-        body = kernel_asm[kernel_asm.index(name + ":"):]
-        lines = body[:body.index("s_endpgm")].split("\n")
-        blocks = list(_asm_blocks(lines))
-        splits = 0
-        for n, (start, end, text) in enumerate(blocks):
-            reads = [t for t in text if t.startswith("ds_read")]
-            if not reads or any(t.startswith("s_waitcnt") for t in text):
-                continue
-            splits += 1
-            dst = set()
-            for t in reads:
-                dst |= _vregs(t.split(",")[0])
-            nxt_start, _, nxt_text = blocks[n + 1]
-            assert nxt_text == ["s_waitcnt lgkmcnt(0)"], (name, nxt_text)
-            for ln in lines[end + 1:nxt_start]:
-                ins = ln.split(";")[0].strip()
-                if ins and not ins.endswith(":"):
-                    assert not (_vregs(ins) & dst), f"{name}: '{ins}' touches a register the LDS reads are filling"
-        # K and V reads of the two inlined tile bodies (the loop and an item's last tile)
-        assert splits == 4, (name, splits)
+        # every kernel reads K and V of at least two inlined tile bodies (the
+        # diagonal tile and the others) through the split form
+        assert _check_kernel(name, kernel_asm) >= 4, name
