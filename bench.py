@@ -375,8 +375,10 @@ def main():
     wq, wk = torch.from_numpy(wq_np).to(dev), torch.from_numpy(wk_np).to(dev)
     out = torch.empty((B, Hq, S, D), dtype=torch.bfloat16, device=dev)
     gate_mask = torch.empty((B, Hq, nb, nb), dtype=torch.uint8, device=dev)
-    gate_scores = torch.empty((B, Hq, nb, nb), dtype=torch.float32, device=dev)
-    gate_ws = torch.empty(seer.gate_workspace_bytes(B, Hq, Hkv, S, D, dg), dtype=torch.uint8, device=dev)
+    # the step's gate call produces the block mask the attention consumes; the
+    # fp32 scores are not stored (the distillation step recomputes them)
+    gate_ws = torch.empty(seer.gate_workspace_bytes(B, Hq, Hkv, S, D, dg, want_scores=False), dtype=torch.uint8,
+                          device=dev)
     k_gate = None if gate_made else topk_for_sparsity(nb, 0.9)
     mask = gate_mask if gate_made else torch.from_numpy(mask_np).to(dev)
 
@@ -384,11 +386,11 @@ def main():
 
     def gate():
         if gate_made:
-            seer.seer_gate_fwd(q, k, wq, wk, mode="threshold", threshold=w["threshold"], scores=gate_scores,
+            seer.seer_gate_fwd(q, k, wq, wk, mode="threshold", threshold=w["threshold"], want_scores=False,
                                block_mask=gate_mask, workspace=gate_ws)
         else:
             seer.seer_gate_fwd(q, k, wq, wk, mode="topk", topk=k_gate, rope_theta=rope_theta,
-                               scores=gate_scores, block_mask=gate_mask, workspace=gate_ws)
+                               want_scores=False, block_mask=gate_mask, workspace=gate_ws)
 
     attn_ws = torch.empty(max(seer.attn_workspace_bytes(B, Hq, Hkv, S, D), 16), dtype=torch.uint8, device=dev)
 
@@ -509,9 +511,9 @@ def main():
     s_real = 1.0 - tiles / causal_tiles
     achieved = sparse_flop / attn_avg / 1e9                     # TFLOP/s of the attention kernel
     peak = computed_peak()
-    # the gate call's compulsory HBM bytes: Q and K read once (bf16), the
-    # fp32 scores and the u8 mask written once
-    gate_bytes = 2 * B * S * D * (Hq + Hkv) + B * Hq * nb * nb * (4 + 1)
+    # the gate call's compulsory HBM bytes: Q and K read once (bf16) and the
+    # u8 mask written once
+    gate_bytes = 2 * B * S * D * (Hq + Hkv) + B * Hq * nb * nb
     rec = {
         "metric": METRIC,
         "value": round(sparse_flop / ms_step / 1e9, 3),
@@ -559,7 +561,8 @@ def main():
                      "attention_ms_min": round(float(np.min(attn_ms)), 4),
                      "frac_of_computed_peak": None if peak is None else round(achieved / peak["bf16_tflops"], 4),
                      "counters": measured_mfma_busy(args.workload)},
-        "gate": {"kernel": "seer_gate_fwd (pool, projections, block RoPE, causal logits, softmax + top-k mask)",
+        "gate": {"kernel": "seer_gate_fwd (pool, projections, block RoPE, causal logits, softmax + top-k mask; "
+                           "mask only, scores not stored)",
                  "ms": round(gate_avg, 4), "bound": "hbm",
                  "compulsory_bytes": gate_bytes,
                  "achieved": round(gate_bytes / gate_avg / 1e6, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -421,8 +421,8 @@ __global__ __launch_bounds__(kST) void gate_softmax_mask_kernel(GateArgs a, Topk
   float* srow = a.scores + (static_cast<size_t>(z) * a.nb + i) * a.nb;
   for (int j = threadIdx.x; j < n; j += kST) row[j] = srow[j];
   __syncthreads();
-  softmax_mask_row(row, srow, a.mask + (static_cast<size_t>(z) * a.nb + i) * a.nb, n, a.nb, a.mode, a.threshold,
-                   tk.k[z % a.Hq]);
+  softmax_mask_row(row, a.skip_scores ? nullptr : srow, a.mask + (static_cast<size_t>(z) * a.nb + i) * a.nb, n,
+                   a.nb, a.mode, a.threshold, tk.k[z % a.Hq]);
 }
 
 // This wave's LDS accesses so far have completed, and the compiler moves no
@@ -457,10 +457,11 @@ __device__ __forceinline__ int wave_sum_int(int x) {
 // The row's first n of nb entries are its logits (the rest are written as
 // probability 0 and mask 0); k is its top-k count (mode 1); hist is this
 // wavefront's 256-word LDS histogram. vec: the row's scores may be accessed
-// as 16-byte groups and its mask bytes as 4-byte groups.
+// as 16-byte groups and its mask bytes as 4-byte groups. store: write the
+// probabilities back over the logits (else only the mask is written).
 template <int G>
 __device__ __forceinline__ void wave_softmax_mask_row(float* srow, uint8_t* mrow, int n, int nb, int mode,
-                                                      float threshold, int k, bool vec, uint32_t* hist) {
+                                                      float threshold, int k, bool vec, bool store, uint32_t* hist) {
   const int lane = threadIdx.x & 63;
   // 256-entry groups that hold causal entries (wave-uniform): the later ones
   // hold only -0.0 keys, which no count, histogram or maximum below can see,
@@ -507,6 +508,7 @@ __device__ __forceinline__ void wave_softmax_mask_row(float* srow, uint8_t* mrow
   for (int t = 0; t < G; ++t) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) key[t][e] = __float_as_uint(v[t][e] * inv);
+    if (!store) continue;
     const int j0 = 256 * t + 4 * lane;
     const float p0 = __uint_as_float(key[t][0] & 0x7fffffffu), p1 = __uint_as_float(key[t][1] & 0x7fffffffu);
     const float p2 = __uint_as_float(key[t][2] & 0x7fffffffu), p3 = __uint_as_float(key[t][3] & 0x7fffffffu);
@@ -655,7 +657,7 @@ __global__ __launch_bounds__(256) void gate_softmax_mask_wave_kernel(GateArgs a,
   const bool vec = (a.nb & 3) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(a.mask) & 3) == 0;
   wave_softmax_mask_row<G>(a.scores + static_cast<size_t>(row) * a.nb, a.mask + static_cast<size_t>(row) * a.nb,
-                           i + 1, a.nb, a.mode, a.threshold, tk.k[z % a.Hq], vec, hist_all[wave]);
+                           i + 1, a.nb, a.mode, a.threshold, tk.k[z % a.Hq], vec, !a.skip_scores, hist_all[wave]);
 }
 
 

@@ -296,6 +296,7 @@ static seer_status gate_impl(const seer_shape* shape, long long hs, int32_t gate
   a.kg = reinterpret_cast<float*>(ws + L.kg);
   a.scores = scores ? scores : reinterpret_cast<float*>(ws + L.scores);
   a.mask = block_mask;
+  a.skip_scores = scores == nullptr;
   a.B = shape->batch;
   a.Hq = shape->heads_q;
   a.Hkv = shape->heads_kv;

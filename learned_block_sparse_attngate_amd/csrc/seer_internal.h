@@ -83,6 +83,7 @@ struct GateArgs {
   float* kg;           // [B,Hwk,nb,Dg]
   float* scores;       // [B,Hq,nb,nb] (caller's output or workspace)
   uint8_t* mask;       // [B,Hq,nb,nb]
+  int skip_scores;     // 1: the caller wants only the mask; the probabilities are not written back
   int B, Hq, Hkv, S, D, nb, Dg, group;
   long long hs;        // tokens between consecutive heads' rows of q/k (S; the packed length for varlen)
   int wk_per_kv;       // 1: Hwk = Hkv, 0: Hwk = Hq

@@ -159,6 +159,25 @@ def test_gate_long_rows_match_oracle(name, nb, topk):
     _check_threshold_mask(mask_t.cpu().numpy(), sc_ref, T, f"T={T:.3e}")
 
 
+@pytest.mark.parametrize("mode", ["topk", "threshold"])
+@pytest.mark.parametrize("nb", [300, 2100, 4100], ids=["nb300", "nb2100", "nb4100"])
+def test_gate_mask_only_equals_mask_with_scores(nb, mode):
+    """Without a scores output the probabilities are not written back; the
+    mask must be the same bits (a wavefront per row up to 4096 blocks, a
+    workgroup per row past that)."""
+    seer = _seer()
+    shape = Shape(1, 2, 1, 64 * nb - 5, 64)
+    say(f"[gate mask only {mode}] shape={shape}")
+    q, k, wq, wk = (dev_bf16(x) if i < 2 else dev_f32(x) for i, x in enumerate(_gate_inputs(shape, 71, 64)))
+    kw = dict(mode="topk", topk=[nb // 10, 3]) if mode == "topk" else dict(mode="threshold", threshold=1.5 / nb)
+    m0, s0 = seer.seer_gate_fwd(q, k, wq, wk, **kw)
+    m1, s1 = seer.seer_gate_fwd(q, k, wq, wk, want_scores=False, **kw)
+    torch.cuda.synchronize()
+    assert s1 is None and s0 is not None
+    say(f"  {int(m0.sum())} active blocks")
+    assert torch.equal(m0, m1)
+
+
 @pytest.mark.parametrize("nb", [517, 1101], ids=["nb517", "nb1101"])
 def test_gate_flat_long_rows_keep_lowest_indices(nb):
     """W_q = 0: every causal score of row i is 1/(i+1), so top-k keeps blocks
