@@ -42,10 +42,10 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_s128k_90")
-    ap.add_argument("--dense-reps", type=int, default=2)
+    ap.add_argument("--dense-reps", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -418,10 +418,13 @@ def main():
         mask_np = gate_mask.cpu().numpy()
 
     tiles = int(np.count_nonzero(np.tril(np.ones((nb, nb), dtype=bool)) & mask_np.astype(bool)))
+    diag_tiles = int(np.count_nonzero(np.diagonal(mask_np, axis1=2, axis2=3)))
     causal_tiles = B * Hq * nb * (nb + 1) // 2
     flop_tile = 4.0 * 64 * 64 * D
     sparse_flop = tiles * flop_tile
     dense_flop = causal_tiles * flop_tile
+    # useful work: a diagonal tile's causal part is 64 * 65 / 2 of its 64 * 64 entries
+    useful_flop = (tiles - diag_tiles * 63.0 / 128.0) * flop_tile
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -557,6 +560,7 @@ def main():
                      "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(args.workload),
+                     "useful_tflops": round(useful_flop / attn_avg / 1e9, 2),
                      "attention_ms_median": round(float(np.median(attn_ms)), 4),
                      "attention_ms_min": round(float(np.min(attn_ms)), 4),
                      "frac_of_computed_peak": None if peak is None else round(achieved / peak["bf16_tflops"], 4),
