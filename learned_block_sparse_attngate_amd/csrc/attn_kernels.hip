@@ -654,10 +654,7 @@ __device__ __forceinline__ void attn_dense_gqa_body(const AttnArgs& p) {
     const int kb = tile_kb(t);
     wait_vm_upto(issued_before(t) - through_copies(t));   // this wave's part of tile t landed
     wg_barrier();                            // every part landed; every wave is done with tile t - 1
-    if (t + kRing - 1 < ntiles) {            // refill the slot of tile t - 1
-      const int tn = t + kRing - 1;
-      issue(tile_kb(tn), tn % kRing);
-    }
+
     const uint32_t off = static_cast<uint32_t>(slot * TILE_BYTES);
     uint32_t kaddr[KS], vaddr[MT];
 #pragma unroll
@@ -665,7 +662,12 @@ __device__ __forceinline__ void attn_dense_gqa_body(const AttnArgs& p) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) vaddr[mt] = vaddr0[mt] + off;
     u32x4_t kr[2 * KS];
-    read_k_tile<D>(kaddr, kr);
+    read_k_issue<D>(kaddr, kr);
+    if (t + kRing - 1 < ntiles) {            // refill the slot of tile t - 1 while the K reads are in flight
+      const int tn = t + kRing - 1;
+      issue(tile_kb(tn), tn % kRing);
+    }
+    read_k_wait<D>(kr);
     f32x16_t sacc[2];
     const float mx = tile_scores<D, kDiag>(kr, qreg, sacc, q_local, hl, c);
     if constexpr (MODE == kDenseGt) {

@@ -50,16 +50,16 @@ namespace {
 
 constexpr int kPoolThreads = 256;
 
+// block i of head row y (b * (Hq + Hkv) + query head, or + Hq + KV head)
 template <int D>
-__global__ __launch_bounds__(kPoolThreads) void gate_pool_kernel(GateArgs a) {
+__device__ __forceinline__ void gate_pool_body(const GateArgs& a, const int i, const int y) {
   constexpr int CPR = D / 8;              // 16-byte chunks per token row
   constexpr int NRG = kPoolThreads / CPR; // row groups
   __shared__ float red[3][NRG][D];
 
-  const int i = blockIdx.x;
   const int H = a.Hq + a.Hkv;
-  const int b = blockIdx.y / H;
-  const int hx = blockIdx.y - b * H;
+  const int b = y / H;
+  const int hx = y - b * H;
   const bool isq = hx < a.Hq;
   const uint16_t* src = isq ? a.q + (static_cast<size_t>(b) * a.Hq + hx) * a.hs * D
                             : a.k + (static_cast<size_t>(b) * a.Hkv + (hx - a.Hq)) * a.hs * D;
@@ -120,12 +120,18 @@ __global__ __launch_bounds__(kPoolThreads) void gate_pool_kernel(GateArgs a) {
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(kPoolThreads) void gate_pool_kernel(GateArgs a) {
+  gate_pool_body<D>(a, blockIdx.x, blockIdx.y);
+}
+
 // ---------------------------------------------------------------------------
 // fp32 tiled GEMM: C[m][n] = alpha * sum_k A[m][k] * Bm(k, n)
 //   Bm(k, n) = B[k*ldb + n] (B_T = false) or B[n*ldb + k] (B_T = true)
 // ---------------------------------------------------------------------------
 constexpr int kGT = 256;
 constexpr int kBM = 64, kBN = 64, kBK = 16;
+static_assert(kBM == kGateTile, "the host builds varlen tile prefixes with kGateTile");
 
 // acc += A(m0 .. m0+63, k) * Bm(k, n0 .. n0+63) over k in [k0, k1), where
 // A(m, k) = A[m*lda + k] (A_T = false) or A[k*lda + m] (A_T = true), on the
@@ -236,10 +242,9 @@ __device__ __forceinline__ void gemm_tile(const float* __restrict__ A, int lda, 
 
 // Projections. blockIdx.z: 0 .. B*Hq-1 are Q' (one per query head), the rest
 // are K' (one per query head, or one per KV head).
-__global__ __launch_bounds__(kGT) void gate_proj_kernel(GateArgs a) {
+__device__ __forceinline__ void gate_proj_body(const GateArgs& a, const int bx, const int by, const int z) {
   const int nq = a.B * a.Hq;
-  const int z = blockIdx.z;
-  const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * kBN;
+  const int m0 = bx * kBM, n0 = by * kBN;
   if (z < nq) {
     const int h = z % a.Hq;
     gemm_tile<false>(a.qp + static_cast<size_t>(z) * a.nb * a.D, a.D, a.wq + static_cast<size_t>(h) * a.D * a.Dg,
@@ -255,13 +260,16 @@ __global__ __launch_bounds__(kGT) void gate_proj_kernel(GateArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kGT) void gate_proj_kernel(GateArgs a) {
+  gate_proj_body(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
 // Causal 64 x 64 tiles of the block logits z = Q' K'^T / sqrt(D). One
 // workgroup per (row z = b * Hq + h, causal tile); ntri tiles per row.
 // Workgroup w runs on XCD w % 8: when the rows split evenly over the 8 XCDs,
 // XCD x takes whole rows z = x, x + 8, ... in turn, so each row's Q' and K'
 // are fetched into one XCD's L2 instead of all eight.
-__global__ __launch_bounds__(kGT) void gate_logits_kernel(GateArgs a, int ntri) {
-  const int w = blockIdx.x;
+__device__ __forceinline__ void gate_logits_body(const GateArgs& a, const int w, const int ntri) {
   const int nz = a.B * a.Hq;
   int z, idx;
   if (nz % 8 == 0) {
@@ -284,6 +292,10 @@ __global__ __launch_bounds__(kGT) void gate_logits_kernel(GateArgs a, int ntri) 
   const float* Bk = a.kg + (static_cast<size_t>(b) * hwk + hk) * a.nb * a.Dg;
   float* C = a.scores + static_cast<size_t>(z) * a.nb * a.nb;
   gemm_tile<true>(Aq, a.Dg, Bk, a.Dg, C, a.nb, a.nb, a.nb, a.Dg, ti * kBM, tj * kBN, a.scale, true);
+}
+
+__global__ __launch_bounds__(kGT) void gate_logits_kernel(GateArgs a, int ntri) {
+  gate_logits_body(a, blockIdx.x, ntri);
 }
 
 // ---------------------------------------------------------------------------
@@ -1272,6 +1284,107 @@ __global__ __launch_bounds__(kLossThreads) void gate_loss_kernel(GateArgs a) {
   if (threadIdx.x == 0) a.loss[0] = static_cast<float>(red[0] / static_cast<double>(n));
 }
 
+// ---------------------------------------------------------------------------
+// A packed batch's gate, one launch per stage (GateVarlenTable). Every
+// workgroup (softmax: every wavefront) finds its sequence by binary search in
+// a prefix table and runs the batch-1 code on that sequence's view, so each
+// sequence's scores and mask are bitwise those of its own batch-1 call.
+// ---------------------------------------------------------------------------
+// last s in [0, n) with p[s] <= x
+__device__ __forceinline__ int varlen_seq(const int* p, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// the batch-1 arguments of sequence s of the run
+__device__ __forceinline__ GateArgs gate_seq(const GateArgs& a, const GateVarlenTable& t, int s) {
+  GateArgs r = a;
+  const size_t t0 = static_cast<size_t>(t.tokp[s]);
+  const size_t b0 = static_cast<size_t>(t.nbp[s]);
+  const size_t hwk = a.wk_per_kv ? a.Hkv : a.Hq;
+  r.q = a.q + t0 * a.D;
+  r.k = a.k + t0 * a.D;
+  r.S = t.tokp[s + 1] - t.tokp[s];
+  r.nb = t.nbp[s + 1] - t.nbp[s];
+  r.qp = a.qp + b0 * a.Hq * a.D;
+  r.kp = a.kp + b0 * a.Hkv * 3 * a.D;
+  r.qg = a.qg + b0 * a.Hq * a.Dg;
+  r.kg = a.kg + b0 * hwk * a.Dg;
+  r.scores = a.scores + t.mp[s] * a.Hq;
+  r.mask = a.mask + t.mp[s] * a.Hq;
+  return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(kPoolThreads) void gate_pool_varlen_kernel(GateArgs a, GateVarlenTable t) {
+  const int s = varlen_seq(t.nbp, t.n, blockIdx.x);
+  gate_pool_body<D>(gate_seq(a, t, s), blockIdx.x - t.nbp[s], blockIdx.y);
+}
+
+__global__ __launch_bounds__(kGT) void gate_proj_varlen_kernel(GateArgs a, GateVarlenTable t) {
+  const int s = varlen_seq(t.pp, t.n, blockIdx.x);
+  gate_proj_body(gate_seq(a, t, s), blockIdx.x - t.pp[s], blockIdx.y, blockIdx.z);
+}
+
+// as gate_rope_kernel over the run: x holds each sequence's [rows, nb, dg]
+// part one after another; the thread index runs over all blocks' pairs
+__global__ __launch_bounds__(256) void gate_rope_varlen_kernel(float* __restrict__ x, int rows, GateVarlenTable t,
+                                                               int dg, double base, double sign) {
+  const int half = dg / 2;
+  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<long long>(t.nbp[t.n]) * half) return;
+  const int gi = static_cast<int>(idx / half), d = static_cast<int>(idx - static_cast<long long>(gi) * half);
+  const int s = varlen_seq(t.nbp, t.n, gi);
+  const int i = gi - t.nbp[s], nb = t.nbp[s + 1] - t.nbp[s];
+  float* xs = x + static_cast<size_t>(t.nbp[s]) * rows * dg;
+  const double ang = sign * static_cast<double>(i) * pow(base, -2.0 * d / dg);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  const int z0 = blockIdx.y * kRopeRows;
+  float x1[kRopeRows], x2[kRopeRows];
+#pragma unroll
+  for (int u = 0; u < kRopeRows; ++u) {
+    const float* r = xs + (static_cast<size_t>(min(z0 + u, rows - 1)) * nb + i) * dg;
+    x1[u] = r[d];
+    x2[u] = r[d + half];
+  }
+#pragma unroll
+  for (int u = 0; u < kRopeRows; ++u) {
+    if (z0 + u >= rows) break;
+    float* r = xs + (static_cast<size_t>(z0 + u) * nb + i) * dg;
+    r[d] = static_cast<float>(static_cast<double>(x1[u]) * cs - static_cast<double>(x2[u]) * sn);
+    r[d + half] = static_cast<float>(static_cast<double>(x2[u]) * cs + static_cast<double>(x1[u]) * sn);
+  }
+}
+
+__global__ __launch_bounds__(kGT) void gate_logits_varlen_kernel(GateArgs a, GateVarlenTable t) {
+  const int s = varlen_seq(t.lp, t.n, blockIdx.x);
+  const int T = (t.nbp[s + 1] - t.nbp[s] + kBM - 1) / kBM;
+  gate_logits_body(gate_seq(a, t, s), blockIdx.x - t.lp[s], T * (T + 1) / 2);
+}
+
+// rows of the run: sequence s holds rows Hq nbp[s] .. Hq nbp[s+1], head major
+template <int G>
+__global__ __launch_bounds__(256) void gate_softmax_mask_varlen_kernel(GateArgs a, TopkTable tk, GateVarlenTable t) {
+  __shared__ __align__(16) uint32_t hist_all[4][256];
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int row = static_cast<int>(blockIdx.x) * 4 + wave;
+  if (row >= a.Hq * t.nbp[t.n]) return;
+  const int s = varlen_seq(t.nbp, t.n, row / a.Hq);
+  const GateArgs b = gate_seq(a, t, s);
+  const int local = row - a.Hq * t.nbp[s];
+  const int z = local / b.nb, i = local - z * b.nb;
+  const bool vec = (b.nb & 3) == 0 && (reinterpret_cast<uintptr_t>(b.scores) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(b.mask) & 3) == 0;
+  wave_softmax_mask_row<G>(b.scores + static_cast<size_t>(local) * b.nb, b.mask + static_cast<size_t>(local) * b.nb,
+                           i + 1, b.nb, b.mode, b.threshold, tk.k[z], vec, !b.skip_scores, hist_all[wave]);
+}
+
 hipError_t launch_rope(const GateArgs& a, float* x, int rows, double sign, hipStream_t st) {
   const long long n = static_cast<long long>(a.nb) * (a.Dg / 2);
   dim3 g(static_cast<unsigned>((n + 255) / 256), (rows + kRopeRows - 1) / kRopeRows);
@@ -1325,6 +1438,41 @@ hipError_t launch_gate(const GateArgs& a, const TopkTable& tk, hipStream_t st) {
     dim3 gs(a.nb, a.B * a.Hq);
     hipLaunchKernelGGL(gate_softmax_mask_kernel, gs, dim3(kST), static_cast<size_t>(a.nb) * sizeof(float), st, a, tk);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_varlen(const GateArgs& a, const TopkTable& tk, const GateVarlenTable& t, int max_nb,
+                              hipStream_t st) {
+  if (t.n < 1 || t.n > kGateVarlenMaxSeqs || max_nb > kGateVarlenMaxBlocks || a.B != 1) return hipErrorInvalidValue;
+  const int nbt = t.nbp[t.n];
+  const dim3 gp(nbt, a.Hq + a.Hkv);
+  if (a.D == 64) hipLaunchKernelGGL(gate_pool_varlen_kernel<64>, gp, dim3(kPoolThreads), 0, st, a, t);
+  else hipLaunchKernelGGL(gate_pool_varlen_kernel<128>, gp, dim3(kPoolThreads), 0, st, a, t);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int hwk = a.wk_per_kv ? a.Hkv : a.Hq;
+  hipLaunchKernelGGL(gate_proj_varlen_kernel, dim3(t.pp[t.n], (a.Dg + kBN - 1) / kBN, a.Hq + hwk), dim3(kGT), 0, st,
+                     a, t);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.rope_base > 0.0) {
+    const long long n = static_cast<long long>(nbt) * (a.Dg / 2);
+    const unsigned gx = static_cast<unsigned>((n + 255) / 256);
+    hipLaunchKernelGGL(gate_rope_varlen_kernel, dim3(gx, (a.Hq + kRopeRows - 1) / kRopeRows), dim3(256), 0, st, a.qg,
+                       a.Hq, t, a.Dg, a.rope_base, 1.0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(gate_rope_varlen_kernel, dim3(gx, (hwk + kRopeRows - 1) / kRopeRows), dim3(256), 0, st, a.kg,
+                       hwk, t, a.Dg, a.rope_base, 1.0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(gate_logits_varlen_kernel, dim3(t.lp[t.n]), dim3(kGT), 0, st, a, t);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const long long rows = static_cast<long long>(a.Hq) * nbt;
+  const dim3 gw(static_cast<unsigned>((rows + 3) / 4));
+  if (max_nb <= 256) hipLaunchKernelGGL(gate_softmax_mask_varlen_kernel<1>, gw, dim3(256), 0, st, a, tk, t);
+  else if (max_nb <= 512) hipLaunchKernelGGL(gate_softmax_mask_varlen_kernel<2>, gw, dim3(256), 0, st, a, tk, t);
+  else if (max_nb <= 1024) hipLaunchKernelGGL(gate_softmax_mask_varlen_kernel<4>, gw, dim3(256), 0, st, a, tk, t);
+  else if (max_nb <= 2048) hipLaunchKernelGGL(gate_softmax_mask_varlen_kernel<8>, gw, dim3(256), 0, st, a, tk, t);
+  else hipLaunchKernelGGL(gate_softmax_mask_varlen_kernel<16>, gw, dim3(256), 0, st, a, tk, t);
   return hipGetLastError();
 }
 

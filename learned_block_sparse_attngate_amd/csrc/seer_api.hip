@@ -754,6 +754,74 @@ static size_t varlen_gt_batch_bytes(const seer_varlen* vl) {
   return need;
 }
 
+// Runs of a packed batch whose gate shares launches: consecutive sequences of
+// at most kGateVarlenMaxBlocks blocks and at most kGateVarlenMaxSeqs of them
+// non-empty; a longer sequence is a run of its own on the batch-1 path.
+struct GateRun {
+  int first, end;     // sequences [first, end)
+  bool single;        // one sequence on the batch-1 path
+};
+
+static long long varlen_nb(const seer_varlen* vl, int i) {
+  return (static_cast<long long>(vl->cu_seqlens[i + 1]) - vl->cu_seqlens[i] + kBlock - 1) / kBlock;
+}
+
+static std::vector<GateRun> gate_runs(const seer_varlen* vl) {
+  std::vector<GateRun> runs;
+  int i = 0;
+  while (i < vl->num_seqs) {
+    const long long nb = varlen_nb(vl, i);
+    if (nb == 0) { ++i; continue; }
+    if (nb > seer::kGateVarlenMaxBlocks) { runs.push_back({i, i + 1, true}); ++i; continue; }
+    int j = i, cnt = 0;
+    while (j < vl->num_seqs && cnt < seer::kGateVarlenMaxSeqs) {
+      const long long nj = varlen_nb(vl, j);
+      if (nj > seer::kGateVarlenMaxBlocks) break;
+      cnt += nj > 0;
+      ++j;
+    }
+    runs.push_back({i, j, false});
+    i = j;
+  }
+  return runs;
+}
+
+// Workspace of a shared run: each intermediate holds the run's sequences one
+// after another (and, without a scores output, the logits maps).
+static GateLayout gate_run_layout(const seer_varlen* vl, const GateRun& r, int dg, int wk_per_kv, bool want_scores) {
+  size_t nbs = 0, nb2 = 0;
+  for (int i = r.first; i < r.end; ++i) {
+    const size_t nb = static_cast<size_t>(varlen_nb(vl, i));
+    nbs += nb;
+    nb2 += nb * nb;
+  }
+  const size_t Hq = vl->heads_q, Hkv = vl->heads_kv, D = vl->head_dim, hwk = wk_per_kv ? Hkv : Hq;
+  GateLayout L{};
+  size_t off = 0;
+  L.qp = off; off += align_up(Hq * nbs * D * 4);
+  L.kp = off; off += align_up(Hkv * nbs * 3 * D * 4);
+  L.qg = off; off += align_up(Hq * nbs * dg * 4);
+  L.kg = off; off += align_up(hwk * nbs * dg * 4);
+  L.scores = off; off += want_scores ? 0 : align_up(Hq * nb2 * 4);
+  L.total = off;
+  return L;
+}
+
+static size_t gate_varlen_need(const seer_varlen* vl, int dg, int wk_per_kv, bool want_scores) {
+  size_t need = 0;
+  for (const GateRun& r : gate_runs(vl)) {
+    size_t n;
+    if (r.single) {
+      const seer_shape s = varlen_shape(vl, r.first);
+      n = gate_layout(&s, dg, wk_per_kv, want_scores).total;
+    } else {
+      n = gate_run_layout(vl, r, dg, wk_per_kv, want_scores).total;
+    }
+    need = std::max(need, n);
+  }
+  return need;
+}
+
 size_t seer_varlen_map_elements(const seer_varlen* vl) {
   long long total = 0;
   if (check_varlen(vl, &total) != SEER_OK) return 0;
@@ -770,12 +838,12 @@ size_t seer_gate_varlen_workspace_size(const seer_varlen* vl, int32_t gate_dim, 
   long long total = 0;
   if (check_varlen(vl, &total) != SEER_OK) return 0;
   size_t need = 0;
-  for (int i = 0; i < vl->num_seqs; ++i) {
+  for (int i = 0; i < vl->num_seqs; ++i) {     // every sequence's own requirement (its argument checks)
     const seer_shape s = varlen_shape(vl, i);
     const size_t n = seer_gate_workspace_size(&s, gate_dim, wk_per_kv_head, want_scores);
     need = n > need ? n : need;
   }
-  return need;
+  return std::max(need, gate_varlen_need(vl, gate_dim, wk_per_kv_head != 0, want_scores != 0));
 }
 
 size_t seer_attn_varlen_workspace_size(const seer_varlen* vl) {
@@ -804,22 +872,89 @@ seer_status seer_gate_varlen_fwd(const seer_varlen* vl, int32_t gate_dim, int32_
   long long total = 0;
   seer_status st = check_varlen(vl, &total);
   if (st != SEER_OK) return st;
-  for (int pass = 0; pass < 2; ++pass) {
-    size_t moff = 0;
-    for (int i = 0; i < vl->num_seqs; ++i) {
-      const seer_shape s = varlen_shape(vl, i);
-      const size_t t0 = static_cast<size_t>(vl->cu_seqlens[i]) * vl->head_dim;
-      const size_t nb = nblocks(&s);
-      if (s.seq_len > 0) {
-        st = gate_impl(&s, total, gate_dim, wk_per_kv_head, rope_theta,
-                       q ? static_cast<const uint16_t*>(q) + t0 : nullptr,
-                       k ? static_cast<const uint16_t*>(k) + t0 : nullptr, w_q, w_k, mode, threshold, topk_k,
-                       topk_per_head, scores ? scores + moff : nullptr, block_mask ? block_mask + moff : nullptr,
-                       workspace, workspace_bytes, hip_stream, pass == 1);
-        if (st != SEER_OK) return st;
-      }
-      moff += static_cast<size_t>(vl->heads_q) * nb * nb;
+  const std::vector<long long> moff = varlen_map_offsets(vl);
+  auto seq = [&](int i, bool launch) {
+    const seer_shape s = varlen_shape(vl, i);
+    const size_t t0 = static_cast<size_t>(vl->cu_seqlens[i]) * vl->head_dim;
+    return gate_impl(&s, total, gate_dim, wk_per_kv_head, rope_theta,
+                     q ? static_cast<const uint16_t*>(q) + t0 : nullptr,
+                     k ? static_cast<const uint16_t*>(k) + t0 : nullptr, w_q, w_k, mode, threshold, topk_k,
+                     topk_per_head, scores ? scores + moff[i] : nullptr, block_mask ? block_mask + moff[i] : nullptr,
+                     workspace, workspace_bytes, hip_stream, launch);
+  };
+  // every sequence's arguments first, then the launches
+  for (int i = 0; i < vl->num_seqs; ++i)
+    if (vl->cu_seqlens[i + 1] > vl->cu_seqlens[i] && (st = seq(i, false)) != SEER_OK) return st;
+  const std::vector<GateRun> runs = gate_runs(vl);
+  if (runs.empty()) return ok();
+  const size_t need = gate_varlen_need(vl, gate_dim, wk_per_kv_head != 0, scores != nullptr);
+  if (workspace_bytes < need)
+    return fail(SEER_ERR_WORKSPACE, "workspace must be %zu bytes, 256-byte aligned (got %zu)", need, workspace_bytes);
+  seer::TopkTable tk{};
+  const seer_shape s0 = varlen_shape(vl, runs[0].first);
+  if ((st = fill_topk(&s0, mode, topk_k, topk_per_head, &tk)) != SEER_OK) return st;
+  for (const GateRun& r : runs) {
+    if (r.single) {
+      if ((st = seq(r.first, true)) != SEER_OK) return st;
+      continue;
     }
+    // the run in one launch per stage: the batch-1 arguments at its first
+    // sequence, the intermediates of its sequences one after another
+    const GateLayout L = gate_run_layout(vl, r, gate_dim, wk_per_kv_head != 0, scores != nullptr);
+    seer::GateVarlenTable t{};
+    int max_nb = 0;
+    long long nbs = 0, pps = 0, lps = 0, nb2 = 0;
+    t.n = r.end - r.first;
+    for (int i = r.first; i < r.end; ++i) {
+      const int k = i - r.first;
+      const long long nb = varlen_nb(vl, i);
+      const long long T = (nb + seer::kGateTile - 1) / seer::kGateTile;
+      t.tokp[k] = vl->cu_seqlens[i] - vl->cu_seqlens[r.first];
+      t.nbp[k] = static_cast<int>(nbs);
+      t.pp[k] = static_cast<int>(pps);
+      t.lp[k] = static_cast<int>(lps);
+      t.mp[k] = nb2;
+      nbs += nb;
+      pps += T;
+      lps += T * (T + 1) / 2 * vl->heads_q;
+      nb2 += nb * nb;
+      max_nb = std::max(max_nb, static_cast<int>(nb));
+    }
+    if (lps > 0x7fffffffLL || static_cast<long long>(vl->heads_q) * nbs > 0x7fffffffLL)
+      return fail(SEER_ERR_UNSUPPORTED, "packed batch too large for one gate launch");
+    t.tokp[t.n] = vl->cu_seqlens[r.end] - vl->cu_seqlens[r.first];
+    t.nbp[t.n] = static_cast<int>(nbs);
+    t.pp[t.n] = static_cast<int>(pps);
+    t.lp[t.n] = static_cast<int>(lps);
+    t.mp[t.n] = nb2;
+    char* ws = static_cast<char*>(workspace);
+    const size_t t0 = static_cast<size_t>(vl->cu_seqlens[r.first]) * vl->head_dim;
+    seer::GateArgs a{};
+    a.q = static_cast<const uint16_t*>(q) + t0;
+    a.k = static_cast<const uint16_t*>(k) + t0;
+    a.wq = w_q;
+    a.wk = w_k;
+    a.qp = reinterpret_cast<float*>(ws + L.qp);
+    a.kp = reinterpret_cast<float*>(ws + L.kp);
+    a.qg = reinterpret_cast<float*>(ws + L.qg);
+    a.kg = reinterpret_cast<float*>(ws + L.kg);
+    a.scores = scores ? scores + moff[r.first] : reinterpret_cast<float*>(ws + L.scores);
+    a.mask = block_mask + moff[r.first];
+    a.skip_scores = scores == nullptr;
+    a.B = 1;
+    a.Hq = vl->heads_q;
+    a.Hkv = vl->heads_kv;
+    a.hs = total;
+    a.D = vl->head_dim;
+    a.Dg = gate_dim;
+    a.group = vl->heads_q / vl->heads_kv;
+    a.wk_per_kv = wk_per_kv_head != 0;
+    a.scale = static_cast<float>(1.0 / sqrt(static_cast<double>(vl->head_dim)));
+    a.mode = mode == SEER_MASK_TOPK ? 1 : 0;
+    a.threshold = threshold;
+    a.rope_base = rope_theta > 0.f ? static_cast<double>(rope_theta) / vl->block : 0.0;
+    const hipError_t e = seer::launch_gate_varlen(a, tk, t, max_nb, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SEER_ERR_HIP, "varlen gate launch failed: %s", hipGetErrorString(e));
   }
   return ok();
 }

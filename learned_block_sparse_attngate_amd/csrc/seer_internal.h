@@ -108,6 +108,26 @@ struct TopkTable {
 
 hipError_t launch_gate(const GateArgs& a, const TopkTable& tk, hipStream_t st);
 
+// A packed batch's gate in one launch per stage: up to kGateVarlenMaxSeqs
+// sequences that are consecutive in the batch, each the batch-1 problem at its
+// token offset. GateArgs then describes the run: q/k at its first token (hs =
+// the packed length), B = 1, scores/mask at its first sequence's maps, and
+// the qp/kp/qg/kg (and, without a scores output, logits) regions hold every
+// sequence's part one after another. Prefix sums over the run's sequences:
+constexpr int kGateTile = 64;               // row / column tile of the gate's projections and logits
+constexpr int kGateVarlenMaxSeqs = 64;
+constexpr int kGateVarlenMaxBlocks = 4096;  // rows a wavefront keeps in registers
+struct GateVarlenTable {
+  int n;
+  int tokp[kGateVarlenMaxSeqs + 1];        // tokens
+  int nbp[kGateVarlenMaxSeqs + 1];         // 64-token blocks (the intermediates' offsets, pool and RoPE grids)
+  int pp[kGateVarlenMaxSeqs + 1];          // projection row tiles
+  int lp[kGateVarlenMaxSeqs + 1];          // logit tile workgroups (causal tiles x Hq)
+  long long mp[kGateVarlenMaxSeqs + 1];    // nb^2 (map offsets, times Hq)
+};
+hipError_t launch_gate_varlen(const GateArgs& a, const TopkTable& tk, const GateVarlenTable& t, int max_nb,
+                              hipStream_t st);
+
 // Decode-stage gate: compressed K cache and per-token gate.
 struct DecodeGateArgs {
   const uint16_t* q;   // bf16 [B,Hq,D], one query per head

@@ -136,6 +136,44 @@ def test_varlen_long_sequence_xcd_path():
     check_close(o_h[:, cu[0]:cu[1]][None], o0, "short seq O")
 
 
+def test_varlen_gate_one_launch_equals_batch1():
+    """The packed gate runs up to 64 consecutive sequences per launch of each
+    stage (a sequence of more than 4096 blocks on its own launches): every
+    sequence's scores and mask are bitwise those of its batch-1 call, with and
+    without a scores output, in top-k mode with block RoPE and in threshold
+    mode. 69 sequences, empty ones among them: two shared runs around the long
+    one."""
+    seer = _seer()
+    hq, hkv, D, dg = 2, 1, 64, 64
+    rng = np.random.default_rng(410)
+    lens = [int(x) for x in rng.integers(1, 64 * 40, size=69)]
+    lens[5] = 0
+    lens[40] = 64 * 4097 + 3                      # past the register-resident row length
+    lens[41] = 0
+    say(f"[varlen gate one launch] {len(lens)} sequences, {sum(lens)} tokens")
+    _, qp, kp, _, cu = _pack(lens, D, 420, hq, hkv)
+    wq, wk = synth.gen_gate_weights(hq, D, dg, 421, var=4.0 / dg)
+    q_d, k_d, wq_d, wk_d = dev_bf16(qp), dev_bf16(kp), dev_f32(wq), dev_f32(wk)
+    offs, n_map = seer.varlen_map_offsets(cu, hq)
+    for kw in (dict(mode="topk", topk=[5, 2], rope_theta=5e5), dict(mode="threshold", threshold=0.02)):
+        m, s = seer.seer_gate_varlen_fwd(q_d, k_d, wq_d, wk_d, cu, **kw)
+        m2, s2 = seer.seer_gate_varlen_fwd(q_d, k_d, wq_d, wk_d, cu, want_scores=False, **kw)
+        torch.cuda.synchronize()
+        assert s2 is None and m.numel() == n_map
+        assert torch.equal(m, m2), f"{kw['mode']}: mask without scores differs"
+        for i, n in enumerate(lens):
+            if n == 0:
+                continue
+            nb = (n + 63) // 64
+            q1 = q_d[:, cu[i]:cu[i + 1]].unsqueeze(0).contiguous()
+            k1 = k_d[:, cu[i]:cu[i + 1]].unsqueeze(0).contiguous()
+            mb, sb = seer.seer_gate_fwd(q1, k1, wq_d, wk_d, **kw)
+            sl = slice(offs[i], offs[i] + hq * nb * nb)
+            assert torch.equal(m[sl].view(1, hq, nb, nb), mb), f"{kw['mode']}: seq {i} mask"
+            assert torch.equal(s[sl].view(1, hq, nb, nb), sb), f"{kw['mode']}: seq {i} scores"
+        say(f"  {kw['mode']}: {int(m.sum())} active blocks, every sequence bitwise equal to its batch-1 call")
+
+
 def test_varlen_gate_and_gt():
     seer = _seer()
     lens = [640, 0, 64 * 30 - 7, 65]

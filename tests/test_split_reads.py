@@ -86,3 +86,8 @@ def test_no_instruction_touches_a_split_read_destination(kernel_asm):
         # every kernel reads K and V of at least two inlined tile bodies (the
         # diagonal tile and the others) through the split form
         assert _check_kernel(name, kernel_asm) >= 4, name
+    # the GQA dense kernel splits its K reads (diagonal tile and the others)
+    gqa = re.findall(r"^(_ZN4seer\S*attn_dense_gqa_kernel\S*):", kernel_asm, re.M)
+    assert len(gqa) == 4, gqa
+    for name in gqa:
+        assert _check_kernel(name, kernel_asm) >= 2, name
