@@ -256,11 +256,33 @@ def bench_varlen(seer, torch, dev, stream, seed, reps: int = 5):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
         tflops = tiles * 4.0 * 64 * 64 * D / ms / 1e9
+
+        # the packed batch's gate (top-k 10% of each row's blocks, mask only)
+        dg = 128
+        wq = torch.randn((Hq, D, dg), generator=g, device=dev) / dg ** 0.5
+        wk = torch.randn((Hq, 3 * D, dg), generator=g, device=dev) / dg ** 0.5
+        gmask = torch.empty(mask.numel(), dtype=torch.uint8, device=dev)
+        gws = torch.empty(max(seer.gate_varlen_workspace_bytes(cu, Hq, Hkv, D, dg, want_scores=False), 16),
+                          dtype=torch.uint8, device=dev)
+        k_top = max(1, (min(lens) // 64) // 10)
+
+        def gate():
+            seer.seer_gate_varlen_fwd(q, k, wq, wk, cu, mode="topk", topk=k_top, rope_theta=5e5, want_scores=False,
+                                      block_mask=gmask, workspace=gws)
+        gate()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            gate()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gate_ms = e0.elapsed_time(e1) / reps
         print(f"[bench] varlen {name}: {len(lens)} sequences, {T} tokens, block-sparse attention {ms:.3f} ms "
-              f"({tflops:.1f} TFLOP/s on executed tiles)", file=sys.stderr, flush=True)
+              f"({tflops:.1f} TFLOP/s on executed tiles), gate {gate_ms:.3f} ms", file=sys.stderr, flush=True)
         res[name] = {"lengths": lens if len(set(lens)) > 1 else f"{len(lens)} x {lens[0]}", "tokens": T,
-                     "sparse_attention_ms": round(ms, 4), "executed_tiles": tiles, "tflops": round(tflops, 2)}
-        del q, k, v, mask, out
+                     "sparse_attention_ms": round(ms, 4), "executed_tiles": tiles, "tflops": round(tflops, 2),
+                     "gate_ms": round(gate_ms, 4), "gate_topk": k_top}
+        del q, k, v, mask, out, gmask, gws
     return res
 
 

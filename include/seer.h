@@ -288,11 +288,15 @@ seer_status seer_decode_attn_fwd_noalloc(const seer_shape* shape, const void* q,
  * sequences together: up to 64 sequences per launch, longest first, each row
  * of each sequence one workgroup of a single grid (in block-sparse mode,
  * sequences of more than 1024 blocks run on their own launches, key-chunked,
- * and share the workspace). The gate runs the sequences one after another
- * and shares the workspace. seer_gt_varlen_workspace_size() covers the
- * scratch of every sequence of the largest shared launch; the other
- * workspace sizes are the largest any sequence needs. All sequences are
- * validated before anything is enqueued. Empty sequences are allowed.
+ * and share the workspace). The gate runs runs of up to 64 consecutive
+ * sequences of at most 4096 blocks each in one launch per stage; a longer
+ * sequence ends a run and runs on its own launches. Its workspace
+ * (seer_gate_varlen_workspace_size()) holds the largest run's intermediates
+ * side by side. seer_gt_varlen_workspace_size() covers the scratch of every
+ * sequence of the largest shared launch; the attention workspace is the
+ * largest any sequence needs. All sequences are validated, and the
+ * workspace checked, before anything is enqueued. Empty sequences are
+ * allowed.
  * ---------------------------------------------------------------------- */
 typedef struct seer_varlen {
   int32_t num_seqs;

@@ -12,7 +12,8 @@ from ._binding import (  # noqa: F401
     seer_decode_attn_fwd_noalloc, NOALLOC_SCRATCH_BYTES,
     SeerVarlen, make_varlen, varlen_map_offsets, seer_gate_varlen_fwd, seer_block_sparse_attn_varlen_fwd,
     seer_attn_maxpool_gt_varlen,
-    gate_workspace_bytes, distill_workspace_bytes, gt_workspace_bytes, attn_workspace_bytes, version,
+    gate_workspace_bytes, gate_varlen_workspace_bytes, distill_workspace_bytes, gt_workspace_bytes,
+    attn_workspace_bytes, version,
     SEER_OK, SEER_ERR_INVALID_ARG, SEER_ERR_SHAPE, SEER_ERR_UNSUPPORTED, SEER_ERR_WORKSPACE, SEER_ERR_HIP,
     SEER_MASK_THRESHOLD, SEER_MASK_TOPK, SEER_F32, SEER_BF16,
 )

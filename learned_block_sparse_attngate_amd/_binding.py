@@ -504,6 +504,14 @@ def make_varlen(cu_seqlens: Sequence[int], heads_q: int, heads_kv: int, head_dim
     return vl
 
 
+def gate_varlen_workspace_bytes(cu_seqlens: Sequence[int], heads_q: int, heads_kv: int, head_dim: int,
+                                gate_dim: int, wk_per_kv_head: bool = False, want_scores: bool = True) -> int:
+    """Workspace of seer_gate_varlen_fwd for this packed batch."""
+    vl = make_varlen(cu_seqlens, heads_q, heads_kv, head_dim)
+    return load_library().seer_gate_varlen_workspace_size(ctypes.byref(vl), gate_dim, int(wk_per_kv_head),
+                                                          int(want_scores))
+
+
 def varlen_map_offsets(cu_seqlens: Sequence[int], heads_q: int):
     """Element offset of each sequence's [Hq, nb_i, nb_i] block map, and the total."""
     offs, n = [], 0

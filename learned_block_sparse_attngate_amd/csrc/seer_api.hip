@@ -882,14 +882,15 @@ seer_status seer_gate_varlen_fwd(const seer_varlen* vl, int32_t gate_dim, int32_
                      topk_per_head, scores ? scores + moff[i] : nullptr, block_mask ? block_mask + moff[i] : nullptr,
                      workspace, workspace_bytes, hip_stream, launch);
   };
-  // every sequence's arguments first, then the launches
-  for (int i = 0; i < vl->num_seqs; ++i)
-    if (vl->cu_seqlens[i + 1] > vl->cu_seqlens[i] && (st = seq(i, false)) != SEER_OK) return st;
   const std::vector<GateRun> runs = gate_runs(vl);
   if (runs.empty()) return ok();
   const size_t need = gate_varlen_need(vl, gate_dim, wk_per_kv_head != 0, scores != nullptr);
-  if (workspace_bytes < need)
-    return fail(SEER_ERR_WORKSPACE, "workspace must be %zu bytes, 256-byte aligned (got %zu)", need, workspace_bytes);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, kAlign))
+    return fail(SEER_ERR_WORKSPACE, "workspace must be %zu bytes, 256-byte aligned (got %zu at %p)", need,
+                workspace_bytes, workspace);
+  // every sequence's arguments first, then the launches
+  for (int i = 0; i < vl->num_seqs; ++i)
+    if (vl->cu_seqlens[i + 1] > vl->cu_seqlens[i] && (st = seq(i, false)) != SEER_OK) return st;
   seer::TopkTable tk{};
   const seer_shape s0 = varlen_shape(vl, runs[0].first);
   if ((st = fill_topk(&s0, mode, topk_k, topk_per_head, &tk)) != SEER_OK) return st;

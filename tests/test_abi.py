@@ -200,6 +200,30 @@ def test_varlen_validation_and_sizes():
                                                  None, B.SEER_F32, None, None, 0, None) == B.SEER_OK
 
 
+def test_varlen_gate_workspace():
+    """The packed gate runs consecutive sequences of up to 4096 blocks in one
+    launch per stage: its workspace holds a run's pooled, projected (and,
+    without scores, logits) parts side by side; a longer sequence runs alone
+    and needs its own batch-1 workspace."""
+    lib = _lib()
+    hq, hkv, d, dg = 32, 8, 128, 128
+    al = lambda n: (n + 255) // 256 * 256
+    nbs = [32, 32, 30]
+    vl = B.make_varlen([0, 2048, 4096, 4096, 6000], hq, hkv, d)     # an empty sequence inside the run
+    inter = al(hq * d * 4 * sum(nbs)) + al(hkv * 3 * d * 4 * sum(nbs)) + 2 * al(hq * dg * 4 * sum(nbs))
+    assert lib.seer_gate_varlen_workspace_size(ctypes.byref(vl), dg, 0, 1) == inter
+    assert lib.seer_gate_varlen_workspace_size(ctypes.byref(vl), dg, 0, 0) == inter + al(hq * sum(n * n for n in nbs) * 4)
+    # a sequence of 4097 blocks ends the run and runs on its own
+    long_len = 64 * 4097
+    vl2 = B.make_varlen([0, 2048, 2048 + long_len, 2 * 2048 + long_len], hq, hkv, d)
+    one = lib.seer_gate_workspace_size(ctypes.byref(_shape(b=1, hq=hq, hkv=hkv, s=long_len, d=d)), dg, 0, 0)
+    assert lib.seer_gate_varlen_workspace_size(ctypes.byref(vl2), dg, 0, 0) == one
+    # too small a workspace is refused before any launch
+    need = lib.seer_gate_varlen_workspace_size(ctypes.byref(vl), dg, 0, 0)
+    assert lib.seer_gate_varlen_fwd(ctypes.byref(vl), dg, 0, 0.0, FAKE, FAKE, FAKE, FAKE, B.SEER_MASK_THRESHOLD,
+                                    0.1, 1, None, None, FAKE, FAKE, need - 256, None) == B.SEER_ERR_WORKSPACE
+
+
 def test_gate_validation():
     s = _shape()
     assert _gate(s, dg=100) == B.SEER_ERR_UNSUPPORTED
