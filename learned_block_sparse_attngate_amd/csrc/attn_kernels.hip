@@ -966,12 +966,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
     if (c0 + 64 + lane < kend) f1 = mrow[c0 + 64 + lane];
   };
   // Q rows of an item (rows past the sequence repeat the last one: their
-  // outputs are never stored)
+  // outputs are never stored), as buffer loads: one scalar resource per item
+  // and 32-bit lane offsets
   auto load_q = [&](const XcdItem& it, uint4 (&qr)[KS]) {
-    const int t = min(it.qb * kBlock + q_local, p.S - 1);
-    const uint16_t* qrow = p.q + (static_cast<size_t>(it.bh) * p.hs + t) * D + 8 * hl;
+    const int t0 = it.qb * kBlock;
+    const int t = min(t0 + q_local, p.S - 1);
+    uint16_t* qblk = const_cast<uint16_t*>(p.q + (static_cast<size_t>(it.bh) * p.hs + t0) * D);
+    const auto rq = __builtin_amdgcn_make_buffer_rsrc(qblk, 0, kBlock * D * 2, kBufferWord3);
+    const uint32_t off = static_cast<uint32_t>(((t - t0) * D + 8 * hl) * 2);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qr[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks);
+    for (int ks = 0; ks < KS; ++ks)
+      qr[ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 32 * ks, 0, 0));
   };
   // first tile of an item: the diagonal if it is active, else the lowest active block
   auto first_tile = [&](const XcdItem& it, uint64_t f0, uint64_t f1) -> int {
