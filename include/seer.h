@@ -167,8 +167,13 @@ seer_status seer_gate_distill_bwd(const seer_shape* shape, int32_t gate_dim, int
  *              bytes per row and chunk (bf16 output, fp32 log-sum-exp) plus
  *              256 bytes of item counters that every call resets. Other long
  *              rows use chunks of 512 blocks: 64 * (head_dim + 1) * 4 bytes
- *              per row and chunk. The size is 0, and workspace may be NULL,
- *              when seq_len <= 65536. The active blocks of each row are
+ *              per row and chunk. Rows of at most 256 blocks at head_dim
+ *              128 (512 at head_dim 64) with batch * heads_q a multiple of 8
+ *              take 256 bytes: a pre-pass counts the mask's active tiles per
+ *              XCD of the XCD-major row order (each XCD takes an eighth of
+ *              the heads), which is used when those counts are balanced.
+ *              Otherwise the size is 0, and workspace may be NULL, when
+ *              seq_len <= 65536. The active blocks of each row are
  *              compacted on chip.
  * ---------------------------------------------------------------------- */
 size_t seer_attn_workspace_size(const seer_shape* shape);

@@ -462,6 +462,31 @@ __device__ __forceinline__ void attn_row(const AttnArgs& p, const int w, const i
   }
 }
 
+// Pre-pass of the XCD-major row order: active causal tiles of the mask rows
+// [16 y, 16 y + 16) of flattened head bh = blockIdx.x, added to the count of
+// the XCD that owns the head in that order (xcd_work, zeroed before).
+constexpr int kWorkRows = 16;
+__global__ __launch_bounds__(256) void attn_xcd_work_kernel(AttnArgs p) {
+  const int bh = blockIdx.x;
+  const int q0 = blockIdx.y * kWorkRows;
+  const int rows = min(kWorkRows, p.nb - q0);
+  const uint8_t* m = p.mask + (static_cast<size_t>(bh) * p.nb + q0) * p.nb;
+  const int n = rows * p.nb;
+  int cnt = 0;
+#pragma unroll 8
+  for (int e = threadIdx.x; e < n; e += 256) {
+    const int r = e / p.nb;
+    cnt += (e - r * p.nb <= q0 + r && m[e] != 0) ? 1 : 0;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+  __shared__ int part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicAdd(p.xcd_work + bh / (p.B * p.Hq / kXcds), part[0] + part[1] + part[2] + part[3]);
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   // ---- which row ---------------------------------------------------------
@@ -476,7 +501,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   const int w = blockIdx.x;
   int qb, bh;
   int chunk = 0;                                  // block-sparse: key chunk of this work item
+  bool xcd_major = false;
   if constexpr (MODE == kSparse) {
+    if (p.xcd_work != nullptr) {
+      // balanced when the most loaded XCD has at most 1.2 x the mean
+      int mx = 0, sum = 0;
+#pragma unroll
+      for (int x = 0; x < kXcds; ++x) {
+        const int cx = p.xcd_work[x];
+        mx = max(mx, cx);
+        sum += cx;
+      }
+      xcd_major = 5 * kXcds * static_cast<long long>(mx) <= 6 * static_cast<long long>(sum);
+    }
+  }
+  if (MODE == kSparse && xcd_major) {
+    // Rows of one item, query block descending (the longest rows first);
+    // within a query block, the workgroups that land on XCD x take the heads
+    // [x BH/8, (x+1) BH/8), so each XCD's L2 serves the K/V of those heads'
+    // groups only. Each XCD then does the work of its heads, so this order
+    // is taken only when the pre-pass found those counts balanced; the host
+    // asks for it only for short rows and B Hq a multiple of 8.
+    const int per = BH / kXcds;
+    qb = p.nb - 1 - w / BH;
+    const int local = w % BH;
+    bh = (local % kXcds) * per + local / kXcds;
+  } else if constexpr (MODE == kSparse) {
     // Key-chunked items: (batch, KV group) major, then chunk c ascending, then
     // head, then query block descending. Consecutive items go round-robin over
     // the XCDs, so all of them work on one C-block K/V chunk of one group at a
@@ -806,10 +856,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_varlen_kernel(AttnArgs p, Va
 // its sequence (a fixed stride per workgroup lets them drift over several
 // chunks). Nothing drains between items: item indices are fetched two items
 // ahead, the next item's mask flags one item ahead, and its Q rows and the K
-// of its first tile are issued during the current item's last tile. An item of a row
-// that spans several chunks writes a bf16 partial output (normalized by its
-// own sum) and its log2-sum-exp; attn_xcd_combine_kernel merges them. Rows
-// inside the first chunk are one item and are written directly.
+// of its first tile are issued during the current item's last tile. An item
+// of a row that spans several chunks writes a bf16 partial output
+// (normalized by its own sum) and its log2-sum-exp; attn_xcd_combine_kernel
+// merges them. Rows inside the first chunk are one item and are written
+// directly.
 constexpr int kXcdDefaultChunk = 128;    // 4 MiB of K/V at D = 128: one XCD's L2
 static_assert(kXcdDefaultChunk <= 128, "an item's flags are two 64-bit ballot words");
 constexpr int kXcdMinBlocks = 1280;      // rows of 80k tokens and more
@@ -1057,7 +1108,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
   load_flags(it1, fb0, fb1);
   wait_vm(0);
   uint64_t f0 = __builtin_amdgcn_ballot_w64(fa0 != 0), f1 = __builtin_amdgcn_ballot_w64(fa1 != 0);
-  bool warm = false;                               // the item's Q and first tile were issued during the previous one
+  bool warm = false;                               // the item's Q and first K tile were issued during the previous one
 
   while (true) {
     // ---- item start ------------------------------------------------------
@@ -1341,6 +1392,11 @@ hipError_t launch_d(const AttnArgs& a, int mode, hipStream_t st) {
     return hipGetLastError();
   }
   if (mode == kSparse) {
+    if (a.xcd_work != nullptr) {
+      hipLaunchKernelGGL(attn_xcd_counters_init, dim3(1), dim3(kWave), 0, st, a.xcd_work);
+      const dim3 wgrid(static_cast<unsigned>(a.B) * a.Hq, static_cast<unsigned>((a.nb + kWorkRows - 1) / kWorkRows));
+      hipLaunchKernelGGL(attn_xcd_work_kernel, wgrid, dim3(256), 0, st, a);
+    }
     const dim3 grid(static_cast<unsigned>(static_cast<long long>(a.B) * a.Hkv * a.items_per_group));
     hipLaunchKernelGGL((attn_fwd_kernel<D, kSparse>), grid, block, 0, st, a);
     if (a.nchunk > 1) {
@@ -1371,6 +1427,7 @@ namespace {
 // tokens) a row is one item; longer rows are cut into chunks of 512 blocks,
 // which the XCDs sweep together.
 int sweep_chunk_blocks(int nb) { return nb > 1024 ? 512 : kListCap; }
+constexpr long long kXcdRowsMaxBlockDims = 256 * 128;   // key blocks x head_dim
 }  // namespace
 
 // The XCD-owned path takes rows of at least kXcdMinBlocks blocks when there
@@ -1397,11 +1454,19 @@ SparsePlan sparse_plan(int B, int Hkv, int group, int nb, int D) {
   pl.chunk = sweep_chunk_blocks(nb);
   pl.nchunk = (nb + pl.chunk - 1) / pl.chunk;
   pl.rotate = 1;
+  // the XCD-major order of one-item rows, for rows of up to 256 blocks at
+  // D = 128 (512 at D = 64: K and V of a KV head up to twice an XCD's L2),
+  // where it measured faster on balanced masks, and heads that split evenly
+  // over the 8 XCDs; 256 bytes of per-XCD counts
+  pl.xcd_rows = pl.nchunk == 1 && static_cast<long long>(nb) * D <= kXcdRowsMaxBlockDims &&
+                (static_cast<long long>(B) * Hkv * group) % kXcds == 0;
   const long long nc = pl.nchunk;
   pl.items_per_group = static_cast<long long>(group) * (nc * nb - static_cast<long long>(pl.chunk) * nc * (nc - 1) / 2);
   if (nb > pl.chunk) {
     const size_t items = static_cast<size_t>(B) * Hkv * pl.items_per_group;
     pl.workspace_bytes = items * kBlock * (static_cast<size_t>(D) + 1) * sizeof(float);
+  } else if (pl.xcd_rows) {
+    pl.workspace_bytes = 256;
   }
   return pl;
 }

@@ -594,6 +594,8 @@ static seer_status attn_impl(const seer_shape* shape, long long hs, const void* 
         a.part_o16 = static_cast<uint16_t*>(workspace);
         a.part_l = reinterpret_cast<float*>(a.part_o16 + slots * 64 * a.D);
         a.xcd_ctr = reinterpret_cast<int*>(a.part_l + slots * 64);
+      } else if (pl.xcd_rows) {
+        a.xcd_work = static_cast<int*>(workspace);
       } else {
         a.part_o = static_cast<float*>(workspace);
         a.part_l = a.part_o + static_cast<size_t>(items) * 64 * a.D;

@@ -36,6 +36,10 @@ struct AttnArgs {
   long long slots_per_head;   // partial-output slots per (batch, head)
   uint16_t* part_o16;  // [B*Hq*slots_per_head][D/16 groups][128 threads][8] bf16 normalized partials
   int* xcd_ctr;        // 8 per-XCD item counters (zeroed by the launch)
+  // block-sparse rows of one item, short sequences: active causal tiles of the
+  // heads each XCD would own in the XCD-major order (counted by a pre-pass);
+  // nullptr: that order is not considered
+  int* xcd_work;
 };
 
 // mode: 0 block-sparse (mask), 1 dense causal, 2 dense causal + ground-truth maxima
@@ -68,6 +72,7 @@ struct SparsePlan {
   long long items_per_group;  // other path: (row, chunk) items per (batch, KV group)
   int njobs;                  // XCD path: (batch, KV group, chunk) jobs
   long long slots_per_head;   // XCD path: partial slots per (batch, head)
+  int xcd_rows;               // one-item rows: the XCD-major order is taken when the mask's work is balanced
   size_t workspace_bytes;
 };
 SparsePlan sparse_plan(int B, int Hkv, int group, int nb, int D);

@@ -258,7 +258,13 @@ def test_workspace_sizes():
     s = _shape(b=2, hq=4, hkv=2, s=200, d=64)
     nb = 4
     align = lambda x: (x + 255) // 256 * 256
-    assert lib.seer_attn_workspace_size(ctypes.byref(s)) == 0   # every row within one key chunk
+    # every row within one key chunk; 8 heads over the 8 XCDs: the per-XCD
+    # counts of the XCD-major order (8 ints in 256 bytes)
+    assert lib.seer_attn_workspace_size(ctypes.byref(s)) == 256
+    for b0, hq0, s0, d0 in ((1, 12, 200, 64), (1, 8, 64 * 257, 128), (1, 8, 64 * 513, 64)):
+        assert lib.seer_attn_workspace_size(ctypes.byref(_shape(b=b0, hq=hq0, hkv=hq0 // 4, s=s0, d=d0))) == 0
+    assert lib.seer_attn_workspace_size(ctypes.byref(_shape(b=1, hq=8, hkv=2, s=64 * 256, d=128))) == 256
+    assert lib.seer_attn_workspace_size(ctypes.byref(_shape(b=1, hq=8, hkv=2, s=64 * 512, d=64))) == 256
     # rows of more than 1024 blocks are cut into key chunks of 512 blocks: chunk
     # c holds the rows with query block >= 512 c (1100 + 588 + 76 rows per query
     # head); each (row, chunk) item reserves a 64 x (D + 1) fp32 partial

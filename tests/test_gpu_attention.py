@@ -119,6 +119,54 @@ def test_llama8b_s8k_50_sampled():
     check_lse(got_l, np.concatenate(l_ref), "8k LSE (sampled)")
 
 
+def _xcd_balanced(mask):
+    """Whether the per-XCD active causal tiles of the XCD-major row order (XCD
+    x owns the flattened heads [x BH/8, (x+1) BH/8)) are within 1.2 x their mean."""
+    B, H, nb, _ = mask.shape
+    per_head = (np.tril(np.ones((nb, nb), dtype=bool)) & (mask != 0)).reshape(B * H, nb, nb).sum(axis=(1, 2))
+    load = per_head.reshape(8, -1).sum(axis=1)
+    return 5 * 8 * int(load.max()) <= 6 * int(load.sum())
+
+
+XCD_MAJOR_CASES = [
+    ("d128_s2387_h16", Shape(1, 16, 4, 64 * 37 + 19, 128), torch.bfloat16),
+    ("d64_s2887_b2_h8", Shape(2, 8, 2, 64 * 45 + 7, 64), torch.float32),
+]
+
+
+@pytest.mark.parametrize("name,shape,dt", XCD_MAJOR_CASES, ids=[c[0] for c in XCD_MAJOR_CASES])
+def test_sparse_xcd_major_order(name, shape, dt):
+    """Short rows with batch x heads a multiple of 8 run in the order a pre-pass
+    picks from the mask: XCD-major when the per-XCD work is balanced, the
+    key-chunked order otherwise (host-side counts below confirm which side of
+    the threshold each mask is on). Both runs are checked against the oracle.
+    A row's tiles are summed in a rotation phased by its workgroup index, so
+    the heads the two masks share agree to rounding, not bitwise."""
+    seer = _seer()
+    seed = 70 + shape.head_dim
+    nb = shape.nb
+    bal = synth.gen_random_upper_noise(synth.gen_block_mask(shape, seed + 1, 0.7).mask, seed + 2)
+    bal[0, 3, nb - 1, :] = 0                      # an empty row
+    imb = bal.copy()
+    per = shape.batch * shape.heads_q // 8        # flattened heads of XCD 0 in that order: dense
+    flat = imb.reshape(-1, nb, nb)
+    flat[:per] = np.tril(np.ones((nb, nb), dtype=np.uint8))
+    assert _xcd_balanced(bal) and not _xcd_balanced(imb)
+    q, k, v = synth.gen_qkv(shape, seed)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    outs = []
+    for what, m in (("balanced", bal), ("imbalanced", imb)):
+        say(f"[{name} {what}] shape={shape} seed={seed} out={dt}")
+        out, lse = seer.seer_block_sparse_attn_fwd(qd, kd, vd, dev_u8(m), out_dtype=dt, want_lse=True)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention(q, k, v, m)
+        check_close(host(out), o_ref, f"{name} {what} O", out_dtype=dt)
+        check_lse(host(lse), l_ref, f"{name} {what} LSE")
+        outs.append(host(out).reshape(-1, shape.seq_len, shape.head_dim))
+    check_close(outs[0][per:], outs[1][per:], f"{name} shared heads, both orders", max_abs=1e-2, mean_abs=1e-4,
+                out_dtype=dt)
+
+
 def _chunk_boundary_rows(B, H, nb, seed, chunk=512):
     """Sampled rows plus every query block next to a key-chunk boundary."""
     extra = [x for c in range(chunk, nb, chunk) for x in (c - 1, c, c + 1) if x < nb]
