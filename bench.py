@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "block-sparse prefill ms, TFLOP/s & speedup vs dense at 128k/90% sparsity"
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 matrix (published)
 
 
 def parse():
@@ -539,6 +540,15 @@ def main():
     # the gate call's compulsory HBM bytes: Q and K read once (bf16) and the
     # u8 mask written once
     gate_bytes = 2 * B * S * D * (Hq + Hkv) + B * Hq * nb * nb
+    # the gate's fp32 matrix work: the projections Q' = Qp W_q (D -> Dg per
+    # query head) and K' = Kp W_k (3D -> Dg per W_k head), and the causal block
+    # logits Q' K'^T. Its kernels run one after another (pool, projections,
+    # logits, softmax / top-k), the HBM-bound ones moving the compulsory bytes
+    # and the matrix ones doing this work, so the call takes at least
+    # bytes / HBM peak + flop / fp32 matrix peak
+    hwk = wk_np.shape[0]
+    gate_flop = 2 * B * nb * dg * (Hq * D + hwk * 3 * D) + 2 * B * Hq * (nb * (nb + 1) // 2) * dg
+    gate_bound_ms = gate_bytes / (PEAK_HBM_GBS * 1e6) + gate_flop / (PEAK_FP32_MFMA_TFLOPS * 1e9)
     rec = {
         "metric": METRIC,
         "value": round(sparse_flop / ms_step / 1e9, 3),
@@ -592,7 +602,11 @@ def main():
                  "ms": round(gate_avg, 4), "bound": "hbm",
                  "compulsory_bytes": gate_bytes,
                  "achieved": round(gate_bytes / gate_avg / 1e6, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                 "frac": round(gate_bytes / gate_avg / 1e6 / PEAK_HBM_GBS, 4)},
+                 "frac": round(gate_bytes / gate_avg / 1e6 / PEAK_HBM_GBS, 4),
+                 "fp32_matrix_flop": gate_flop,
+                 "time_bound_ms": round(gate_bound_ms, 4),
+                 "time_bound": "compulsory bytes at the HBM peak plus the fp32 matrix work at its peak, in sequence",
+                 "frac_of_time_bound": round(gate_bound_ms / gate_avg, 4)},
         "decode": decode,
         "varlen": varlen,
         "peak_computed": peak,

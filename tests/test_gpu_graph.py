@@ -1,7 +1,8 @@
 """HIP graph capture of the hot path: a decode step (compressed-K update,
-decode gate, block-sparse decode attention) and a prefill step (gate, then
-block-sparse attention on the XCD-owned persistent path) captured once and
-replayed several times, with eager work between the replays; every replay
+decode gate, block-sparse decode attention) and prefill steps (gate, then
+block-sparse attention on the XCD-owned persistent path, and on short rows in
+the XCD-major order with its balance pre-pass) captured once and replayed
+several times, with eager work between the replays; every replay
 must give the eager call's bits (the kernels are deterministic and clear
 their own counters with a kernel, not a memset)."""
 import numpy as np
@@ -89,3 +90,31 @@ def test_graph_prefill_step_xcd_path():
         seer.seer_block_sparse_attn_fwd(qq, kk, vv, mask, out=out, workspace=aws)
 
     _replay_and_check(step, [mask, scores, out], "prefill")
+
+
+def test_graph_prefill_step_xcd_major_rows():
+    """Short rows (128 blocks, 32 heads): the gate's uniform top-k mask gives
+    every head the same work, so the pre-pass's per-XCD counts are balanced
+    and the rows run in the XCD-major order; the counts are cleared by a
+    kernel inside the captured step."""
+    seer = _seer()
+    shape = Shape(1, 32, 8, 8192, 128)
+    say(f"[graph prefill xcd-major] shape={shape}")
+    assert seer.attn_workspace_bytes(1, shape.heads_q, shape.heads_kv, shape.seq_len, shape.head_dim) == 256
+    q, k, v = synth.gen_qkv(shape, 305)
+    wq, wk = synth.gen_gate_weights(shape.heads_q, shape.head_dim, 128, 306)
+    qq, kk, vv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    wqd, wkd = dev_f32(wq), dev_f32(wk)
+    nb = shape.nb
+    mask = torch.empty((1, shape.heads_q, nb, nb), dtype=torch.uint8, device="cuda")
+    gws = torch.empty(seer.gate_workspace_bytes(1, shape.heads_q, shape.heads_kv, shape.seq_len, shape.head_dim, 128,
+                                                want_scores=False), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(qq)
+    aws = torch.empty(256, dtype=torch.uint8, device="cuda")
+
+    def step():
+        seer.seer_gate_fwd(qq, kk, wqd, wkd, rope_theta=500000.0, mode="topk", topk=nb // 4, want_scores=False,
+                           block_mask=mask, workspace=gws)
+        seer.seer_block_sparse_attn_fwd(qq, kk, vv, mask, out=out, workspace=aws)
+
+    _replay_and_check(step, [mask, out], "prefill xcd-major")
