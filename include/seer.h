@@ -172,8 +172,11 @@ seer_status seer_gate_distill_bwd(const seer_shape* shape, int32_t gate_dim, int
  *              take 256 bytes: a pre-pass counts the mask's active tiles per
  *              XCD of the XCD-major row order (each XCD takes an eighth of
  *              the heads), which is used when those counts are balanced.
- *              Otherwise the size is 0, and workspace may be NULL, when
- *              seq_len <= 65536. The active blocks of each row are
+ *              Rows of 257 to 1024 blocks at head_dim 128 with
+ *              batch * heads_q * blocks >= 8192 also take 256 bytes: the
+ *              per-XCD row queues of a persistent launch, which every call
+ *              resets. Otherwise the size is 0, and workspace may be NULL,
+ *              when seq_len <= 65536. The active blocks of each row are
  *              compacted on chip.
  * ---------------------------------------------------------------------- */
 size_t seer_attn_workspace_size(const seer_shape* shape);

@@ -169,12 +169,22 @@ __device__ __forceinline__ void tile_update(const f32x16_t (&sacc)[2], const u32
     }
 }
 
+// Called twice per row: hook(0) during the row's last tile, once its V copy is
+// issued (at the end of a row without tiles), and hook(1) before the row's
+// output stores. attn_sparse_rows_kernel claims its next row at the first
+// and hands the claim to its workgroup at the second. The other kernels pass
+// nothing.
+struct NoRowHook {
+  __device__ void operator()(int) const {}
+};
+
 // One (batch, query head, query block) row -- or one key chunk of it -- of
-// the tile loop below. `w` is the row's workgroup index in the launch the
-// block-sparse circular sweep is phased by (see the sweep below).
-template <int D, int MODE>
+// the tile loop below. `w` is the row's workgroup index in the launch (its
+// claim index in a persistent launch) the block-sparse circular sweep is
+// phased by (see the sweep below).
+template <int D, int MODE, typename Hook = NoRowHook>
 __device__ __forceinline__ void attn_row(const AttnArgs& p, const int w, const int qb, const int bh,
-                                         const int chunk) {
+                                         const int chunk, Hook hook = Hook{}) {
   constexpr int CPR = D / 8;               // 16-byte chunks per K/V row
   constexpr int KS = D / 16;               // MFMA k-steps for S^T
   constexpr int MT = D / 32;               // MFMA m-tiles for O^T
@@ -295,6 +305,7 @@ __device__ __forceinline__ void attn_row(const AttnArgs& p, const int w, const i
     u32x4_t kr[2 * KS];                           // kr[2 ks + mt]: keys 32 mt + l32, dims 16 ks + 8 hl ..
     read_k_issue<D>(kaddr, kr);
     issue_v(kb);
+    if (next < 0) hook(0);                         // the row's last tile
     read_k_wait<D>(kr);
 
     f32x16_t sacc[2];
@@ -394,12 +405,14 @@ __device__ __forceinline__ void attn_row(const AttnArgs& p, const int w, const i
         kb = next;
       }
     }
+    if (cnt == 0 && !diag_on) hook(0);
   } else {
     compute(std::true_type{}, qb, qb > 0 ? 0 : -1);
     for (int kb = 0; kb < qb; ++kb) compute(std::false_type{}, kb, kb + 1 < qb ? kb + 1 : -1);
   }
 
   // ---- epilogue: normalize, store O and LSE --------------------------------
+  hook(1);
   const float ltot = pair_sum(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   const float lse2 = ltot > 0.f ? m + __log2f(ltot) : -INFINITY;
@@ -485,6 +498,94 @@ __global__ __launch_bounds__(256) void attn_xcd_work_kernel(AttnArgs p) {
   __syncthreads();
   if (threadIdx.x == 0)
     atomicAdd(p.xcd_work + bh / (p.B * p.Hq / kXcds), part[0] + part[1] + part[2] + part[3]);
+}
+
+// Block-sparse rows of one item in a persistent launch: kRowSlots
+// workgroups per XCD (its resident capacity). Queue y holds the rows of the
+// flattened heads [h0(y), h0(y+1)), h0(y) = y B Hq / 8, query block descending
+// with the heads interleaved, and the workgroups of XCD x take their rows from
+// queue x in order, so each XCD's L2 serves its own heads' KV groups. Slot s
+// starts with row s of its queue (the counters start at kRowSlots); each later
+// row is claimed from a per-queue counter during the current row's last tile.
+// A workgroup whose queue has run dry takes its rows from the queue with the
+// most rows left (the heads' masks can give one XCD half again the mean work),
+// and ends once every queue is dry.
+constexpr int kRowSlots = 128;             // resident workgroups per XCD: 32 CUs x 4
+__device__ __forceinline__ int rows_h0(const AttnArgs& p, int y) { return (y * p.B * p.Hq) / kXcds; }
+__device__ __forceinline__ int rows_queue_len(const AttnArgs& p, int y) {
+  return (rows_h0(p, y + 1) - rows_h0(p, y)) * p.nb;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_sparse_rows_kernel(AttnArgs p) {
+  constexpr int kNone = 0x7fffffff;
+  __shared__ int claim_s[2];
+  const int tid = threadIdx.x;
+  const int x = static_cast<int>(blockIdx.x % kXcds);
+  int y = x;                                       // the queue this workgroup claims from
+  int n = rows_queue_len(p, y);
+  int j = static_cast<int>(blockIdx.x / kXcds);    // its first row: row s of queue x
+  while (true) {
+    if (j >= n) {
+      // queue y is dry: wave 0 reads every queue's counter (device-scope
+      // loads: the counters move on other XCDs) and claims from the queue
+      // with the most rows left, or the workgroup ends
+      if (tid < kWave) {
+        int rem = -1;
+        if (tid < kXcds)
+          rem = rows_queue_len(p, tid) - __hip_atomic_load(p.xcd_ctr + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int best = rem, by = tid;
+#pragma unroll
+        for (int o = 1; o < kXcds; o <<= 1) {
+          const int ob = __shfl_xor(best, o), oy = __shfl_xor(by, o);
+          if (ob > best || (ob == best && oy < by)) {
+            best = ob;
+            by = oy;
+          }
+        }
+        if (tid == 0) {
+          claim_s[0] = by;
+          claim_s[1] = best > 0 ? atomicAdd(p.xcd_ctr + by, 1) : kNone;
+        }
+      }
+      __syncthreads();
+      y = __builtin_amdgcn_readfirstlane(claim_s[0]);
+      j = __builtin_amdgcn_readfirstlane(claim_s[1]);
+      __syncthreads();                             // both waves hold them before the LDS words are reused
+      if (j == kNone) return;
+      n = rows_queue_len(p, y);
+      continue;
+    }
+    const int h0 = rows_h0(p, y);
+    const int nh = rows_h0(p, y + 1) - h0;
+    const int i = j / nh;
+    int pend = 0;                                  // thread 0: the claim in flight
+    int* const cy = p.xcd_ctr + y;
+    auto hook = [&](int stage) {
+      if (tid != 0) return;
+      if (stage == 0) {
+        // an address the compiler cannot prove uniform: a uniform one makes
+        // it read the result back at once
+        int off = 0;
+        asm volatile("" : "+v"(off));
+        pend = atomicAdd(cy + off, 1);
+      } else {
+        claim_s[1] = pend;
+      }
+    };
+    attn_row<D, kSparse>(p, j * kXcds, p.nb - 1 - i, h0 + (j - i * nh), 0, hook);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wg_barrier();
+    j = __builtin_amdgcn_readfirstlane(static_cast<int>(lds_read_u32(lds_addr(&claim_s[1]))));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wg_barrier();                                  // both waves hold it before the LDS word is reused
+  }
+}
+
+// Counters of attn_sparse_rows_kernel: each queue's first kRowSlots rows are
+// the slots' first rows.
+__global__ void attn_rows_counters_init(int* ctr) {
+  if (threadIdx.x < kXcds) ctr[threadIdx.x] = kRowSlots;
 }
 
 template <int D, int MODE>
@@ -1391,6 +1492,13 @@ hipError_t launch_d(const AttnArgs& a, int mode, hipStream_t st) {
     }
     return hipGetLastError();
   }
+  if constexpr (D == 128) {
+    if (mode == kSparse && a.rows) {
+      hipLaunchKernelGGL(attn_rows_counters_init, dim3(1), dim3(kWave), 0, st, a.xcd_ctr);
+      hipLaunchKernelGGL((attn_sparse_rows_kernel<D>), dim3(kXcds * kRowSlots), block, 0, st, a);
+      return hipGetLastError();
+    }
+  }
   if (mode == kSparse) {
     if (a.xcd_work != nullptr) {
       hipLaunchKernelGGL(attn_xcd_counters_init, dim3(1), dim3(kWave), 0, st, a.xcd_work);
@@ -1460,12 +1568,17 @@ SparsePlan sparse_plan(int B, int Hkv, int group, int nb, int D) {
   // over the 8 XCDs; 256 bytes of per-XCD counts
   pl.xcd_rows = pl.nchunk == 1 && static_cast<long long>(nb) * D <= kXcdRowsMaxBlockDims &&
                 (static_cast<long long>(B) * Hkv * group) % kXcds == 0;
+  // longer one-item rows at D = 128 with at least 8 rows per resident
+  // workgroup: the persistent launch of attn_sparse_rows_kernel, 256 bytes of
+  // per-queue counters
+  pl.rows = pl.nchunk == 1 && D == 128 && static_cast<long long>(nb) * D > kXcdRowsMaxBlockDims &&
+            static_cast<long long>(B) * Hkv * group * nb >= 8LL * kXcds * kRowSlots;
   const long long nc = pl.nchunk;
   pl.items_per_group = static_cast<long long>(group) * (nc * nb - static_cast<long long>(pl.chunk) * nc * (nc - 1) / 2);
   if (nb > pl.chunk) {
     const size_t items = static_cast<size_t>(B) * Hkv * pl.items_per_group;
     pl.workspace_bytes = items * kBlock * (static_cast<size_t>(D) + 1) * sizeof(float);
-  } else if (pl.xcd_rows) {
+  } else if (pl.xcd_rows || pl.rows) {
     pl.workspace_bytes = 256;
   }
   return pl;

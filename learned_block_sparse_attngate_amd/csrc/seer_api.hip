@@ -596,6 +596,9 @@ static seer_status attn_impl(const seer_shape* shape, long long hs, const void* 
         a.xcd_ctr = reinterpret_cast<int*>(a.part_l + slots * 64);
       } else if (pl.xcd_rows) {
         a.xcd_work = static_cast<int*>(workspace);
+      } else if (pl.rows) {
+        a.rows = 1;
+        a.xcd_ctr = static_cast<int*>(workspace);
       } else {
         a.part_o = static_cast<float*>(workspace);
         a.part_l = a.part_o + static_cast<size_t>(items) * 64 * a.D;

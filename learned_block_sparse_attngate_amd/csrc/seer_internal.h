@@ -40,6 +40,7 @@ struct AttnArgs {
   // heads each XCD would own in the XCD-major order (counted by a pre-pass);
   // nullptr: that order is not considered
   int* xcd_work;
+  int rows;            // block-sparse: one-item rows in the persistent launch (attn_sparse_rows_kernel, xcd_ctr)
 };
 
 // mode: 0 block-sparse (mask), 1 dense causal, 2 dense causal + ground-truth maxima
@@ -73,6 +74,7 @@ struct SparsePlan {
   int njobs;                  // XCD path: (batch, KV group, chunk) jobs
   long long slots_per_head;   // XCD path: partial slots per (batch, head)
   int xcd_rows;               // one-item rows: the XCD-major order is taken when the mask's work is balanced
+  int rows;                   // one-item rows in a persistent launch with per-XCD queues and stealing
   size_t workspace_bytes;
 };
 SparsePlan sparse_plan(int B, int Hkv, int group, int nb, int D);

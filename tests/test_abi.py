@@ -265,6 +265,12 @@ def test_workspace_sizes():
         assert lib.seer_attn_workspace_size(ctypes.byref(_shape(b=b0, hq=hq0, hkv=hq0 // 4, s=s0, d=d0))) == 0
     assert lib.seer_attn_workspace_size(ctypes.byref(_shape(b=1, hq=8, hkv=2, s=64 * 256, d=128))) == 256
     assert lib.seer_attn_workspace_size(ctypes.byref(_shape(b=1, hq=8, hkv=2, s=64 * 512, d=64))) == 256
+    # one-item rows over 256 blocks at D = 128 with >= 8 rows per resident
+    # workgroup (8 x 1024): the persistent launch's 8 queue counters
+    assert lib.seer_attn_workspace_size(ctypes.byref(_shape(b=1, hq=32, hkv=8, s=64 * 300, d=128))) == 256
+    assert lib.seer_attn_workspace_size(ctypes.byref(_shape(b=1, hq=32, hkv=8, s=64 * 1024, d=128))) == 256
+    assert lib.seer_attn_workspace_size(ctypes.byref(_shape(b=1, hq=8, hkv=2, s=64 * 300, d=128))) == 0
+    assert lib.seer_attn_workspace_size(ctypes.byref(_shape(b=1, hq=32, hkv=8, s=64 * 600, d=64))) == 0
     # rows of more than 1024 blocks are cut into key chunks of 512 blocks: chunk
     # c holds the rows with query block >= 512 c (1100 + 588 + 76 rows per query
     # head); each (row, chunk) item reserves a 64 x (D + 1) fp32 partial

@@ -167,6 +167,40 @@ def test_sparse_xcd_major_order(name, shape, dt):
                 out_dtype=dt)
 
 
+ROWS_CASES = [
+    # one-item rows of more than 256 blocks at D = 128 with at least 8 rows per
+    # resident workgroup: the persistent launch with per-XCD queues and stealing
+    ("d128_s19217_h32_bf16", Shape(1, 32, 8, 64 * 300 + 17, 128), torch.bfloat16),
+    ("d128_s33000_b2_h16_f32", Shape(2, 16, 4, 64 * 515 + 40, 128), torch.float32),
+]
+
+
+@pytest.mark.parametrize("name,shape,dt", ROWS_CASES, ids=[c[0] for c in ROWS_CASES])
+def test_sparse_persistent_rows(name, shape, dt):
+    """Per-head sparsity in [0.8, 0.97] and the heads of the first queue fully
+    dense, so the other workgroups run dry early and take rows from that queue;
+    an empty row, a row active only on its diagonal and one without its
+    diagonal, a ragged last block. Sampled rows, every head, against the oracle."""
+    seed = 90 + shape.batch
+    nb = shape.nb
+    bh = shape.batch * shape.heads_q
+    rng = np.random.Generator(np.random.PCG64(seed))
+    s_heads = synth.per_head_sparsity(bh, 0.8, 0.97, 0.9, rng).reshape(shape.batch, shape.heads_q)
+    m = synth.gen_block_mask(shape, seed + 1, s_heads).mask.copy()
+    per = bh // 8                                  # flattened heads of queue 0
+    flat = m.reshape(-1, nb, nb)
+    flat[:per] = np.tril(np.ones((nb, nb), dtype=np.uint8))
+    b1, h1 = divmod(per, shape.heads_q)            # the first head of queue 1
+    m[b1, h1, nb - 1, :] = 0                       # no active key: O = 0, LSE = -inf
+    m[b1, h1 + 1, 200, :] = 0
+    m[b1, h1 + 1, 200, 200] = 1                    # only the diagonal
+    m[b1, h1 + 2, nb - 2, nb - 2] = 0              # diagonal off
+    m = synth.gen_random_upper_noise(m, seed + 2)
+    rows = sample_rows(shape.batch, shape.heads_q, nb, 2, seed + 3)
+    rows += [(b1, h1, nb - 1), (b1, h1 + 1, 200), (b1, h1 + 2, nb - 2)]
+    _run_sampled(shape, seed, m, dt, sorted(set(rows)), name)
+
+
 def _chunk_boundary_rows(B, H, nb, seed, chunk=512):
     """Sampled rows plus every query block next to a key-chunk boundary."""
     extra = [x for c in range(chunk, nb, chunk) for x in (c - 1, c, c + 1) if x < nb]
