@@ -134,6 +134,19 @@ XCD_MAJOR_CASES = [
 ]
 
 
+@pytest.mark.parametrize("shape,dt", [(Shape(1, 8, 2, 16384, 128), torch.bfloat16),
+                                      (Shape(1, 8, 8, 64 * 512 - 5, 64), torch.float32)],
+                         ids=["d128_s16384_nb256", "d64_s32763_nb512"])
+def test_sparse_xcd_major_longest_rows(shape, dt):
+    """The longest rows the XCD-major order takes (256 blocks at D = 128, 512
+    at D = 64) on a balanced mask, sampled rows against the oracle."""
+    seed = 75 + shape.head_dim
+    m = synth.gen_random_upper_noise(synth.gen_block_mask(shape, seed + 1, 0.85).mask, seed + 2)
+    assert _xcd_balanced(m)
+    rows = sample_rows(shape.batch, shape.heads_q, shape.nb, 3, seed + 3)
+    _run_sampled(shape, seed, m, dt, rows, f"xcd-major {shape.seq_len}")
+
+
 @pytest.mark.parametrize("name,shape,dt", XCD_MAJOR_CASES, ids=[c[0] for c in XCD_MAJOR_CASES])
 def test_sparse_xcd_major_order(name, shape, dt):
     """Short rows with batch x heads a multiple of 8 run in the order a pre-pass
@@ -172,6 +185,10 @@ ROWS_CASES = [
     # resident workgroup: the persistent launch with per-XCD queues and stealing
     ("d128_s19217_h32_bf16", Shape(1, 32, 8, 64 * 300 + 17, 128), torch.bfloat16),
     ("d128_s33000_b2_h16_f32", Shape(2, 16, 4, 64 * 515 + 40, 128), torch.float32),
+    # the longest one-item rows (1024 blocks), one head per queue
+    ("d128_s65536_h8_bf16", Shape(1, 8, 2, 65536, 128), torch.bfloat16),
+    # 12 heads: queues of one or two heads
+    ("d128_s44800_h12_bf16", Shape(1, 12, 3, 64 * 700, 128), torch.bfloat16),
 ]
 
 
