@@ -573,7 +573,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_rows_kernel(AttnArgs 
         claim_s[1] = pend;
       }
     };
-    attn_row<D, kSparse>(p, j * kXcds, p.nb - 1 - i, h0 + (j - i * nh), 0, hook);
+    // the sweep's phase is the claim index modulo the resident slots
+    attn_row<D, kSparse>(p, (j % kSweepPhases) * kXcds, p.nb - 1 - i, h0 + (j - i * nh), 0, hook);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     wg_barrier();
     j = __builtin_amdgcn_readfirstlane(static_cast<int>(lds_read_u32(lds_addr(&claim_s[1]))));
@@ -606,14 +607,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs p) {
   if constexpr (MODE == kSparse) {
     if (p.xcd_work != nullptr) {
       // balanced when the most loaded XCD has at most 1.2 x the mean
-      int mx = 0, sum = 0;
+      long long mx = 0, sum = 0;
 #pragma unroll
       for (int x = 0; x < kXcds; ++x) {
-        const int cx = p.xcd_work[x];
+        const long long cx = static_cast<unsigned>(p.xcd_work[x]);
         mx = max(mx, cx);
         sum += cx;
       }
-      xcd_major = 5 * kXcds * static_cast<long long>(mx) <= 6 * static_cast<long long>(sum);
+      xcd_major = 5 * kXcds * mx <= 6 * sum;
     }
   }
   if (MODE == kSparse && xcd_major) {
