@@ -261,7 +261,11 @@ __device__ __forceinline__ void gate_proj_body(const GateArgs& a, const int bx, 
 }
 
 __global__ __launch_bounds__(kGT) void gate_proj_kernel(GateArgs a) {
-  gate_proj_body(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  // the K' projections (3D deep) are dispatched first, the Q' ones (D deep)
+  // fill in after them
+  const int nq = a.B * a.Hq, nk = static_cast<int>(gridDim.z) - nq;
+  const int z = static_cast<int>(blockIdx.z) < nk ? nq + static_cast<int>(blockIdx.z) : static_cast<int>(blockIdx.z) - nk;
+  gate_proj_body(a, blockIdx.x, blockIdx.y, z);
 }
 
 // Causal 64 x 64 tiles of the block logits z = Q' K'^T / sqrt(D). One
@@ -1045,8 +1049,10 @@ __global__ __launch_bounds__(kRowWaves * kWave) void decode_gate_kernel(DecodeGa
 // -1 rotates back (the transpose, used by the gradient).
 // ---------------------------------------------------------------------------
 constexpr int kRopeRows = 8;               // rows rotated per thread with one angle
-__global__ __launch_bounds__(256) void gate_rope_kernel(float* __restrict__ x, int rows, int nb, int dg,
-                                                        double base, double sign) {
+// rows kRopeRows zy .. of x [rows][nb][dg]: one thread per (block position i,
+// pair d) computes the fp64 angle once and rotates that pair in each row
+__device__ __forceinline__ void rope_rows(float* __restrict__ x, int rows, int nb, int dg, double base, double sign,
+                                          int zy) {
   const int half = dg / 2;
   const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;   // over nb * half
   if (idx >= static_cast<long long>(nb) * half) return;
@@ -1054,7 +1060,7 @@ __global__ __launch_bounds__(256) void gate_rope_kernel(float* __restrict__ x, i
   const double ang = sign * static_cast<double>(i) * pow(base, -2.0 * d / dg);
   double sn, cs;
   sincos(ang, &sn, &cs);
-  const int z0 = blockIdx.y * kRopeRows;
+  const int z0 = zy * kRopeRows;
   float x1[kRopeRows], x2[kRopeRows];
 #pragma unroll
   for (int u = 0; u < kRopeRows; ++u) {
@@ -1069,6 +1075,16 @@ __global__ __launch_bounds__(256) void gate_rope_kernel(float* __restrict__ x, i
     r[d] = static_cast<float>(static_cast<double>(x1[u]) * cs - static_cast<double>(x2[u]) * sn);
     r[d + half] = static_cast<float>(static_cast<double>(x2[u]) * cs + static_cast<double>(x1[u]) * sn);
   }
+}
+
+// Q' (rows0 rows at x0) and K' (rows1 rows at x1) in one launch: grid.y
+// covers x0's row groups, then x1's
+__global__ __launch_bounds__(256) void gate_rope_kernel(float* __restrict__ x0, int rows0, float* __restrict__ x1,
+                                                        int rows1, int nb, int dg, double base, double sign) {
+  const int ty0 = (rows0 + kRopeRows - 1) / kRopeRows;
+  const int zy = static_cast<int>(blockIdx.y);
+  if (zy < ty0) rope_rows(x0, rows0, nb, dg, base, sign, zy);
+  else rope_rows(x1, rows1, nb, dg, base, sign, zy - ty0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1385,10 +1401,10 @@ __global__ __launch_bounds__(256) void gate_softmax_mask_varlen_kernel(GateArgs 
                            i + 1, b.nb, b.mode, b.threshold, tk.k[z], vec, !b.skip_scores, hist_all[wave]);
 }
 
-hipError_t launch_rope(const GateArgs& a, float* x, int rows, double sign, hipStream_t st) {
+hipError_t launch_rope(const GateArgs& a, float* x0, int rows0, float* x1, int rows1, double sign, hipStream_t st) {
   const long long n = static_cast<long long>(a.nb) * (a.Dg / 2);
-  dim3 g(static_cast<unsigned>((n + 255) / 256), (rows + kRopeRows - 1) / kRopeRows);
-  hipLaunchKernelGGL(gate_rope_kernel, g, dim3(256), 0, st, x, rows, a.nb, a.Dg, a.rope_base, sign);
+  dim3 g(static_cast<unsigned>((n + 255) / 256), (rows0 + kRopeRows - 1) / kRopeRows + (rows1 + kRopeRows - 1) / kRopeRows);
+  hipLaunchKernelGGL(gate_rope_kernel, g, dim3(256), 0, st, x0, rows0, x1, rows1, a.nb, a.Dg, a.rope_base, sign);
   return hipGetLastError();
 }
 
@@ -1407,8 +1423,7 @@ hipError_t launch_gate_logits(const GateArgs& a, hipStream_t st) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   if (a.rope_base > 0.0) {
-    if ((e = launch_rope(a, a.qg, a.B * a.Hq, 1.0, st)) != hipSuccess) return e;
-    if ((e = launch_rope(a, a.kg, a.B * hwk, 1.0, st)) != hipSuccess) return e;
+    if ((e = launch_rope(a, a.qg, a.B * a.Hq, a.kg, a.B * hwk, 1.0, st)) != hipSuccess) return e;
   }
 
   const int T = (a.nb + kBM - 1) / kBM;
@@ -1516,8 +1531,7 @@ hipError_t launch_gate_distill(const GateArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(gate_dproj_kernel, gd, dim3(kGT), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.rope_base > 0.0) {
-    if ((e = launch_rope(a, a.dqg, nq, -1.0, st)) != hipSuccess) return e;
-    if ((e = launch_rope(a, a.dkg, nq, -1.0, st)) != hipSuccess) return e;
+    if ((e = launch_rope(a, a.dqg, nq, a.dkg, nq, -1.0, st)) != hipSuccess) return e;
   }
   const int hwk = a.wk_per_kv ? a.Hkv : a.Hq;
   dim3 gw((3 * a.D + kBM - 1) / kBM, (a.Dg + kBN - 1) / kBN, a.Hq + hwk);
