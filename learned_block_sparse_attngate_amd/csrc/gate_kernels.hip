@@ -569,6 +569,13 @@ __device__ __forceinline__ void wave_softmax_mask_row(float* srow, uint8_t* mrow
 #pragma unroll
         for (int e = 0; e < 4; ++e) kmax = max(kmax, static_cast<int32_t>(key[t][e]));
     int lo = 0, hi = wave_max_int(kmax) >> 23;          // count(>= 2^lo) = n >= k; the answer is <= hi
+    // the k-th largest usually lies within 16 binades of the largest: one
+    // count there first halves the search in that case (either branch keeps
+    // the invariant, so the result is the same)
+    if (hi > 16) {
+      if (count_ge((hi - 16) << 23) >= k) lo = hi - 16;
+      else hi = hi - 17;
+    }
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (count_ge(mid << 23) >= k) lo = mid;
