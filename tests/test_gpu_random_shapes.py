@@ -100,3 +100,49 @@ def test_random_shape_gate(name, shape, seed, p, dt):
                 kth = np.partition(row, i + 1 - n)[i + 1 - n]
                 outside = np.abs(row - kth) > MASK_BAND
                 assert not ((got_k[b, h, i, :i + 1] != want_k[b, h, i, :i + 1]) & outside).any()
+
+
+def _draw_long_cases(n, seed):
+    """Rows long enough for the persistent row queues (257-1024 blocks at
+    D = 128 with >= 8 rows per resident workgroup) or the XCD-major order
+    (up to 256 blocks, batch x heads a multiple of 8)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        hkv = int(rng.choice([2, 4, 8]))
+        g = int(rng.choice([1, 2, 4]))
+        b = int(rng.choice([1, 2]))
+        long_rows = i % 2 == 0
+        s = int(rng.integers(64 * 257, 64 * 1024 + 1)) if long_rows else int(rng.integers(64 * 64, 64 * 256 + 1))
+        while long_rows and b * hkv * g * ((s + 63) // 64) < 8192:
+            g *= 2
+        while not long_rows and (b * hkv * g) % 8 != 0:
+            g *= 2
+        p = float(rng.choice([0.05, 0.1, 0.3]))
+        dt = torch.float32 if rng.random() < 0.5 else torch.bfloat16
+        cases.append((f"L{i}_b{b}_h{hkv * g}x{hkv}_s{s}_p{p}", Shape(b, hkv * g, hkv, s, 128), 700 + i, p, dt))
+    return cases
+
+
+LONG_CASES = _draw_long_cases(6, 2025)
+
+
+@pytest.mark.parametrize("name,shape,seed,p,dt", LONG_CASES, ids=[c[0] for c in LONG_CASES])
+def test_random_long_rows_attention(name, shape, seed, p, dt):
+    """Random masks on the long-row schedules; sampled query blocks of every
+    head against the oracle."""
+    from gpu_util import sample_rows
+    seer = _seer()
+    say(f"[random long rows {name}] shape={shape} seed={seed} out={dt} "
+        f"workspace={seer.attn_workspace_bytes(shape.batch, shape.heads_q, shape.heads_kv, shape.seq_len, 128)}")
+    q, k, v = synth.gen_qkv(shape, seed)
+    m = _mask(shape, seed, p)
+    out, lse = seer.seer_block_sparse_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_u8(m), out_dtype=dt,
+                                               want_lse=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(shape.batch, shape.heads_q, shape.nb, 1, seed + 2)
+    got = np.concatenate([host(out[b, h, 64 * i:64 * i + 64]) for (b, h, i) in rows])
+    got_l = np.concatenate([host(lse[b, h, 64 * i:64 * i + 64]) for (b, h, i) in rows])
+    o_ref, l_ref = oracle.attention_rows(q, k, v, m, rows)
+    check_close(got, np.concatenate(o_ref), f"{name} O (sampled)", out_dtype=dt)
+    check_lse(got_l, np.concatenate(l_ref), f"{name} LSE (sampled)")
