@@ -169,6 +169,102 @@ __device__ __forceinline__ void tile_update(const f32x16_t (&sacc)[2], const u32
     }
 }
 
+// The block-sparse kernels split tile_scores / tile_update by the tile's place
+// in the row. The row's first tile (m = -inf on entry, the diagonal when it
+// is active) takes its maximum, which becomes m, and skips the rescale of the
+// still-zero accumulators. A later tile skips its maximum unless it could move
+// m: P = exp2(s c - m) is computed under the current m first, and only when
+// some lane's probabilities sum past kLazyCheck is the maximum taken and the
+// rescale rule of tile_update applied (and P recomputed if m moved). A score
+// that exceeds m by the slack (8) has P > 2^7.9 > kLazyCheck, so every tile
+// that tile_update would rescale takes that branch, and every other tile
+// keeps the P it computed under the unchanged m: the results are bitwise those
+// of tile_scores + tile_update, with 16 v_max3, the pair max, the scaling and
+// the compare gone from most tiles.
+constexpr float kLazyCheck = 64.0f;
+
+// S^T = K Q^T for one tile without its row maximum.
+template <int D>
+__device__ __forceinline__ void tile_qk(const u32x4_t (&kr)[D / 8], const uint4 (&qreg)[D / 16],
+                                        f32x16_t (&sacc)[2]) {
+  sacc[0] = f32x16_t{};
+  sacc[1] = f32x16_t{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      sacc[mt] = mfma_32x32x16(__builtin_bit_cast(uint4, kr[2 * ks + mt]), qreg[ks], sacc[mt]);
+}
+
+// P = exp2(s c - m) packed to bf16 in the B-operand layout of O^T = V^T P^T
+// (the order of tile_update), and the lane's sum of P
+__device__ __forceinline__ float tile_probs(const f32x16_t (&sacc)[2], float c, float m, uint4 (&pb)[4]) {
+  float ls = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float e[8];
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8) {
+        e[s8] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][8 * hh + s8], c, -m));
+        ls += e[s8];
+      }
+      pb[2 * mt + hh] = make_uint4(pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
+                                   pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7]));
+    }
+  }
+  return ls;
+}
+
+template <int D>
+__device__ __forceinline__ void tile_pv(const u32x2_t (&vr)[D / 4], const uint4 (&pb)[4], f32x16_t (&oacc)[D / 32]) {
+  constexpr int MT = D / 32;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x2_t lo = vr[(ks * MT + mt) * 2], hi = vr[(ks * MT + mt) * 2 + 1];
+      oacc[mt] = mfma_32x32x16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[ks], oacc[mt]);
+    }
+}
+
+// First tile of a row: m = -inf, lsum = 0 and oacc = 0 on entry; mx is the
+// tile's maximum from tile_scores (finite: the row's first tile holds a
+// causal key for every query). Leaves P in pb.
+__device__ __forceinline__ void tile_softmax_first(const f32x16_t (&sacc)[2], float mx, float c, float& m,
+                                                   float& lsum, uint4 (&pb)[4]) {
+  m = mx;
+  lsum = tile_probs(sacc, c, m, pb);
+}
+
+// A later tile of a row (see kLazyCheck). Leaves P in pb.
+template <int D>
+__device__ __forceinline__ void tile_softmax_lazy(const f32x16_t (&sacc)[2], float c, float& m, float& lsum,
+                                                  f32x16_t (&oacc)[D / 32], uint4 (&pb)[4]) {
+  constexpr int MT = D / 32;
+  float ls = tile_probs(sacc, c, m, pb);
+  if (__builtin_amdgcn_ballot_w64(ls > kLazyCheck)) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
+    mx = pair_max(mx) * c;
+    const bool upd = mx > m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(upd)) {
+      const float mn = upd ? mx : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < MT; ++i) oacc[i] *= alpha;
+      m = mn;
+      ls = tile_probs(sacc, c, m, pb);
+    }
+  }
+  lsum += ls;
+}
+
 // Called twice per row: hook(0) during the row's last tile, once its V copy is
 // issued (at the end of a row without tiles), and hook(1) before the row's
 // output stores. attn_sparse_rows_kernel claims its next row at the first
@@ -298,8 +394,14 @@ __device__ __forceinline__ void attn_row(const AttnArgs& p, const int w, const i
   // issued while the wave's operand reads from LDS are in flight. Both waits
   // are for everything outstanding: the ground-truth row-max store of a tile
   // is issued after the second one, so the next tile's first wait covers it.
-  auto compute = [&](auto diag_tag, int kb, int next) {
+  // kFirst: the row's first tile (the diagonal when it is active), which sets
+  // the running max; later tiles take their maximum only when it could move
+  // it (tile_softmax_lazy), except in ground-truth mode, which records every
+  // tile's maximum.
+  auto compute = [&](auto diag_tag, auto first_tag, int kb, int next) {
     constexpr bool kDiag = decltype(diag_tag)::value;   // the diagonal tile needs element causality
+    constexpr bool kFirst = decltype(first_tag)::value;
+    constexpr bool kLazy = MODE != kDenseGt && !kFirst;
     wait_vm(0);                                    // K(kb) landed, and every copy and store before it
     wg_barrier();
     u32x4_t kr[2 * KS];                           // kr[2 ks + mt]: keys 32 mt + l32, dims 16 ks + 8 hl ..
@@ -309,7 +411,16 @@ __device__ __forceinline__ void attn_row(const AttnArgs& p, const int w, const i
     read_k_wait<D>(kr);
 
     f32x16_t sacc[2];
-    const float mx = tile_scores<D, kDiag>(kr, qreg, sacc, q_local, hl, c);
+    float mx = 0.f;
+    uint4 pb[4];
+    if constexpr (kLazy) {
+      static_assert(!kDiag, "the diagonal tile is a row's first");
+      tile_qk<D>(kr, qreg, sacc);
+      tile_softmax_lazy<D>(sacc, c, m, lsum, oacc, pb);
+    } else {
+      mx = tile_scores<D, kDiag>(kr, qreg, sacc, q_local, hl, c);
+      if constexpr (kFirst) tile_softmax_first(sacc, mx, c, m, lsum, pb);
+    }
 
     wait_vm(0);                                    // V(kb) landed
     wg_barrier();
@@ -321,7 +432,8 @@ __device__ __forceinline__ void attn_row(const AttnArgs& p, const int w, const i
     if (next >= 0) issue_k(next);
     read_v_wait<D>(vr);
 
-    tile_update<D>(sacc, vr, mx, c, m, lsum, oacc);
+    if constexpr (kLazy || kFirst) tile_pv<D>(vr, pb, oacc);
+    else tile_update<D>(sacc, vr, mx, c, m, lsum, oacc);
   };
 
   // ---- main loop over active key blocks -----------------------------------
@@ -390,7 +502,7 @@ __device__ __forceinline__ void attn_row(const AttnArgs& p, const int w, const i
     bool issued = false;                        // the sweep's first tile already in flight
     if (diag_on) {
       const int nxt = cnt > 0 ? entry(0) : -1;
-      compute(std::true_type{}, qb, nxt);
+      compute(std::true_type{}, std::true_type{}, qb, nxt);
       issued = cnt > 0;
     } else if (has_diag) {
       wait_vm(0);                            // the early copy of the diagonal tile is not used
@@ -399,16 +511,23 @@ __device__ __forceinline__ void attn_row(const AttnArgs& p, const int w, const i
     if (cnt > 0) {
       int kb = entry(0);
       if (!issued) issue_k(kb);
-      for (int n = 0; n < cnt; ++n) {
+      int n = 0;
+      if (!diag_on) {                          // the sweep's first tile is the row's first
+        const int next = cnt > 1 ? entry(1) : -1;
+        compute(std::false_type{}, std::true_type{}, kb, next);
+        kb = next;
+        n = 1;
+      }
+      for (; n < cnt; ++n) {
         const int next = n + 1 < cnt ? entry(n + 1) : -1;
-        compute(std::false_type{}, kb, next);
+        compute(std::false_type{}, std::false_type{}, kb, next);
         kb = next;
       }
     }
     if (cnt == 0 && !diag_on) hook(0);
   } else {
-    compute(std::true_type{}, qb, qb > 0 ? 0 : -1);
-    for (int kb = 0; kb < qb; ++kb) compute(std::false_type{}, kb, kb + 1 < qb ? kb + 1 : -1);
+    compute(std::true_type{}, std::true_type{}, qb, qb > 0 ? 0 : -1);
+    for (int kb = 0; kb < qb; ++kb) compute(std::false_type{}, std::false_type{}, kb, kb + 1 < qb ? kb + 1 : -1);
   }
 
   // ---- epilogue: normalize, store O and LSE --------------------------------
@@ -1185,7 +1304,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
   // batch of copies is issued while the wave's operand reads from LDS are in
   // flight, which hides the time the copy instructions take to issue. `qn`:
   // load the next item's Q rows into qreg once this tile's scores are issued.
-  auto compute = [&](bool diag, size_t kvo_t, int kb_t, size_t nkv, int next, bool qn) {
+  // `first`: the item's first tile (the only one that can be the diagonal),
+  // which sets the running max; later tiles take their maximum only when it
+  // could move it (tile_update_lazy).
+  auto compute = [&](auto first_tag, bool diag, size_t kvo_t, int kb_t, size_t nkv, int next, bool qn) {
+    constexpr bool first = decltype(first_tag)::value;
     wait_vm(0);                                    // this tile's K landed (and everything before it)
     wg_barrier();
     u32x4_t kr[2 * KS];
@@ -1193,15 +1316,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
     issue_v(p.v + kvo_t, kb_t);
     read_k_wait<D>(kr);
     f32x16_t sacc[2];
-    const float mx = tile_scores_rt<D>(kr, qreg, sacc, q_local, hl, c, diag);
-    if (qn) load_q(it1, qreg);                     // qreg is free once the scores are issued
+    uint4 pb[4];
+    if constexpr (first) {
+      const float mx = tile_scores_rt<D>(kr, qreg, sacc, q_local, hl, c, diag);
+      if (qn) load_q(it1, qreg);                   // qreg is free once the scores are issued
+      tile_softmax_first(sacc, mx, c, m, lsum, pb);
+    } else {
+      tile_qk<D>(kr, qreg, sacc);
+      if (qn) load_q(it1, qreg);
+      tile_softmax_lazy<D>(sacc, c, m, lsum, oacc, pb);
+    }
     wait_vm(qn ? KS : 0);                          // this tile's V landed
     wg_barrier();
     u32x2_t vr[8 * MT];
     read_v_issue<D>(vaddr, vr);
     if (next >= 0) issue_k(p.k + nkv, next);
     read_v_wait<D>(vr);
-    tile_update<D>(sacc, vr, mx, c, m, lsum, oacc);
+    tile_pv<D>(vr, pb, oacc);
   };
 
   // ---- prologue: the first item is started cold ---------------------------
@@ -1254,17 +1385,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
     // to the next item (its first tile's copies and its Q rows)
     warm = false;
     if (kb >= 0) {
-      bool diag = kb == it.qb;
-      int cur_kb = kb;
+      const bool diag = kb == it.qb;
       int next = pop_flag(f0, f1, c0);
-      while (next >= 0) {
-        compute(diag, kvo, cur_kb, kvo, next, false);
-        diag = false;
-        cur_kb = next;
-        next = pop_flag(f0, f1, c0);
-      }
       warm = it1.bh >= 0;
-      compute(diag, kvo, cur_kb, warm ? kvo1 : kvo, warm ? kb1 : -1, warm);
+      if (next < 0) {
+        compute(std::true_type{}, diag, kvo, kb, warm ? kvo1 : kvo, warm ? kb1 : -1, warm);
+      } else {
+        compute(std::true_type{}, diag, kvo, kb, kvo, next, false);
+        int cur_kb = next;
+        next = pop_flag(f0, f1, c0);
+        while (next >= 0) {
+          compute(std::false_type{}, false, kvo, cur_kb, kvo, next, false);
+          cur_kb = next;
+          next = pop_flag(f0, f1, c0);
+        }
+        compute(std::false_type{}, false, kvo, cur_kb, warm ? kvo1 : kvo, warm ? kb1 : -1, warm);
+      }
     }
 
     // ---- epilogue ----------------------------------------------------------

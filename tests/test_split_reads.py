@@ -55,12 +55,25 @@ def kernel_asm(tmp_path_factory):
 
 
 def _check_kernel(name, kernel_asm):
-    """Number of split reads in kernel `name`; fails on a violation."""
+    """Number of split reads in kernel `name`; fails on a violation.
+
+    From each issuing block, every control-flow path (fall-through and branch
+    targets, as laid out in the assembly) is followed up to the next non-empty
+    inline-asm block, which must be the wait; the instructions on the way must
+    not name a destination register of the reads."""
     body = kernel_asm[kernel_asm.index(name + ":"):]
-    lines = body[:body.index("s_endpgm")].split("\n")
+    # the function's end label: the compiler may lay out an early s_endpgm
+    # (an exit path) or a loop's wait before its issue
+    lines = body[:body.index(".Lfunc_end")].split("\n")
+    labels = {}
+    for i, ln in enumerate(lines):
+        m = re.match(r"^(\.?\w+):", ln.strip())
+        if m:
+            labels[m.group(1)] = i
     blocks = list(_asm_blocks(lines))
+    block_at = {b[0]: b for b in blocks}
     splits = 0
-    for n, (start, end, text) in enumerate(blocks):
+    for start, end, text in blocks:
         reads = [t for t in text if t.startswith("ds_read")]
         if not reads or any(t.startswith("s_waitcnt") for t in text):
             continue
@@ -68,17 +81,31 @@ def _check_kernel(name, kernel_asm):
         dst = set()
         for t in reads:
             dst |= _vregs(t.split(",")[0])
-        # empty inline-asm blocks (register-opacity markers) may sit between
-        # the two; the instructions around them are checked like the others
-        nxt = n + 1
-        while not blocks[nxt][2]:
-            nxt += 1
-        nxt_start, _, nxt_text = blocks[nxt]
-        assert nxt_text == ["s_waitcnt lgkmcnt(0)"], (name, nxt_text)
-        for ln in lines[end + 1:nxt_start]:
-            ins = ln.split(";")[0].strip()
-            if ins and not ins.endswith(":"):
-                assert not (_vregs(ins) & dst), f"{name}: '{ins}' touches a register the LDS reads are filling"
+        todo, seen = [end + 1], set()
+        while todo:
+            i = todo.pop()
+            while True:
+                assert i < len(lines), f"{name}: a path from a split read runs off the function"
+                if i in seen:
+                    break
+                seen.add(i)
+                if i in block_at:
+                    _, bend, btext = block_at[i]
+                    if not btext:            # empty block: a register-opacity marker
+                        i = bend + 1
+                        continue
+                    assert btext == ["s_waitcnt lgkmcnt(0)"], (name, btext)
+                    break
+                ins = lines[i].split(";")[0].strip()
+                if ins and not re.match(r"^\.?\w+:", ins):
+                    assert not (_vregs(ins) & dst), f"{name}: '{ins}' touches a register the LDS reads are filling"
+                    assert not ins.startswith("s_endpgm"), f"{name}: a split read reaches the end unwaited"
+                    m = re.match(r"s_(c?)branch\w*\s+(\S+)", ins)
+                    if m:
+                        todo.append(labels[m.group(2)])
+                        if not m.group(1):   # unconditional: no fall-through
+                            break
+                i += 1
     return splits
 
 
@@ -98,3 +125,34 @@ def test_no_instruction_touches_a_split_read_destination(kernel_asm):
     assert len(gqa) == 4, gqa
     for name in gqa:
         assert _check_kernel(name, kernel_asm) >= 2, name
+
+
+_SYNTH = """_ZN4seer3fooEv:
+\t;;#ASMSTART
+\tds_read_b128 v[0:3], v10
+\t;;#ASMEND
+\ts_cbranch_scc1 .LBB0_2
+\tv_mov_b32 v20, v21
+.LBB0_1:                                ; %tail
+\t;;#ASMSTART
+\ts_waitcnt lgkmcnt(0)
+\t;;#ASMEND
+\ts_endpgm
+.LBB0_2:
+\tv_add_f32_e32 v{reg}, v12, v13
+\ts_branch .LBB0_1
+.Lfunc_end0:
+"""
+
+
+@pytest.mark.parametrize("reg,bad", [(14, False), (2, True)])
+def test_checker_follows_branches(reg, bad):
+    """The checker follows a branch taken between the two blocks (a loop's
+    wait laid out before its issue) and finds a destination register named on
+    that path only."""
+    asm = _SYNTH.format(reg=reg)
+    if bad:
+        with pytest.raises(AssertionError):
+            _check_kernel("_ZN4seer3fooEv", asm)
+    else:
+        assert _check_kernel("_ZN4seer3fooEv", asm) == 1
