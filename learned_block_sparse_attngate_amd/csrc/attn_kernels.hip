@@ -61,7 +61,19 @@ constexpr float kRescaleSlack = 8.0f;    // log2 units the running max may lag b
 constexpr int kXcds = 8;                 // workgroups are dealt round-robin to the 8 XCDs
 constexpr int kSweepPhases = 128;        // resident workgroups per XCD (32 CUs x 4)
 
-enum Mode { kSparse = 0, kDense = 1, kDenseGt = 2 };
+enum Mode {
+  kSparse = 0,
+  kDense = 1,
+  kDenseGt = 2,
+};
+
+// Partial-output slots before query block qb of one head in the XCD-owned
+// path: rows qb' >= C own qb'/C + 1 slots each (one per key chunk they reach;
+// the diagonal chunk's slot is not written).
+__device__ __host__ __forceinline__ long long xcd_slot_base(long long qb, long long C) {
+  const long long k = qb / C;
+  return qb + C * k * (k - 1) / 2 + k * (qb - k * C) - C;
+}
 
 
 // S^T = K Q^T for one tile (32 keys x 32 queries per m-tile, two m-tiles),
@@ -263,6 +275,75 @@ __device__ __forceinline__ void tile_softmax_lazy(const f32x16_t (&sacc)[2], flo
     }
   }
   lsum += ls;
+}
+
+// A row's output over its key chunks: O = sum_c w_c O_c / sum_c w_c, w_c =
+// 2^(L_c - max L), over the chunk in registers (oacc unnormalized, its inv and
+// log2-sum-exp lse2 on entry) and the row's partials of chunks [0, chunk),
+// normalized bf16 outputs and log2-sum-exps that attn_sparse_xcd_kernel wrote
+// to the workspace: the 8-value group g of thread tid (oacc[g / 2] values
+// 8 (g % 2) ..) is 16 bytes at uint4 index g * kThreads + tid of the slot,
+// the register layout here. On return oacc holds the weighted sum, inv and
+// lse2 the row's. The log-sum-exps are loaded 16 at a time and the slots
+// kSlots at a time, all loads of a batch issued before any is used, so a row
+// waits for a few memory round trips, not one per chunk.
+template <int D, int kSlots>
+__device__ __forceinline__ void merge_chunk_partials(const AttnArgs& p, int bh, int qb, int chunk, int tid,
+                                                     int q_local, f32x16_t (&oacc)[D / 32], float& inv,
+                                                     float& lse2) {
+  constexpr int MT = D / 32;
+  constexpr int NG = 2 * MT;                  // 16-byte groups per thread and slot
+  const long long slot0 = static_cast<long long>(bh) * p.slots_per_head + xcd_slot_base(qb, p.chunk);
+  const float* lsl = p.part_l + slot0 * kBlock + q_local;
+  float lmax = lse2;
+  for (int c0 = 0; c0 < chunk; c0 += 16) {
+    float l[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) l[u] = c0 + u < chunk ? lsl[(c0 + u) * kBlock] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) lmax = fmaxf(lmax, l[u]);
+  }
+  float wsum = 0.f;
+  if (lmax > -INFINITY) {
+    const float wown = __builtin_amdgcn_exp2f(lse2 - lmax);   // 0 when the chunk in registers has no active tile
+    wsum = wown;
+    const float sown = wown * inv;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) oacc[mt] *= sown;
+    const uint4* src = reinterpret_cast<const uint4*>(p.part_o16 + slot0 * kBlock * D) + tid;
+    for (int c0 = 0; c0 < chunk; c0 += kSlots) {
+      uint4 v[kSlots][NG];
+      float wl[kSlots];
+#pragma unroll
+      for (int u = 0; u < kSlots; ++u) {
+        const bool ok = c0 + u < chunk;
+        const int cc = ok ? c0 + u : c0;        // a slot that exists; its weight is 0 below
+        wl[u] = ok ? lsl[cc * kBlock] : -INFINITY;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) v[u][g] = src[static_cast<long long>(cc) * (kBlock * D / 8) + g * kThreads];
+      }
+#pragma unroll
+      for (int u = 0; u < kSlots; ++u) {
+        const float wu = __builtin_amdgcn_exp2f(wl[u] - lmax);
+        wsum += wu;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const uint32_t wd[4] = {v[u][g].x, v[u][g].y, v[u][g].z, v[u][g].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i0 = 8 * (g % 2) + 2 * e;
+            oacc[g / 2][i0] = fmaf(wu, __uint_as_float(wd[e] << 16), oacc[g / 2][i0]);
+            oacc[g / 2][i0 + 1] = fmaf(wu, __uint_as_float(wd[e] & 0xffff0000u), oacc[g / 2][i0 + 1]);
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x16_t{};
+  }
+  inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  lse2 = wsum > 0.f ? lmax + __log2f(wsum) : -INFINITY;
 }
 
 // Called twice per row: hook(0) during the row's last tile, once its V copy is
@@ -1064,7 +1145,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_varlen_kernel(AttnArgs p, Va
 //
 // The key range is cut into chunks of C blocks. A job is one chunk of one
 // (batch, KV group): the (row, chunk) items of every query head of the group
-// whose causal range reaches the chunk, head major, query block descending.
+// whose rows lie past the chunk, head major, query block descending. The
+// chunk that holds a row's diagonal is an item of a second launch of the same
+// kernel (kDiagPhase, after the first has finished, with the same jobs holding
+// the rows inside their chunk instead): it writes the row's output, merging
+// its own chunk (in registers) with the row's partials of the earlier chunks
+// in its epilogue, where the merge's loads from HBM run under the tiles of the
+// other workgroups on the CU.
 // Jobs are dealt to the 8 XCDs in the order 0..7, 7..0, 0..7, ... (so each XCD
 // gets chunks c and n-1-c of the groups, which evens out the causal triangle)
 // and every XCD works through its own jobs one after another: the K/V of the
@@ -1077,11 +1164,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_varlen_kernel(AttnArgs p, Va
 // its sequence (a fixed stride per workgroup lets them drift over several
 // chunks). Nothing drains between items: item indices are fetched two items
 // ahead, the next item's mask flags one item ahead, and its Q rows and the K
-// of its first tile are issued during the current item's last tile. An item
-// of a row that spans several chunks writes a bf16 partial output
-// (normalized by its own sum) and its log2-sum-exp; attn_xcd_combine_kernel
-// merges them. Rows inside the first chunk are one item and are written
-// directly.
+// of its first tile are issued during the current item's last tile. Every
+// item of the first launch writes a bf16 partial output (normalized by its own
+// sum) and its log2-sum-exp.
 constexpr int kXcdDefaultChunk = 128;    // 4 MiB of K/V at D = 128: one XCD's L2
 static_assert(kXcdDefaultChunk <= 128, "an item's flags are two 64-bit ballot words");
 constexpr int kXcdMinBlocks = 1280;      // rows of 80k tokens and more
@@ -1121,7 +1206,7 @@ struct XcdCursor {
   long long kvo = 0;       // element offset of the job's K/V head
 };
 
-template <int D>
+template <int D, bool kDiagPhase>
 __device__ __forceinline__ XcdItem xcd_item(const AttnArgs& p, int x, int j, XcdCursor& cur) {
   while (true) {
     if (cur.job < 0) {
@@ -1130,7 +1215,9 @@ __device__ __forceinline__ XcdItem xcd_item(const AttnArgs& p, int x, int j, Xcd
       cur.c = cur.job % p.nchunk;
       const int gi = cur.job / p.nchunk;
       const int bb = gi / p.Hkv, gg = gi - bb * p.Hkv;
-      cur.rows = p.nb - cur.c * kXcdDefaultChunk;
+      // rows past the chunk; in the diagonal phase the rows inside it
+      cur.rows = kDiagPhase ? min(p.nb - cur.c * kXcdDefaultChunk, kXcdDefaultChunk)
+                            : max(p.nb - (cur.c + 1) * kXcdDefaultChunk, 0);
       cur.count = p.group * cur.rows;
       cur.bh0 = bb * p.Hq + gg * p.group;
       cur.kvo = (static_cast<long long>(bb) * p.Hkv + gg) * p.hs * D;
@@ -1147,17 +1234,12 @@ __device__ __forceinline__ XcdItem xcd_item(const AttnArgs& p, int x, int j, Xcd
     cur.hbase += cur.rows;
     ++cur.hig;
   }
-  return XcdItem{cur.bh0 + cur.hig, p.nb - 1 - (mi - cur.hbase), cur.c, cur.kvo};
+  const int top = kDiagPhase ? cur.c * kXcdDefaultChunk + cur.rows - 1 : p.nb - 1;   // query blocks descending
+  return XcdItem{cur.bh0 + cur.hig, top - (mi - cur.hbase), cur.c, cur.kvo};
 }
 
-// Partial-output slots before query block qb of one head: rows qb' >= C own
-// qb'/C + 1 slots each (one per key chunk they reach).
-__device__ __host__ __forceinline__ long long xcd_slot_base(long long qb, long long C) {
-  const long long k = qb / C;
-  return qb + C * k * (k - 1) / 2 + k * (qb - k * C) - C;
-}
 
-template <int D>
+template <int D, bool kDiagPhase>
 __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p) {
   constexpr int CPR = D / 8;               // 16-byte chunks per K/V row
   constexpr int KS = D / 16;               // MFMA k-steps for S^T (= Q loads per thread)
@@ -1282,9 +1364,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
   __syncthreads();
   const int j0 = claim;
   XcdCursor cur;
-  XcdItem it = xcd_item<D>(p, x, j0, cur);            // this item
+  XcdItem it = xcd_item<D, kDiagPhase>(p, x, j0, cur);            // this item
   if (it.bh < 0) return;
-  XcdItem it1 = xcd_item<D>(p, x, j0 + 1, cur);       // the next one
+  XcdItem it1 = xcd_item<D, kDiagPhase>(p, x, j0 + 1, cur);       // the next one
   int j2 = j0 + 2;                                 // the one after
   int pend = 0;                                    // wave 0 lane 0: claim in flight (the item after j2)
   bool claimed = false;
@@ -1367,7 +1449,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       wg_barrier();                                // both waves hold it before the LDS word is reused
     }
-    const XcdItem it2 = xcd_item<D>(p, x, j2, cur);
+    const XcdItem it2 = xcd_item<D, kDiagPhase>(p, x, j2, cur);
     load_flags(it2, fb0, fb1);                     // the item after next; read at the next item's start
     claimed = it2.bh >= 0;
     if (claimed && tid == 0) {
@@ -1407,27 +1489,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
     const float ltot = pair_sum(lsum);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     const float lse2 = ltot > 0.f ? m + __log2f(ltot) : -INFINITY;
-    if (it.qb >= kXcdDefaultChunk) {
-      // normalized bf16 partial: the thread's 8-value group g (oacc[g / 2]
-      // values 8 (g % 2) ..) is 16 bytes at uint4 index g * kThreads + tid of
-      // the slot, so each store instruction writes 1 KiB contiguous. The
-      // stores are non-temporal: the partials are read once, by the merge, and
-      // would otherwise push the chunk's K/V out of the XCD's L2
-      const long long slot = static_cast<long long>(it.bh) * p.slots_per_head +
-                             xcd_slot_base(it.qb, kXcdDefaultChunk) + it.c;
-      uint4* po = reinterpret_cast<uint4*>(p.part_o16 + slot * kBlock * D) + tid;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-          __builtin_nontemporal_store(
-              u32x4_t{pack_bf16x2(oacc[mt][8 * h2 + 0] * inv, oacc[mt][8 * h2 + 1] * inv),
-                      pack_bf16x2(oacc[mt][8 * h2 + 2] * inv, oacc[mt][8 * h2 + 3] * inv),
-                      pack_bf16x2(oacc[mt][8 * h2 + 4] * inv, oacc[mt][8 * h2 + 5] * inv),
-                      pack_bf16x2(oacc[mt][8 * h2 + 6] * inv, oacc[mt][8 * h2 + 7] * inv)},
-              reinterpret_cast<u32x4_t*>(po + (2 * mt + h2) * kThreads));
-      if (hl == 0) p.part_l[slot * kBlock + q_local] = lse2;
-    } else {
+    if constexpr (kDiagPhase) {
+      // the row's last chunk: merged with its earlier chunks' partials
+      float inv_r = inv, lse2_r = lse2;
+      if (it.c > 0) merge_chunk_partials<D, 3>(p, it.bh, it.qb, it.c, tid, q_local, oacc, inv_r, lse2_r);
       const int t = it.qb * kBlock + q_local;
       if (t < p.S) {
         const size_t obase = (static_cast<size_t>(it.bh) * p.hs + t) * D;
@@ -1436,8 +1501,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             const int dim = 32 * mt + 8 * r4 + 4 * hl;
-            const float o0 = oacc[mt][4 * r4 + 0] * inv, o1 = oacc[mt][4 * r4 + 1] * inv;
-            const float o2 = oacc[mt][4 * r4 + 2] * inv, o3 = oacc[mt][4 * r4 + 3] * inv;
+            const float o0 = oacc[mt][4 * r4 + 0] * inv_r, o1 = oacc[mt][4 * r4 + 1] * inv_r;
+            const float o2 = oacc[mt][4 * r4 + 2] * inv_r, o3 = oacc[mt][4 * r4 + 3] * inv_r;
             if (p.out_bf16) {
               *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + obase + dim) =
                   make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
@@ -1446,8 +1511,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
             }
           }
         }
-        if (p.lse != nullptr && hl == 0) p.lse[static_cast<size_t>(it.bh) * p.hs + t] = lse2 * kLn2;
+        if (p.lse != nullptr && hl == 0) p.lse[static_cast<size_t>(it.bh) * p.hs + t] = lse2_r * kLn2;
       }
+    } else {
+      // normalized bf16 partial: the thread's 8-value group g (oacc[g / 2]
+      // values 8 (g % 2) ..) is 16 bytes at uint4 index g * kThreads + tid of
+      // the slot, so each store instruction writes 1 KiB contiguous. The
+      // stores are non-temporal: the partials are read once, by the merge, and
+      // would otherwise push the chunk's K/V out of the XCD's L2
+      const long long slot = static_cast<long long>(it.bh) * p.slots_per_head +
+                             xcd_slot_base(it.qb, kXcdDefaultChunk) + it.c;
+      uint4* po = reinterpret_cast<uint4*>(p.part_o16 + slot * kBlock * D) + tid;
+  #pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+  #pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          __builtin_nontemporal_store(
+              u32x4_t{pack_bf16x2(oacc[mt][8 * h2 + 0] * inv, oacc[mt][8 * h2 + 1] * inv),
+                      pack_bf16x2(oacc[mt][8 * h2 + 2] * inv, oacc[mt][8 * h2 + 3] * inv),
+                      pack_bf16x2(oacc[mt][8 * h2 + 4] * inv, oacc[mt][8 * h2 + 5] * inv),
+                      pack_bf16x2(oacc[mt][8 * h2 + 6] * inv, oacc[mt][8 * h2 + 7] * inv)},
+              reinterpret_cast<u32x4_t*>(po + (2 * mt + h2) * kThreads));
+      if (hl == 0) p.part_l[slot * kBlock + q_local] = lse2;
     }
     m = -INFINITY;
     lsum = 0.f;
@@ -1465,91 +1550,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_sparse_xcd_kernel(AttnArgs p
 // Per-XCD item counters of attn_sparse_xcd_kernel start at 0 on every call.
 __global__ void attn_xcd_counters_init(int* ctr) {
   if (threadIdx.x < kXcds) ctr[threadIdx.x] = 0;
-}
-
-// Merge of the bf16 partials written by attn_sparse_xcd_kernel:
-// O = sum_c w_c O_c / sum_c w_c, w_c = 2^(L_c - max L), LSE = max L + log2(sum w).
-// One workgroup per row qb >= C, thread and value layout as in the writer. The slots are
-// read kXcdMergeBatch at a time, all loads of a batch issued before any is
-// used, so the merge runs at memory bandwidth rather than one latency per slot.
-constexpr int kXcdMergeBatch = 4;
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void attn_xcd_combine_kernel(AttnArgs p) {
-  constexpr int MT = D / 32;
-  constexpr int HALF = D / 2;
-  constexpr int NV = HALF / 8;                     // 16-byte loads per thread and slot
-  const int rows = p.nb - p.chunk;
-  const int bh = blockIdx.x / rows;
-  const int qb = p.chunk + static_cast<int>(blockIdx.x % rows);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hl = lane >> 5;
-  const int q_local = wave * 32 + l32;
-  const int n = qb / p.chunk + 1;
-  const long long slot0 = static_cast<long long>(bh) * p.slots_per_head + xcd_slot_base(qb, p.chunk);
-  const float* lse = p.part_l + slot0 * kBlock + q_local;
-  float lmax = -INFINITY;
-  for (int c0 = 0; c0 < n; c0 += 2 * kXcdMergeBatch) {
-    float l[2 * kXcdMergeBatch];
-#pragma unroll
-    for (int u = 0; u < 2 * kXcdMergeBatch; ++u) l[u] = c0 + u < n ? lse[(c0 + u) * kBlock] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < 2 * kXcdMergeBatch; ++u) lmax = fmaxf(lmax, l[u]);
-  }
-  float acc[HALF];
-#pragma unroll
-  for (int i = 0; i < HALF; ++i) acc[i] = 0.f;
-  float wsum = 0.f;
-  if (lmax > -INFINITY) {
-    const uint4* src = reinterpret_cast<const uint4*>(p.part_o16 + slot0 * kBlock * D) + tid;
-    for (int c0 = 0; c0 < n; c0 += kXcdMergeBatch) {
-      uint4 v[kXcdMergeBatch][NV];
-      float w[kXcdMergeBatch];
-#pragma unroll
-      for (int u = 0; u < kXcdMergeBatch; ++u) {
-        const bool ok = c0 + u < n;
-        const int cc = ok ? c0 + u : c0;           // a slot that exists; its weight is 0 below
-        w[u] = ok ? lse[cc * kBlock] : -INFINITY;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) v[u][i] = src[static_cast<long long>(cc) * (kBlock * D / 8) + i * kThreads];
-      }
-#pragma unroll
-      for (int u = 0; u < kXcdMergeBatch; ++u) {
-        const float wu = __builtin_amdgcn_exp2f(w[u] - lmax);
-        wsum += wu;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          const uint32_t wd[4] = {v[u][i].x, v[u][i].y, v[u][i].z, v[u][i].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[8 * i + 2 * e] = fmaf(wu, __uint_as_float(wd[e] << 16), acc[8 * i + 2 * e]);
-            acc[8 * i + 2 * e + 1] = fmaf(wu, __uint_as_float(wd[e] & 0xffff0000u), acc[8 * i + 2 * e + 1]);
-          }
-        }
-      }
-    }
-  }
-  const int t = qb * kBlock + q_local;
-  if (t >= p.S) return;
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const size_t obase = (static_cast<size_t>(bh) * p.hs + t) * D;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int dim = 32 * mt + 8 * r4 + 4 * hl;
-      const float* a = acc + 16 * mt + 4 * r4;
-      if (p.out_bf16) {
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + obase + dim) =
-            make_uint2(pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv));
-      } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + obase + dim) =
-            make_float4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);
-      }
-    }
-  }
-  if (p.lse != nullptr && hl == 0)
-    p.lse[static_cast<size_t>(bh) * p.hs + t] = wsum > 0.f ? (lmax + __log2f(wsum)) * kLn2 : -INFINITY;
 }
 
 // Merge the per-chunk partials of rows spanning several key chunks:
@@ -1620,13 +1620,9 @@ hipError_t launch_d(const AttnArgs& a, int mode, hipStream_t st) {
   const dim3 block(kThreads);
   if (mode == kSparse && a.xcd) {
     hipLaunchKernelGGL(attn_xcd_counters_init, dim3(1), dim3(kWave), 0, st, a.xcd_ctr);
-    hipLaunchKernelGGL((attn_sparse_xcd_kernel<D>), dim3(kXcds * kXcdSlots), block, 0, st, a);
-    if (a.nb > a.chunk) {
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      const dim3 cgrid(static_cast<unsigned>(a.B) * a.Hq * (a.nb - a.chunk));
-      hipLaunchKernelGGL((attn_xcd_combine_kernel<D>), cgrid, block, 0, st, a);
-    }
+    hipLaunchKernelGGL((attn_sparse_xcd_kernel<D, false>), dim3(kXcds * kXcdSlots), block, 0, st, a);
+    hipLaunchKernelGGL(attn_xcd_counters_init, dim3(1), dim3(kWave), 0, st, a.xcd_ctr);
+    hipLaunchKernelGGL((attn_sparse_xcd_kernel<D, true>), dim3(kXcds * kXcdSlots), block, 0, st, a);
     return hipGetLastError();
   }
   if constexpr (D == 128) {

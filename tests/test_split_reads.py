@@ -111,11 +111,14 @@ def _check_kernel(name, kernel_asm):
 
 def test_no_instruction_touches_a_split_read_destination(kernel_asm):
     names = re.findall(
-        r"^(_ZN4seer\S*(?:attn_sparse_xcd_kernel|attn_sparse_rows_kernel|attn_fwd_kernel|attn_varlen_kernel)\S*):",
+        r"^(_ZN4seer\S*(?:attn_sparse_xcd_kernel|attn_sparse_rows_kernel|attn_fwd_kernel|"
+        r"attn_varlen_kernel)\S*):",
         kernel_asm, re.M)
-    # D = 64 and 128; the persistent rows (D = 128); the row kernels in
-    # block-sparse, dense and ground-truth mode
-    assert len(names) == 2 + 1 + 6 + 6, names
+    # D = 64 and 128: the XCD-owned chunks in both phases (chunks past the
+    # row, the row's diagonal chunk with the merge); the
+    # persistent rows (D = 128); the row kernels in block-sparse, dense and
+    # ground-truth mode
+    assert len(names) == 2 + 2 + 1 + 6 + 6, names
     for name in names:
         # every kernel reads K and V of at least two inlined tile bodies (the
         # diagonal tile and the others) through the split form
