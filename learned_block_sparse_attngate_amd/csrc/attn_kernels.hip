@@ -1169,7 +1169,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_varlen_kernel(AttnArgs p, Va
 // sum) and its log2-sum-exp.
 constexpr int kXcdDefaultChunk = 128;    // 4 MiB of K/V at D = 128: one XCD's L2
 static_assert(kXcdDefaultChunk <= 128, "an item's flags are two 64-bit ballot words");
-constexpr int kXcdMinBlocks = 1280;      // rows of 80k tokens and more
+constexpr int kXcdMinBlocks = 960;       // rows of 60k tokens and more
 constexpr int kXcdSlots = 128;           // resident workgroups per XCD: 32 CUs x 4
 
 
@@ -1672,11 +1672,11 @@ constexpr long long kXcdRowsMaxBlockDims = 256 * 128;   // key blocks x head_dim
 }  // namespace
 
 // The XCD-owned path takes rows of at least kXcdMinBlocks blocks when there
-// are at least 64 (batch, KV group, chunk) jobs to deal over the 8 XCDs (it
-// measured 1-3% faster than the other path from 80k tokens up, slower at 64k
-// and below, where fewer K/V re-reads miss the L2); otherwise the rows go to
-// attn_fwd_kernel (cut into chunks of 512 blocks above 1024 blocks, with the
-// circular sweep).
+// are at least 64 (batch, KV group, chunk) jobs to deal over the 8 XCDs (with
+// 32/8 heads at 90% it measured 4% faster than the persistent rows at 60k and
+// 12% at 64k, 3-8% slower at 48k and 56k, where fewer K/V re-reads miss the
+// L2); otherwise the rows go to attn_sparse_rows_kernel or attn_fwd_kernel
+// (cut into chunks of 512 blocks above 1024 blocks, with the circular sweep).
 SparsePlan sparse_plan(int B, int Hkv, int group, int nb, int D) {
   SparsePlan pl{};
   const int C = kXcdDefaultChunk;

@@ -268,7 +268,7 @@ def test_workspace_sizes():
     # one-item rows over 256 blocks at D = 128 with >= 8 rows per resident
     # workgroup (8 x 1024): the persistent launch's 8 queue counters
     assert lib.seer_attn_workspace_size(ctypes.byref(_shape(b=1, hq=32, hkv=8, s=64 * 300, d=128))) == 256
-    assert lib.seer_attn_workspace_size(ctypes.byref(_shape(b=1, hq=32, hkv=8, s=64 * 1024, d=128))) == 256
+    assert lib.seer_attn_workspace_size(ctypes.byref(_shape(b=1, hq=32, hkv=8, s=64 * 959, d=128))) == 256
     assert lib.seer_attn_workspace_size(ctypes.byref(_shape(b=1, hq=8, hkv=2, s=64 * 300, d=128))) == 0
     assert lib.seer_attn_workspace_size(ctypes.byref(_shape(b=1, hq=32, hkv=8, s=64 * 600, d=64))) == 0
     # rows of more than 1024 blocks are cut into key chunks of 512 blocks: chunk
@@ -280,10 +280,10 @@ def test_workspace_sizes():
     assert lib.seer_attn_workspace_size(ctypes.byref(s3)) == 0
     s4 = _shape(b=1, hq=2, hkv=1, s=64 * 1024 + 1, d=64)
     assert lib.seer_attn_workspace_size(ctypes.byref(s4)) == 2 * (1025 + 513 + 1) * 64 * 65 * 4
-    # rows of >= 1280 blocks with >= 64 (batch, KV group, 128-block chunk) jobs
+    # rows of >= 960 blocks with >= 64 (batch, KV group, 128-block chunk) jobs
     # take the XCD-owned path: rows qb >= 128 own qb // 128 + 1 slots of a
     # 64 x D bf16 partial and 64 fp32 log-sum-exps; 256 bytes of item counters
-    for nb5, d5 in ((1300, 128), (2048, 64)):
+    for nb5, d5 in ((1300, 128), (2048, 64), (960, 128), (1024, 128)):
         s5 = _shape(b=1, hq=16, hkv=8, s=64 * nb5 - 3, d=d5)
         slots = sum(q // 128 + 1 for q in range(128, nb5))
         assert lib.seer_attn_workspace_size(ctypes.byref(s5)) == 16 * slots * 64 * (2 * d5 + 4) + 256

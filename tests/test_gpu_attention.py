@@ -278,17 +278,19 @@ def test_sparse_multichunk_all_ones_matches_dense():
 
 
 XCD_CASES = [
-    # rows of >= 1280 blocks and >= 64 (batch, KV group, 128-block chunk) jobs:
+    # rows of >= 960 blocks and >= 64 (batch, KV group, 128-block chunk) jobs:
     # the XCD-owned persistent path with bf16 partials
     ("d64_s83183_g2_f32", Shape(1, 16, 8, 64 * 1300 - 17, 64), torch.float32),
     ("d128_s82565_g1_bf16", Shape(1, 8, 8, 64 * 1290 + 5, 128), torch.bfloat16),
+    # the shortest rows of the path (960 blocks, a last chunk of 64 blocks)
+    ("d128_s61400_g1_bf16", Shape(1, 8, 8, 64 * 960 - 40, 128), torch.bfloat16),
 ]
 
 
 @pytest.mark.parametrize("name,shape,dt", XCD_CASES, ids=[c[0] for c in XCD_CASES])
 def test_sparse_xcd_rows(name, shape, dt):
     """Rows cut into 128-block key chunks owned by XCDs (persistent workgroups,
-    bf16 partials, merge kernel): chunk-boundary rows, a ragged last block, an
+    bf16 partials merged by the rows' diagonal chunks): chunk-boundary rows, a ragged last block, an
     empty row, rows active only in their first chunk, only on the diagonal,
     only in the first and last chunk (empty chunks between), with a full chunk,
     and without the diagonal."""
