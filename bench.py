@@ -99,7 +99,7 @@ MFMA_COUNTERS = os.path.join(ROOT, "profiles", "attn_sparse_llama8b_s128k_90_mfm
 
 
 def measured_mfma_busy(workload: str):
-    """Fraction of the main block-sparse kernel's cycles its MFMA pipes were
+    """Fraction of the block-sparse call's kernel cycles its MFMA pipes were
     busy (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs) and
     the engine clock during it, from the committed counter summary; None if
     that summary is missing, for another workload, or for other kernel source."""
@@ -588,7 +588,8 @@ def main():
             "overhead_vs_dense": round(gt_ms / dense_ms - 1.0, 4),
             "map_shape": [B, Hq, nb, nb],
             "pages_overhead_vs_flashattention": "< 0.05 (explainer section 3.4, customized training kernel)"},
-        "roofline": {"kernel": "seer_block_sparse_attn_fwd (one call: main block-sparse kernel + merge of partial outputs)",
+        "roofline": {"kernel": "seer_block_sparse_attn_fwd (one call: at 128k the two launches of the XCD-owned "
+                               "chunk kernel, the second merging the partial outputs)",
                      "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(args.workload),
