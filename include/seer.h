@@ -159,24 +159,25 @@ seer_status seer_gate_distill_bwd(const seer_shape* shape, int32_t gate_dim, int
  * lse          device fp32 [B,Hq,S] output, or NULL
  * workspace    device scratch of at least seer_attn_workspace_size() bytes,
  *              16-byte aligned, used only when block_mask is non-NULL. Rows
- *              of more than 1024 blocks (seq_len > 65536) are processed in
- *              key chunks and leave per-chunk partial outputs there that a
- *              second kernel merges. Rows of at least 1280 blocks with at
- *              least 64 (batch, KV head, 128-block chunk) pairs use chunks of
- *              128 blocks, each owned by one XCD: 64 * (2 * head_dim + 4)
- *              bytes per row and chunk (bf16 output, fp32 log-sum-exp) plus
- *              256 bytes of item counters that every call resets. Other long
- *              rows use chunks of 512 blocks: 64 * (head_dim + 1) * 4 bytes
- *              per row and chunk. Rows of at most 256 blocks at head_dim
- *              128 (512 at head_dim 64) with batch * heads_q a multiple of 8
- *              take 256 bytes: a pre-pass counts the mask's active tiles per
- *              XCD of the XCD-major row order (each XCD takes an eighth of
- *              the heads), which is used when those counts are balanced.
- *              Rows of 257 to 1024 blocks at head_dim 128 with
- *              batch * heads_q * blocks >= 8192 also take 256 bytes: the
- *              per-XCD row queues of a persistent launch, which every call
- *              resets. Otherwise the size is 0, and workspace may be NULL,
- *              when seq_len <= 65536. The active blocks of each row are
+ *              of at least 960 blocks with at least 64 (batch, KV head,
+ *              128-block chunk) pairs are processed in key chunks of 128
+ *              blocks, each owned by one XCD: the chunks before a row's
+ *              diagonal chunk leave partial outputs there, which the diagonal
+ *              chunk's pass merges; 64 * (2 * head_dim + 4) bytes per row and
+ *              chunk it reaches (bf16 output, fp32 log-sum-exp) plus 256 bytes
+ *              of item counters that every call resets. Other rows of more
+ *              than 1024 blocks (seq_len > 65536) use key chunks of 512
+ *              blocks whose partials a second kernel merges:
+ *              64 * (head_dim + 1) * 4 bytes per row and chunk. Rows of at
+ *              most 256 blocks at head_dim 128 (512 at head_dim 64) with
+ *              batch * heads_q a multiple of 8 take 256 bytes: a pre-pass
+ *              counts the mask's active tiles per XCD of the XCD-major row
+ *              order (each XCD takes an eighth of the heads), which is used
+ *              when those counts are balanced. Other rows of 257 to 1024
+ *              blocks at head_dim 128 with batch * heads_q * blocks >= 8192
+ *              also take 256 bytes: the per-XCD row queues of a persistent
+ *              launch, which every call resets. Otherwise the size is 0 and
+ *              workspace may be NULL. The active blocks of each row are
  *              compacted on chip.
  * ---------------------------------------------------------------------- */
 size_t seer_attn_workspace_size(const seer_shape* shape);
