@@ -284,9 +284,10 @@ __device__ __forceinline__ void tile_softmax_lazy(const f32x16_t (&sacc)[2], flo
 // to the workspace: the 8-value group g of thread tid (oacc[g / 2] values
 // 8 (g % 2) ..) is 16 bytes at uint4 index g * kThreads + tid of the slot,
 // the register layout here. On return oacc holds the weighted sum, inv and
-// lse2 the row's. The log-sum-exps are loaded 16 at a time and the slots
-// kSlots at a time, all loads of a batch issued before any is used, so a row
-// waits for a few memory round trips, not one per chunk.
+// lse2 the row's. One pass with a running maximum: the slots are loaded
+// kSlots at a time with their log2-sum-exps, all loads of a batch issued
+// before any is used, and the sum so far is rescaled when a batch raises the
+// maximum, so a row waits for one memory round trip per batch.
 template <int D, int kSlots>
 __device__ __forceinline__ void merge_chunk_partials(const AttnArgs& p, int bh, int qb, int chunk, int tid,
                                                      int q_local, f32x16_t (&oacc)[D / 32], float& inv,
@@ -295,55 +296,58 @@ __device__ __forceinline__ void merge_chunk_partials(const AttnArgs& p, int bh, 
   constexpr int NG = 2 * MT;                  // 16-byte groups per thread and slot
   const long long slot0 = static_cast<long long>(bh) * p.slots_per_head + xcd_slot_base(qb, p.chunk);
   const float* lsl = p.part_l + slot0 * kBlock + q_local;
-  float lmax = lse2;
-  for (int c0 = 0; c0 < chunk; c0 += 16) {
-    float l[16];
+  const uint4* src = reinterpret_cast<const uint4*>(p.part_o16 + slot0 * kBlock * D) + tid;
+  // running state: maximum M, wsum = sum_c 2^(L_c - M), oacc = sum_c 2^(L_c - M) O_c
+  float mrun = lse2, wsum;
+  if (lse2 > -INFINITY) {
+    wsum = 1.f;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) l[u] = c0 + u < chunk ? lsl[(c0 + u) * kBlock] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) lmax = fmaxf(lmax, l[u]);
-  }
-  float wsum = 0.f;
-  if (lmax > -INFINITY) {
-    const float wown = __builtin_amdgcn_exp2f(lse2 - lmax);   // 0 when the chunk in registers has no active tile
-    wsum = wown;
-    const float sown = wown * inv;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) oacc[mt] *= sown;
-    const uint4* src = reinterpret_cast<const uint4*>(p.part_o16 + slot0 * kBlock * D) + tid;
-    for (int c0 = 0; c0 < chunk; c0 += kSlots) {
-      uint4 v[kSlots][NG];
-      float wl[kSlots];
-#pragma unroll
-      for (int u = 0; u < kSlots; ++u) {
-        const bool ok = c0 + u < chunk;
-        const int cc = ok ? c0 + u : c0;        // a slot that exists; its weight is 0 below
-        wl[u] = ok ? lsl[cc * kBlock] : -INFINITY;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) v[u][g] = src[static_cast<long long>(cc) * (kBlock * D / 8) + g * kThreads];
-      }
-#pragma unroll
-      for (int u = 0; u < kSlots; ++u) {
-        const float wu = __builtin_amdgcn_exp2f(wl[u] - lmax);
-        wsum += wu;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          const uint32_t wd[4] = {v[u][g].x, v[u][g].y, v[u][g].z, v[u][g].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i0 = 8 * (g % 2) + 2 * e;
-            oacc[g / 2][i0] = fmaf(wu, __uint_as_float(wd[e] << 16), oacc[g / 2][i0]);
-            oacc[g / 2][i0 + 1] = fmaf(wu, __uint_as_float(wd[e] & 0xffff0000u), oacc[g / 2][i0 + 1]);
-          }
-        }
-      }
-    }
+    for (int mt = 0; mt < MT; ++mt) oacc[mt] *= inv;
   } else {
+    wsum = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x16_t{};
   }
+  for (int c0 = 0; c0 < chunk; c0 += kSlots) {
+    uint4 v[kSlots][NG];
+    float wl[kSlots];
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+      const bool ok = c0 + u < chunk;
+      const int cc = ok ? c0 + u : c0;          // a slot that exists; its weight is 0 below
+      wl[u] = ok ? lsl[cc * kBlock] : -INFINITY;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) v[u][g] = src[static_cast<long long>(cc) * (kBlock * D / 8) + g * kThreads];
+    }
+    float mnew = mrun;
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) mnew = fmaxf(mnew, wl[u]);
+    if (mnew == -INFINITY) continue;            // nothing so far has a key
+    if (mnew > mrun) {                          // the batch raises the maximum: rescale the sum so far
+      const float sc = __builtin_amdgcn_exp2f(mrun - mnew);   // 0 while mrun = -inf
+      wsum *= sc;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) oacc[mt] *= sc;
+      mrun = mnew;
+    }
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+      const float wu = __builtin_amdgcn_exp2f(wl[u] - mrun);
+      wsum += wu;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const uint32_t wd[4] = {v[u][g].x, v[u][g].y, v[u][g].z, v[u][g].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i0 = 8 * (g % 2) + 2 * e;
+          oacc[g / 2][i0] = fmaf(wu, __uint_as_float(wd[e] << 16), oacc[g / 2][i0]);
+          oacc[g / 2][i0 + 1] = fmaf(wu, __uint_as_float(wd[e] & 0xffff0000u), oacc[g / 2][i0 + 1]);
+        }
+      }
+    }
+  }
   inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  lse2 = wsum > 0.f ? lmax + __log2f(wsum) : -INFINITY;
+  lse2 = wsum > 0.f ? mrun + __log2f(wsum) : -INFINITY;
 }
 
 // Called twice per row: hook(0) during the row's last tile, once its V copy is
@@ -1230,12 +1234,20 @@ __device__ __forceinline__ XcdItem xcd_item(const AttnArgs& p, int x, int j, Xcd
     cur.job = -1;
   }
   const int mi = j - cur.begin;
-  while (mi >= cur.hbase + cur.rows) {
-    cur.hbase += cur.rows;
-    ++cur.hig;
+  if constexpr (kDiagPhase) {
+    // query block major, ascending, the group's heads in turn: the items
+    // resident on the XCD read the K/V of the chunk's first blocks up to
+    // about their own query block, and the heads of one query block read the
+    // same tiles at the same time
+    const int r = mi / p.group;
+    return XcdItem{cur.bh0 + (mi - r * p.group), cur.c * kXcdDefaultChunk + r, cur.c, cur.kvo};
+  } else {
+    while (mi >= cur.hbase + cur.rows) {
+      cur.hbase += cur.rows;
+      ++cur.hig;
+    }
+    return XcdItem{cur.bh0 + cur.hig, p.nb - 1 - (mi - cur.hbase), cur.c, cur.kvo};   // query blocks descending
   }
-  const int top = kDiagPhase ? cur.c * kXcdDefaultChunk + cur.rows - 1 : p.nb - 1;   // query blocks descending
-  return XcdItem{cur.bh0 + cur.hig, top - (mi - cur.hbase), cur.c, cur.kvo};
 }
 
 
