@@ -112,3 +112,86 @@ def test_persistent_stealing_balances_the_xcds():
     # XCD's own time; stealing comes within 10% of that
     assert with_steal < 0.6 * without
     assert with_steal < 1.1 * without * (4 + 7) / (8 * 4)
+
+
+# ---- the XCD-owned key chunks: two launches of attn_sparse_xcd_kernel -------
+
+CHUNK = 128
+
+
+def xcd_job(x, t, njobs):
+    """Job at position t of XCD x's sequence (16 jobs dealt as 0..7, 7..0 over
+    each pair of positions), or -1 past its end."""
+    base = 2 * XCDS * (t >> 1)
+    k = base + 2 * XCDS - 1 - x if t & 1 else base + x
+    return k if k < njobs else -1
+
+
+def xcd_items(x, batch, hkv, group, nb, diag):
+    """(batch, query head, query block, chunk) items of XCD x's sequence in one
+    launch: the chunks before each row's diagonal chunk (diag=False), or each
+    row's diagonal chunk (diag=True)."""
+    nch = -(-nb // CHUNK)
+    njobs = batch * hkv * nch
+    t = 0
+    while True:
+        job = xcd_job(x, t, njobs)
+        if job < 0:
+            return
+        c, gi = job % nch, job // nch
+        b, g = gi // hkv, gi % hkv
+        if diag:
+            rows = min(nb - c * CHUNK, CHUNK)
+            for mi in range(group * rows):          # query block major, ascending, heads in turn
+                yield b, g * group + mi % group, c * CHUNK + mi // group, c
+        else:
+            rows = max(nb - (c + 1) * CHUNK, 0)
+            for mi in range(group * rows):          # head major, query block descending
+                yield b, g * group + mi // rows, nb - 1 - mi % rows, c
+        t += 1
+
+
+def xcd_slot_base(qb, c):
+    k = qb // c
+    return qb + c * k * (k - 1) // 2 + k * (qb - k * c) - c
+
+
+@pytest.mark.parametrize("batch,hkv,group,nb", [(1, 8, 4, 2048), (1, 8, 1, 960), (2, 4, 2, 1000),
+                                                (1, 16, 1, 1300), (1, 8, 2, 1290), (3, 8, 1, 1025)])
+def test_xcd_two_launches_cover_every_item_once(batch, hkv, group, nb):
+    """The first launch takes exactly the (row, chunk) items before each row's
+    diagonal chunk, the second exactly one item per row (its diagonal chunk),
+    each once, every XCD's sequence ends, and the partial slots the first
+    launch writes are distinct and inside the per-head slot range the second
+    launch reads from."""
+    hq = hkv * group
+    first = [it for x in range(XCDS) for it in xcd_items(x, batch, hkv, group, nb, False)]
+    second = [it for x in range(XCDS) for it in xcd_items(x, batch, hkv, group, nb, True)]
+    want_first = {(b, h, qb, c) for b in range(batch) for h in range(hq) for qb in range(nb)
+                  for c in range(qb // CHUNK)}
+    want_second = {(b, h, qb, qb // CHUNK) for b in range(batch) for h in range(hq) for qb in range(nb)}
+    assert len(first) == len(set(first)) and set(first) == want_first
+    assert len(second) == len(set(second)) and set(second) == want_second
+    per_head = xcd_slot_base(nb, CHUNK)
+    slots = [(b, h, xcd_slot_base(qb, CHUNK) + c) for b, h, qb, c in first]
+    assert len(slots) == len(set(slots))
+    assert all(0 <= s < per_head for _, _, s in slots)
+    # every slot a diagonal item reads was written by the first launch
+    written = set(slots)
+    for b, h, qb, c in second:
+        assert all((b, h, xcd_slot_base(qb, CHUNK) + cc) in written for cc in range(c))
+
+
+def test_xcd_first_launch_balanced_at_128k():
+    """At 128k with 8 KV groups (the headline layer) every XCD gets chunks c and
+    15 - c of each group in the first launch: the same number of items and the
+    same number of causal tiles, and in the second launch the same number of
+    rows and of partial slots to merge."""
+    nb, hkv, group = 2048, 8, 4
+    items = [list(xcd_items(x, 1, hkv, group, nb, False)) for x in range(XCDS)]
+    assert len({len(i) for i in items}) == 1
+    tiles = [sum(min(CHUNK, qb - c * CHUNK) for _, _, qb, c in i) for i in items]
+    assert len(set(tiles)) == 1
+    diag = [list(xcd_items(x, 1, hkv, group, nb, True)) for x in range(XCDS)]
+    assert len({len(d) for d in diag}) == 1
+    assert len({sum(c for _, _, _, c in d) for d in diag}) == 1
