@@ -342,3 +342,68 @@ def test_workload_sampled(name):
     extra = [x for c in range(128, shape.nb, 128) for x in (c - 1, c)]
     rows = sorted(set(rows) | {(0, 5, x) for x in extra})
     _run_sampled(shape, w["seed"], minfo.mask, torch.bfloat16, rows, name)
+
+
+def _growing_scores(shape, seed, hot_blocks, boost_log2):
+    """Q/K/V from the seed with a shared direction u per KV group added to the
+    queries (amplitude a) and to the keys of `hot_blocks` (amplitude b), a b
+    chosen so those keys score about `boost_log2` log2 units above the others.
+    A row that meets a hot block after its first tile then raises its running
+    maximum far past the lazy rescale's slack, and the chunks of a long row
+    carry very different log-sum-exps into their merge."""
+    q, k, v = synth.gen_qkv(shape, seed)
+    qf, kf = synth.f32_from_bf16_bits(q).copy(), synth.f32_from_bf16_bits(k).copy()
+    d = shape.head_dim
+    g = shape.heads_q // shape.heads_kv
+    rng = np.random.default_rng(seed + 1)
+    a = 4.0
+    b = boost_log2 / (a * np.log2(np.e) / np.sqrt(d))
+    for kv in range(shape.heads_kv):
+        u = rng.standard_normal(d).astype(np.float32)
+        u /= np.linalg.norm(u)
+        qf[:, kv * g:(kv + 1) * g] += a * u
+        for blk in hot_blocks:
+            kf[:, kv, 64 * blk:64 * blk + 64] += b * u
+    return synth.bf16_bits_from_f32(qf), synth.bf16_bits_from_f32(kf), v
+
+
+def test_sparse_running_max_grows_past_slack():
+    """Later tiles of a row raise the running maximum by ~24 log2 units (three
+    times the slack), through the row kernel: the lazy update's rescale branch
+    against the oracle, every row."""
+    seer = _seer()
+    shape = Shape(1, 4, 2, 64 * 40 - 7, 64)
+    q, k, v = _growing_scores(shape, 90, (2, 9, 17, 30), 24.0)
+    mask = np.ones((1, 4, shape.nb, shape.nb), dtype=np.uint8)
+    mask[0, 1, :, 9] = 0                          # one head without the second hot block
+    say(f"[growing max] shape={shape}")
+    out, lse = seer.seer_block_sparse_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_u8(mask),
+                                               out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(q, k, v, mask)
+    check_close(host(out), o_ref, "growing max O", out_dtype=torch.float32)
+    check_lse(host(lse), l_ref, "growing max LSE")
+
+
+def test_sparse_xcd_running_max_grows_past_slack():
+    """The same through the XCD-owned path (960 blocks, 8 KV groups): hot
+    blocks in the first, a middle and the last chunks, so the first launch's
+    partials and the diagonal chunks' merge see log-sum-exps ~24 log2 units
+    apart (the one-pass merge's rescale). Sampled rows of every head."""
+    seer = _seer()
+    shape = Shape(1, 8, 8, 64 * 960, 128)
+    q, k, v = _growing_scores(shape, 91, (2, 300, 700, 940), 24.0)
+    nb = shape.nb
+    mask = synth.gen_block_mask(shape, 92, 0.8).mask.copy()
+    mask[:, :, :, [2, 300, 700, 940]] = 1
+    rows = sample_rows(1, 8, nb, 2, 93) + [(0, h, x) for h in (0, 7) for x in (1, 2, 127, 128, 301, 701, 939, 959)]
+    rows = sorted(set(rows))
+    say(f"[growing max xcd] shape={shape} rows={len(rows)}")
+    out, lse = seer.seer_block_sparse_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_u8(mask),
+                                               out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    got = np.concatenate([host(out[b, h, 64 * i:64 * i + 64]) for (b, h, i) in rows])
+    got_l = np.concatenate([host(lse[b, h, 64 * i:64 * i + 64]) for (b, h, i) in rows])
+    o_ref, l_ref = oracle.attention_rows(q, k, v, mask, rows)
+    check_close(got, np.concatenate(o_ref), "growing max xcd O (sampled)", out_dtype=torch.float32)
+    check_lse(got_l, np.concatenate(l_ref), "growing max xcd LSE (sampled)")
