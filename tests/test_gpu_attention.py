@@ -286,6 +286,8 @@ XCD_CASES = [
     ("d128_s61400_g1_bf16", Shape(1, 8, 8, 64 * 960 - 40, 128), torch.bfloat16),
     # two sequences, GQA groups of 2: jobs of both batches dealt over the XCDs
     ("d128_s64000_b2_g2_f32", Shape(2, 8, 4, 64 * 1000, 128), torch.float32),
+    # a last chunk of one row (1025 blocks), head_dim 64
+    ("d64_s65537_g1_f32", Shape(1, 8, 8, 64 * 1024 + 1, 64), torch.float32),
 ]
 
 
@@ -311,7 +313,7 @@ def test_sparse_xcd_rows(name, shape, dt):
     m = synth.gen_random_upper_noise(m, seed + 2)
     rows = sample_rows(shape.batch, shape.heads_q, nb, 2, seed + 3)
     rows += [(b, h, x) for b in {0, shape.batch - 1} for h in (0, shape.heads_q - 1)
-             for c in range(128, nb, 128) for x in (c - 1, c, c + 1)]
+             for c in range(128, nb, 128) for x in (c - 1, c, c + 1) if x < nb]
     rows += [(0, 1, nb - 1), (0, 2, nb - 2), (0, 3, 600), (0, 4, nb - 3), (0, 5, 700), (0, 6, 900)]
     _run_sampled(shape, seed, m, dt, sorted(set(rows)), name)
 
