@@ -354,7 +354,7 @@ def cpu_model() -> str:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); this build has no multi-GPU path",
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); the library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
 
