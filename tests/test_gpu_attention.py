@@ -288,6 +288,10 @@ XCD_CASES = [
     ("d128_s64000_b2_g2_f32", Shape(2, 8, 4, 64 * 1000, 128), torch.float32),
     # a last chunk of one row (1025 blocks), head_dim 64
     ("d64_s65537_g1_f32", Shape(1, 8, 8, 64 * 1024 + 1, 64), torch.float32),
+    # GQA groups of 8 (the diagonal launch's query-block-major order over 8 heads)
+    ("d64_s64000_g8_bf16", Shape(1, 64, 8, 64 * 1000, 64), torch.bfloat16),
+    # 88 jobs (2 x 4 KV groups x 11 chunks): the last 16 of the dealing only partly filled
+    ("d64_s89550_b2_g2_f32", Shape(2, 8, 4, 64 * 1400 - 50, 64), torch.float32),
 ]
 
 

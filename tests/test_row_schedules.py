@@ -157,7 +157,8 @@ def xcd_slot_base(qb, c):
 
 
 @pytest.mark.parametrize("batch,hkv,group,nb", [(1, 8, 4, 2048), (1, 8, 1, 960), (2, 4, 2, 1000),
-                                                (1, 16, 1, 1300), (1, 8, 2, 1290), (3, 8, 1, 1025)])
+                                                (1, 16, 1, 1300), (1, 8, 2, 1290), (3, 8, 1, 1025),
+                                                (1, 8, 8, 1000), (2, 3, 2, 1400), (2, 4, 2, 1400)])
 def test_xcd_two_launches_cover_every_item_once(batch, hkv, group, nb):
     """The first launch takes exactly the (row, chunk) items before each row's
     diagonal chunk, the second exactly one item per row (its diagonal chunk),
