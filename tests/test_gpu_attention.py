@@ -413,3 +413,21 @@ def test_sparse_xcd_running_max_grows_past_slack():
     o_ref, l_ref = oracle.attention_rows(q, k, v, mask, rows)
     check_close(got, np.concatenate(o_ref), "growing max xcd O (sampled)", out_dtype=torch.float32)
     check_lse(got_l, np.concatenate(l_ref), "growing max xcd LSE (sampled)")
+
+
+@pytest.mark.parametrize("name,shape", [("persistent_rows_s19200", Shape(1, 32, 8, 64 * 300, 128)),
+                                        ("xcd_two_launches_s61440", Shape(1, 8, 8, 64 * 960, 128))])
+def test_deterministic_reruns_dynamic_schedules(name, shape):
+    """The persistent launches hand out rows and items through atomic counters,
+    so which workgroup runs which item changes from call to call; every item's
+    arithmetic and every merge order are fixed, so O and LSE are bitwise equal
+    across calls."""
+    seer = _seer()
+    q, k, v = (dev_bf16(x) for x in synth.gen_qkv(shape, 47))
+    m = dev_u8(synth.gen_block_mask(shape, 48, 0.9).mask)
+    say(f"[determinism {name}] shape={shape}")
+    runs = [seer.seer_block_sparse_attn_fwd(q, k, v, m, want_lse=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, l in runs[1:]:
+        assert torch.equal(o.view(torch.int16), runs[0][0].view(torch.int16))
+        assert torch.equal(l, runs[0][1])
